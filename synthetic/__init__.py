@@ -1,0 +1,142 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module serves both the CPU oracle checks and the GPU library checks, and
+holds none of the quantizer's arithmetic: it only draws random numbers and
+stores them as bfloat16 bit patterns (uint16).
+
+Recipe (all tensors row-major):
+  * random numbers from numpy's PCG64 ``default_rng([seed, tensor_id])``,
+    drawn in float64 in row chunks of ``CHUNK`` elements, cast to float32,
+    then to bfloat16 by round-to-nearest-even on the float32 bit pattern;
+  * ``quantize_x``      256x1024  N(0,1), round(0.001 n) positions (drawn
+                        without replacement) replaced by N(0,1)*50;
+  * ``activations_t3``  8192x8192 Student-t(3) * 0.02 (heavy tails);
+  * ``llama_x``         16384x4096 Student-t(4), 8 seeded columns * 40;
+  * ``llama_w``         14336x4096 N(0, 0.02);
+  * ``llama_dy``        16384x14336 N(0, 1e-3);
+  * ``mx_if4``          16384x8192 N(0,1) with round(0.005 n / 32) aligned
+                        1x32 row blocks replaced by U(-1,1);
+  * ``gemm_a``/``gemm_b`` 8192x8192 N(0,1), independent streams.
+Every generator takes ``rows``/``cols`` so tests can draw smaller tensors of
+the same distribution.
+"""
+from __future__ import annotations
+
+import hashlib
+
+import numpy as np
+
+CHUNK = 1 << 20
+
+# tensor ids keep the streams of different tensors independent
+TID = {"quantize_x": 1, "activations_t3": 2, "llama_x": 3, "llama_w": 4, "llama_dy": 5,
+       "mx_if4": 6, "gemm_a": 7, "gemm_b": 8, "uniform": 9, "edge": 10}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def _draw(rng: np.random.Generator, n: int, fn) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint16)
+    for i in range(0, n, CHUNK):
+        m = min(CHUNK, n - i)
+        out[i:i + m] = f32_to_bf16_bits(fn(rng, m).astype(np.float32))
+    return out
+
+
+def normal(rows, cols, sigma=1.0, seed=0, tensor="uniform"):
+    rng = np.random.default_rng([seed, TID[tensor]])
+    return _draw(rng, rows * cols, lambda g, m: g.standard_normal(m) * sigma).reshape(rows, cols)
+
+
+def quantize_x(rows=256, cols=1024, seed=0):
+    rng = np.random.default_rng([seed, TID["quantize_x"]])
+    n = rows * cols
+    x = rng.standard_normal(n)
+    k = int(round(0.001 * n))
+    pos = rng.choice(n, size=k, replace=False)
+    x[pos] = rng.standard_normal(k) * 50.0
+    return f32_to_bf16_bits(x.astype(np.float32)).reshape(rows, cols)
+
+
+def activations_t3(rows=8192, cols=8192, seed=0):
+    rng = np.random.default_rng([seed, TID["activations_t3"]])
+    return _draw(rng, rows * cols, lambda g, m: g.standard_t(3.0, m) * 0.02).reshape(rows, cols)
+
+
+def llama_x(rows=16384, cols=4096, seed=0, n_outlier_cols=8, factor=40.0):
+    rng = np.random.default_rng([seed, TID["llama_x"]])
+    cols_out = np.sort(rng.choice(cols, size=min(n_outlier_cols, cols), replace=False))
+    gain = np.ones(cols, dtype=np.float64)
+    gain[cols_out] = factor
+    out = np.empty(rows * cols, dtype=np.uint16)
+    rows_per = max(1, CHUNK // cols)
+    for r0 in range(0, rows, rows_per):
+        r1 = min(rows, r0 + rows_per)
+        blk = rng.standard_t(4.0, (r1 - r0, cols)) * gain
+        out[r0 * cols:r1 * cols] = f32_to_bf16_bits(blk.astype(np.float32)).ravel()
+    return out.reshape(rows, cols)
+
+
+def llama_w(rows=14336, cols=4096, seed=0):
+    return normal(rows, cols, 0.02, seed, "llama_w")
+
+
+def llama_dy(rows=16384, cols=14336, seed=0):
+    return normal(rows, cols, 1e-3, seed, "llama_dy")
+
+
+def mx_if4(rows=16384, cols=8192, seed=0, frac=0.005, block=32):
+    rng = np.random.default_rng([seed, TID["mx_if4"]])
+    n = rows * cols
+    x = np.empty(n, dtype=np.uint16)
+    for i in range(0, n, CHUNK):
+        m = min(CHUNK, n - i)
+        x[i:i + m] = f32_to_bf16_bits(rng.standard_normal(m).astype(np.float32))
+    nblk = n // block
+    k = int(round(frac * nblk))
+    which = rng.choice(nblk, size=k, replace=False)
+    u = rng.uniform(-1.0, 1.0, (k, block))
+    xv = x.reshape(nblk, block)
+    xv[which] = f32_to_bf16_bits(u.astype(np.float32))
+    return x.reshape(rows, cols), np.sort(which)
+
+
+def gemm_a(rows=8192, cols=8192, seed=0):
+    return normal(rows, cols, 1.0, seed, "gemm_a")
+
+
+def gemm_b(rows=8192, cols=8192, seed=0):
+    return normal(rows, cols, 1.0, seed, "gemm_b")
+
+
+def edge_cases(rows=64, cols=256, seed=0):
+    """bf16 bit patterns that probe the corners: exact zeros (both signs), ties
+    of the scaled grid, subnormals, huge magnitudes, all-equal blocks."""
+    rng = np.random.default_rng([seed, TID["edge"]])
+    x = f32_to_bf16_bits(rng.standard_normal(rows * cols).astype(np.float32)).reshape(rows, cols)
+    x[0, :32] = 0                                   # zero blocks
+    x[0, 32:48] = 0x8000                            # negative zeros
+    x[1, :16] = f32_to_bf16_bits(np.float32([6, 1, 1.5, 2, 2.5, 3, 3.5, 5, 0.25, 0.75, 1.25, 1.75,
+                                             -5, -2.5, -0.25, -1.75]))
+    x[1, 16:32] = f32_to_bf16_bits(np.float32([3.5] + [0.25 * i for i in range(15)]))
+    x[2, :16] = rng.integers(1, 0x80, 16).astype(np.uint16)          # positive subnormals
+    x[2, 16:32] = rng.integers(0x8001, 0x8080, 16).astype(np.uint16)  # negative subnormals
+    x[3, :16] = f32_to_bf16_bits(np.float32(rng.standard_normal(16) * 1e37))
+    x[3, 16:32] = f32_to_bf16_bits(np.full(16, 1.5, np.float32))      # all equal
+    x[4, :16] = f32_to_bf16_bits(np.float32(rng.standard_normal(16) * 1e-30))
+    x[4, 16:32] = f32_to_bf16_bits(np.float32(np.r_[1e-38, rng.standard_normal(15) * 1e-3]))
+    x[5, :32] = f32_to_bf16_bits(np.float32(np.r_[1000.0, np.full(31, 1e-3)]))
+    return x
+
+
+def digest(h: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(h).tobytes()).hexdigest()

@@ -1,0 +1,166 @@
+"""Pins of the oracle's Hadamard transform, sign diagonal and Philox stream
+(CPU only)."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle as O
+import synthetic as S
+
+H16 = scipy.linalg.hadamard(16).astype(np.float64)
+
+
+def test_fwht_is_sylvester_hadamard_over_four():
+    """Column j of the transform is column j of scipy's (Sylvester-ordered)
+    Hadamard matrix divided by 4, exactly."""
+    for j in range(16):
+        e = np.zeros(16, np.float32)
+        e[j] = 1.0
+        np.testing.assert_array_equal(O.fwht16(e).astype(np.float64), H16[:, j] / 4)
+    np.testing.assert_array_equal(H16 @ H16.T, 16 * np.eye(16))
+
+
+def test_fwht_within_fp32_bound_of_dense_product():
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        v = np.float32(rng.standard_normal(16) * 10.0 ** rng.uniform(-3, 3))
+        want = H16 @ v.astype(np.float64) / 4
+        got = O.fwht16(v).astype(np.float64)
+        # four butterfly stages: each partial sum carries at most 4 roundings
+        bound = 4 * 2.0 ** -24 * np.abs(v).astype(np.float64).sum() / 4 * 1.01
+        assert np.max(np.abs(got - want)) <= bound
+
+
+def test_fwht_is_an_involution_and_keeps_the_norm():
+    rng = np.random.default_rng(1)
+    for _ in range(500):
+        v = np.float32(rng.standard_normal(16))
+        w = O.fwht16(O.fwht16(v))
+        np.testing.assert_allclose(w, v, rtol=0, atol=8 * 2.0 ** -24 * np.abs(v).max() * 4)
+        y = O.fwht16(v)
+        assert abs(np.sum(y.astype(np.float64) ** 2) - np.sum(v.astype(np.float64) ** 2)) \
+            <= 1e-6 * np.sum(v.astype(np.float64) ** 2)
+    # integer inputs stay exact: the round trip is the identity
+    v = np.float32(np.arange(16) - 7)
+    np.testing.assert_array_equal(O.fwht16(O.fwht16(v)), v)
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("kind", ["random", "det"])
+def test_rht_view_is_signed_hadamard(axis, kind):
+    x = S.normal(48, 64, 1.0, 0)
+    xf = S.bf16_bits_to_f32(x).astype(np.float64)
+    view = xf if axis == "row" else xf.T
+    mask = O.rht_sign_mask(kind, 1234)
+    d = np.array([-1.0 if (mask >> i) & 1 else 1.0 for i in range(16)])
+    y = O.rht_view(x, axis, kind, 1234)
+    want = (view.reshape(view.shape[0], -1, 16) * d) @ H16.T / 4
+    np.testing.assert_allclose(y.reshape(want.shape), want, rtol=0, atol=1e-5)
+    if kind == "det":
+        assert mask == 0
+
+
+def test_shared_signs_keep_inner_products():
+    """With one sign diagonal for both operands the rotated operands have the
+    same inner products (the GEMM result is unchanged)."""
+    a = S.normal(32, 128, 1.0, 0, "gemm_a")
+    b = S.normal(32, 128, 1.0, 0, "gemm_b")
+    ya = O.rht_view(a, "row", "random", 99).astype(np.float64)
+    yb = O.rht_view(b, "row", "random", 99).astype(np.float64)
+    za = S.bf16_bits_to_f32(a).astype(np.float64) @ S.bf16_bits_to_f32(b).astype(np.float64).T
+    np.testing.assert_allclose(ya @ yb.T, za, rtol=0, atol=1e-4)
+
+
+def test_rht_signs_differ_by_seed():
+    masks = {O.rht_sign_mask("random", s) for s in range(64)}
+    assert len(masks) > 60
+    assert all(0 <= m < (1 << 16) for m in masks)
+
+
+# ---- Philox4x32-10 against rocRAND ------------------------------------------
+
+ROCRAND_PROBE = r"""
+#include <hip/hip_runtime.h>
+#include <rocrand/rocrand_philox4x32_10.h>
+#include <cstdio>
+#include <cstdlib>
+int main(int argc, char** argv) {
+  for (int i = 1; i + 2 < argc; i += 3) {
+    unsigned long long seed = strtoull(argv[i], 0, 0), sub = strtoull(argv[i + 1], 0, 0),
+                       q = strtoull(argv[i + 2], 0, 0);
+    rocrand_device::philox4x32_10_engine e(seed, sub, 4ull * q);
+    unsigned a = e(), b = e(), c = e(), d = e();
+    printf("%u %u %u %u\n", a, b, c, d);
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def rocrand_probe():
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    d = tempfile.mkdtemp()
+    src = os.path.join(d, "p.cpp")
+    open(src, "w").write(ROCRAND_PROBE)
+    exe = os.path.join(d, "p")
+    subprocess.run([hipcc, "-O1", "-x", "hip", "--offload-arch=gfx950", "-o", exe, src], check=True,
+                   capture_output=True)
+    return exe
+
+
+def test_philox_matches_rocrand_engine(rocrand_probe):
+    """rocRAND's engine(seed, subsequence, offset=4q) runs the block with
+    key = seed and counter = (q lo, q hi, subsequence lo, subsequence hi):
+    the same mapping the SR stream uses (stream = subsequence)."""
+    cases = [(0, 0, 0), (0, 0, 1), (1, 0, 0), (0x1234567890, 3, 77), (2 ** 64 - 1, 1, 2 ** 40 + 5),
+             (0xDEADBEEF, 0, 123456789), (7, 0x52485400, 0)]
+    args = [str(v) for c in cases for v in c]
+    out = subprocess.run([rocrand_probe, *args], check=True, capture_output=True, text=True).stdout.split("\n")
+    for (seed, sub, q), line in zip(cases, out):
+        want = [int(t) for t in line.split()]
+        got = [O.sr_word(seed, sub, 4 * q + j) for j in range(4)]
+        assert got == want, (seed, sub, q)
+    # the sign diagonal is word 0 of the counter (0,0,"RHT\0",0) block
+    w = O.philox4x32_10([0, 0, 0x52485400, 0], [7, 0])
+    assert O.rht_sign_mask("random", 7) == (int(w[0]) & 0xFFFF)
+
+
+def test_sr_words_array_matches_scalar():
+    w = O.sr_words(11, 1, 1000, 64)
+    assert [int(v) for v in w] == [O.sr_word(11, 1, 1000 + i) for i in range(64)]
+
+
+# ---- stochastic rounding ---------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e1m2", "int4"])
+def test_sr_is_unbiased(fmt):
+    """E[q] = |z| for z inside the grid range, and P(round up) = frac."""
+    g = O.grid(fmt)
+    n = 1 << 20
+    w = O.sr_words(2024, 0, 0, n)
+    rng = np.random.default_rng(7)
+    for a in [0.1, 0.3, 1.2, 1.9, 2.2, 2.7, 3.3, 4.4, 5.5]:
+        a = np.float32(min(a, g[7] * 0.95))
+        codes = O.round_sr_array(np.full(n, a, np.float32), w, fmt)
+        q = g[codes & 7]
+        lo = g[g <= a].max()
+        hi = g[g > a].min()
+        frac = (float(a) - lo) / (hi - lo)
+        sigma = (hi - lo) * np.sqrt(frac * (1 - frac) / n)
+        assert abs(q.mean() - float(a)) < 5 * sigma + 1e-12
+        assert set(np.unique(q)) <= {lo, hi}
+    # grid points never move; saturation above the top
+    for k in range(8):
+        z = np.full(4096, g[k], np.float32)
+        assert np.all(O.round_sr_array(z, w[:4096], fmt) == k)
+    assert O.round_sr(g[7] * 3, fmt, 0) == 7
+    assert O.round_sr(-1e-3, fmt, 0) & 8
+    _ = rng

@@ -1,0 +1,190 @@
+"""Benchmark of the 4-bit block quantizer on one MI355X.
+
+Workload (one step): the 8192 x 8192 bf16 activation tensor with Student-t(3)
+entries scaled by 0.02, transformed by the seeded 16-wide RHT and quantized
+twice with the two-level scale (E4M3 block scale + FP32 tensor scale):
+NVFP4-style E2M1 (alpha = amax / (6 x 448)) and E1M2 (alpha = amax / (3.5 x 448)).
+Each quantization is the tensor-amax pass followed by the fused
+RHT + quantize kernel, so a step reads the input four times and writes two
+sets of codes and scales.  Inputs rotate over 8 resident copies (1 GiB, more
+than the 256 MB Infinity Cache) so that every step reads HBM.
+
+value = bf16 input bytes quantized per second (2 bytes x 2 quantizations x n
+per step / step time).  The roofline object is for the dominant kernel, the
+fused RHT + quantize kernel: algorithmic bytes per launch (bf16 in + packed
+codes + E4M3 scales = 171,966,464 B) over its average launch time from HIP
+events on the stream it runs on.  The secondary `qgemm` object times the
+MXFP4 block-scaled GEMM at 8192^3 (A, B: N(0,1) bf16 -> RHT -> MXFP4).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP4_PEAK_TFLOPS = 10100.0
+ROWS = COLS = 8192
+N_ELEM = ROWS * COLS
+QUANT_BYTES = N_ELEM * 2 + N_ELEM // 2 + N_ELEM // 16  # bf16 in + codes + E4M3 scales
+AMAX_BYTES = N_ELEM * 2
+PMC_FILE = os.path.join(ROOT, "profiles", "quantize_row_e2m1_e4m3_rht_8192x8192_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "block_scaled_bit_ufp4_amd", "csrc", "quantize.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--copies", type=int, default=8)
+    p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--no-gemm", action="store_true", help="skip the qgemm leg")
+    p.add_argument("--cpu-rows", type=int, default=4096)
+    return p.parse_args()
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the quantize kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        d = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != src_hash(KERNEL_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x_bits, rows):
+    import oracle as O
+    sample = np.ascontiguousarray(x_bits[:rows])
+    t0 = time.perf_counter()
+    for fmt in ("e2m1", "e1m2"):
+        cfg = O.Cfg(fmt, "e4m3", rht="random", rht_seed=0)
+        a = O.amax(sample, cfg)
+        O.quantize(sample, cfg, amax_value=a)
+    dt = time.perf_counter() - t0
+    return {"value": round(2 * 2 * sample.size / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of 8192 rows (two-level E2M1 and E1M2, amax + quantize, RHT), "
+                      f"{dt:.1f} s single-threaded plain C",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the quantizer shards by rows "
+                                   "with no exchange except a 4-byte amax MAX all-reduce, not run here)"}))
+        sys.exit(2)
+    import torch
+    import block_scaled_bit_ufp4_amd as U
+    import synthetic as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    x_bits = S.activations_t3(ROWS, COLS, seed=0)
+    print(f"# generated input in {time.time() - t0:.1f} s, sha256 {S.digest(x_bits)[:16]}", file=sys.stderr,
+          flush=True)
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(args.copies - 1)]
+    cfgs = [U.Cfg("e2m1", "e4m3", rht="random", rht_seed=0), U.Cfg("e1m2", "e4m3", rht="random", rht_seed=0)]
+    outs = [[U.alloc_qtensor(ROWS, COLS, c) for c in cfgs] for _ in range(args.copies)]
+    amaxes = [[torch.zeros(1, dtype=torch.float32, device=dev) for _ in cfgs] for _ in range(args.copies)]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        j = i % args.copies
+        for f, cfg in enumerate(cfgs):
+            U.ufp4_amax(xs[j], cfg, out=amaxes[j][f])
+            if ev is not None:
+                ev[f][0].record(stream)
+            U.ufp4_quantize(xs[j], cfg, amax=amaxes[j][f], out=outs[j][f])
+            if ev is not None:
+                ev[f][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in cfgs] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    q_ms = [np.mean([evs[i][f][0].elapsed_time(evs[i][f][1]) for i in range(args.steps)]) for f in range(len(cfgs))]
+    value = 2 * N_ELEM * len(cfgs) / (ms_step * 1e-3) / 1e9
+    achieved = QUANT_BYTES / (q_ms[0] * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+    out = {
+        "metric": "quantize GB/s (bf16 in) and % HBM peak; qGEMM TFLOP/s, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "8192x8192 bf16 Student-t(3)*0.02 activations; RHT-16 (seeded signs) + "
+                               "two-level E4M3/FP32 scale; E2M1 (NVFP4-style) and E1M2; amax pass + fused "
+                               "quantize per format",
+                   "rows": ROWS, "cols": COLS, "block": 16, "input_copies": args.copies},
+        "pct_hbm_peak_step": round(100.0 * (2 * (AMAX_BYTES + QUANT_BYTES)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "row_kernel (fused RHT + E2M1 + E4M3 two-level quantize)",
+                     "bytes_per_launch": QUANT_BYTES, "avg_launch_ms": round(q_ms[0], 5),
+                     "e1m2_avg_launch_ms": round(q_ms[1], 5)},
+    }
+    if not args.no_gemm:
+        out["qgemm"] = bench_gemm(U, S, torch, dev, stream)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x_bits, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+def bench_gemm(U, S, torch, dev, stream, reps=10):
+    M = N = K = 8192
+    a = torch.from_numpy(S.gemm_a(M, K).view(np.int16)).view(torch.bfloat16).to(dev)
+    b = torch.from_numpy(S.gemm_b(N, K).view(np.int16)).view(torch.bfloat16).to(dev)
+    cfg = U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=0)
+    qa, qb = U.ufp4_quantize(a, cfg), U.ufp4_quantize(b, cfg)
+    c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        U.ufp4_qgemm(qa, qb, "mxfp4", c=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        U.ufp4_qgemm(qa, qb, "mxfp4", c=c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out", "ms": round(ms, 4),
+            "tflops": round(tflops, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tflops / FP4_PEAK_TFLOPS, 4)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,363 @@
+// api.hip -- the C ABI of libufp4 (declared in include/ufp4.h): argument
+// validation on the host, then dispatch to the gfx950 kernels.
+//
+// The operations and their definitions are documented in ufp4.h, with the
+// passages of the pages each follows.  Nothing here allocates device memory;
+// every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ufp4.h"
+#include "device.hpp"
+#include "kernels.hpp"
+
+using namespace ufp4;
+
+static thread_local int g_last_hip_error = 0;
+
+static int hip_fail(hipError_t e)
+{
+    if (e == hipSuccess) return UFP4_OK;
+    g_last_hip_error = (int)e;
+    return UFP4_ERR_HIP;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Host-side Philox4x32-10 word 0 for the sign diagonal (SC'11 round function).
+static uint32_t host_philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1)
+{
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c0;
+}
+
+static uint32_t sign_mask(int rht, uint64_t seed)
+{
+    if (rht != UFP4_RHT_RANDOM) return 0u;
+    return host_philox_word0(0u, 0u, 0x52485400u, 0u, (uint32_t)seed, (uint32_t)(seed >> 32)) & 0xFFFFu;
+}
+
+static int check_config(const ufp4_config *c)
+{
+    if (!c) return UFP4_ERR_INVALID_ARG;
+    if (c->format < UFP4_E2M1 || c->format > UFP4_IF4) return UFP4_ERR_INVALID_ARG;
+    if (c->scale < UFP4_SCALE_FP32 || c->scale > UFP4_SCALE_E8M0) return UFP4_ERR_INVALID_ARG;
+    if (c->rht < UFP4_RHT_NONE || c->rht > UFP4_RHT_DETERMINISTIC) return UFP4_ERR_INVALID_ARG;
+    if (c->rounding != UFP4_RTNE && c->rounding != UFP4_SR) return UFP4_ERR_INVALID_ARG;
+    if (c->axis != UFP4_ROW && c->axis != UFP4_COL) return UFP4_ERR_INVALID_ARG;
+    if (c->block != 16 && c->block != 32) return UFP4_ERR_INVALID_ARG;
+    if (c->reserved != 0) return UFP4_ERR_INVALID_ARG;
+    if (c->scale == UFP4_SCALE_E8M0) {
+        if (c->format != UFP4_E2M1 || c->block != 32 || c->rounding != UFP4_RTNE) return UFP4_ERR_UNSUPPORTED;
+    } else if (c->block != 16) {
+        return UFP4_ERR_UNSUPPORTED;
+    }
+    if (c->format == UFP4_IF4 && (c->scale != UFP4_SCALE_E4M3 || c->rounding != UFP4_RTNE))
+        return UFP4_ERR_UNSUPPORTED;
+    return UFP4_OK;
+}
+
+// Shape/alignment rules of a source x[rows][ldx] read along `axis`.
+static int check_source(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int axis, int block)
+{
+    if (!x && rows * cols > 0) return UFP4_ERR_INVALID_ARG;
+    if (dtype != UFP4_BF16 && dtype != UFP4_F32) return UFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return UFP4_ERR_SHAPE;
+    if (ldx < cols) return UFP4_ERR_SHAPE;
+    const int64_t L = axis == UFP4_ROW ? cols : rows;
+    if (L % block) return UFP4_ERR_SHAPE;
+    if (axis == UFP4_COL && cols % 8) return UFP4_ERR_SHAPE;
+    if (!aligned16(x) || ldx % 8) return UFP4_ERR_ALIGN;
+    if (rows * cols >= ((int64_t)1 << 40)) return UFP4_ERR_SHAPE;
+    return UFP4_OK;
+}
+
+static void fill_args(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int axis, uint32_t smask,
+                      RowArgs &ra, ColArgs &ca)
+{
+    memset(&ra, 0, sizeof(ra));
+    memset(&ca, 0, sizeof(ca));
+    (void)dtype;
+    ra.x = x;
+    ra.ldx = ldx;
+    ra.L = cols;
+    ra.n_oct = axis == UFP4_ROW ? rows * cols / 8 : 0;
+    ra.contiguous = ldx == cols;
+    ra.smask = smask;
+    ca.x = x;
+    ca.ldx = ldx;
+    ca.R = rows;
+    ca.C = cols;
+    ca.smask = smask;
+}
+
+extern "C" {
+
+int ufp4_version(void) { return (0 << 16) | 1; }
+
+const char *ufp4_strerror(int code)
+{
+    switch (code) {
+    case UFP4_OK: return "ok";
+    case UFP4_ERR_INVALID_ARG: return "invalid argument (null pointer, unknown enum value or dtype)";
+    case UFP4_ERR_SHAPE: return "shape not supported (block multiple, tile multiple or leading dimension)";
+    case UFP4_ERR_ALIGN: return "pointer not 16-byte aligned or leading dimension not a multiple of 8";
+    case UFP4_ERR_UNSUPPORTED: return "unsupported combination of format, scale, block and rounding";
+    case UFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case UFP4_ERR_HIP: return "HIP launch failed (see ufp4_last_hip_error)";
+    }
+    return "unknown error code";
+}
+
+int ufp4_last_hip_error(void) { return g_last_hip_error; }
+
+size_t ufp4_workspace_size(int op, int64_t rows, int64_t cols, const ufp4_config *cfg)
+{
+    switch (op) {
+    case UFP4_OP_STATS: return (size_t)STATS_WGS * UFP4_NSUMS * sizeof(double);
+    case UFP4_OP_ETA: return (size_t)ETA_WGS * 3 * sizeof(double);
+    case UFP4_OP_QGEMM:
+        // dequantize-to-bf16 path: both operands as bf16 ((M + N) x K)
+        if (cfg && cfg->scale != UFP4_SCALE_E8M0) return (size_t)(rows * cols * 2);
+        return 0;
+    }
+    (void)rows;
+    (void)cols;
+    return 0;
+}
+
+int ufp4_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int axis, int rht_kind,
+             uint64_t rht_seed, void *y, int y_dtype, int64_t ldy, void *stream)
+{
+    if (axis != UFP4_ROW && axis != UFP4_COL) return UFP4_ERR_INVALID_ARG;
+    if (rht_kind < UFP4_RHT_NONE || rht_kind > UFP4_RHT_DETERMINISTIC) return UFP4_ERR_INVALID_ARG;
+    if (y_dtype != UFP4_BF16 && y_dtype != UFP4_F32) return UFP4_ERR_INVALID_ARG;
+    int rc = check_source(x, x_dtype, rows, cols, ldx, axis, 16);
+    if (rc) return rc;
+    const int64_t V = axis == UFP4_ROW ? rows : cols, L = axis == UFP4_ROW ? cols : rows;
+    if (!y && V * L > 0) return UFP4_ERR_INVALID_ARG;
+    if (ldy < L) return UFP4_ERR_SHAPE;
+    if (!aligned16(y) || ldy % 8) return UFP4_ERR_ALIGN;
+    RowArgs ra;
+    ColArgs ca;
+    fill_args(x, x_dtype, rows, cols, ldx, axis, sign_mask(rht_kind, rht_seed), ra, ca);
+    ra.y = y;
+    ra.ldy = ldy;
+    ca.y = y;
+    ca.ldy = ldy;
+    LaunchSpec sp{0, 0, 0, x_dtype, rht_kind != UFP4_RHT_NONE, axis};
+    return hip_fail(launch_rht(sp, y_dtype, ra, ca, (hipStream_t)stream));
+}
+
+int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+              float *amax, void *stream)
+{
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!amax) return UFP4_ERR_INVALID_ARG;
+    rc = check_source(x, x_dtype, rows, cols, ldx, cfg->axis, 16);
+    if (rc) return rc;
+    RowArgs ra;
+    ColArgs ca;
+    fill_args(x, x_dtype, rows, cols, ldx, cfg->axis, sign_mask(cfg->rht, cfg->rht_seed), ra, ca);
+    ra.amax_out = reinterpret_cast<unsigned int *>(amax);
+    ca.amax_out = reinterpret_cast<unsigned int *>(amax);
+    LaunchSpec sp{0, 0, 0, x_dtype, cfg->rht != UFP4_RHT_NONE, cfg->axis};
+    return hip_fail(launch_amax(sp, ra, ca, (hipStream_t)stream));
+}
+
+int ufp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+                  const float *amax, ufp4_qtensor *out, void *stream)
+{
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!out) return UFP4_ERR_INVALID_ARG;
+    rc = check_source(x, x_dtype, rows, cols, ldx, cfg->axis, cfg->block);
+    if (rc) return rc;
+    if (rows * cols > 0 && (!out->codes || !out->scales)) return UFP4_ERR_INVALID_ARG;
+    if (cfg->scale == UFP4_SCALE_E4M3 && (!amax || !out->tensor_scale)) return UFP4_ERR_INVALID_ARG;
+    if (((uintptr_t)out->codes & 7u) || ((uintptr_t)out->scales & 3u)) return UFP4_ERR_ALIGN;
+    out->rows = rows;
+    out->cols = cols;
+    out->cfg = *cfg;
+    RowArgs ra;
+    ColArgs ca;
+    fill_args(x, x_dtype, rows, cols, ldx, cfg->axis, sign_mask(cfg->rht, cfg->rht_seed), ra, ca);
+    ra.codes = out->codes;
+    ra.scales = out->scales;
+    ra.amax = amax;
+    ra.tensor_scale = out->tensor_scale;
+    ra.sr_seed = cfg->sr_seed;
+    ra.sr_stream = cfg->sr_stream;
+    ca.codes = out->codes;
+    ca.scales = out->scales;
+    ca.amax = amax;
+    ca.tensor_scale = out->tensor_scale;
+    ca.sr_seed = cfg->sr_seed;
+    ca.sr_stream = cfg->sr_stream;
+    LaunchSpec sp{cfg->format, cfg->scale, cfg->rounding == UFP4_SR, x_dtype, cfg->rht != UFP4_RHT_NONE, cfg->axis};
+    return hip_fail(launch_quantize(sp, ra, ca, (hipStream_t)stream));
+}
+
+static int check_qtensor(const ufp4_qtensor *q)
+{
+    if (!q) return UFP4_ERR_INVALID_ARG;
+    int rc = check_config(&q->cfg);
+    if (rc) return rc;
+    if (q->rows < 0 || q->cols < 0) return UFP4_ERR_SHAPE;
+    const int64_t L = q->cfg.axis == UFP4_ROW ? q->cols : q->rows;
+    if (L % q->cfg.block) return UFP4_ERR_SHAPE;
+    if (q->rows * q->cols > 0 && (!q->codes || !q->scales)) return UFP4_ERR_INVALID_ARG;
+    if (q->cfg.scale == UFP4_SCALE_E4M3 && !q->tensor_scale) return UFP4_ERR_INVALID_ARG;
+    if (((uintptr_t)q->codes & 3u) || ((uintptr_t)q->scales & 3u)) return UFP4_ERR_ALIGN;
+    return UFP4_OK;
+}
+
+int ufp4_dequantize(const ufp4_qtensor *q, int inverse_rht, void *y, int y_dtype, int64_t ldy, void *stream)
+{
+    int rc = check_qtensor(q);
+    if (rc) return rc;
+    if (y_dtype != UFP4_BF16 && y_dtype != UFP4_F32) return UFP4_ERR_INVALID_ARG;
+    const int64_t V = q->cfg.axis == UFP4_ROW ? q->rows : q->cols, L = q->cfg.axis == UFP4_ROW ? q->cols : q->rows;
+    if (!y && V * L > 0) return UFP4_ERR_INVALID_ARG;
+    if (ldy < L) return UFP4_ERR_SHAPE;
+    if (!aligned16(y) || ldy % 8) return UFP4_ERR_ALIGN;
+    DeqArgs a;
+    a.codes = q->codes;
+    a.scales = q->scales;
+    a.tensor_scale = q->tensor_scale;
+    a.L = L;
+    a.n_oct = V * L / 8;
+    a.smask = sign_mask(q->cfg.rht, q->cfg.rht_seed);
+    a.y = y;
+    a.ldy = ldy;
+    const int inv = inverse_rht && q->cfg.rht != UFP4_RHT_NONE;
+    return hip_fail(launch_dequant(q->cfg.format, q->cfg.scale, inv, y_dtype, a, (hipStream_t)stream));
+}
+
+int ufp4_stats(const void *x, int x_dtype, int64_t ldx, const ufp4_qtensor *q, double *sums, void *ws,
+               size_t ws_bytes, void *stream)
+{
+    int rc = check_qtensor(q);
+    if (rc) return rc;
+    if (!sums) return UFP4_ERR_INVALID_ARG;
+    rc = check_source(x, x_dtype, q->rows, q->cols, ldx, q->cfg.axis, q->cfg.block);
+    if (rc) return rc;
+    const size_t need = ufp4_workspace_size(UFP4_OP_STATS, q->rows, q->cols, &q->cfg);
+    if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
+    if ((uintptr_t)ws & 7u || (uintptr_t)sums & 7u) return UFP4_ERR_ALIGN;
+    StatsArgs a;
+    a.x = x;
+    a.ldx = ldx;
+    a.V = q->cfg.axis == UFP4_ROW ? q->rows : q->cols;
+    a.L = q->cfg.axis == UFP4_ROW ? q->cols : q->rows;
+    a.axis = q->cfg.axis;
+    a.smask = sign_mask(q->cfg.rht, q->cfg.rht_seed);
+    a.codes = q->codes;
+    a.scales = q->scales;
+    a.tensor_scale = q->tensor_scale;
+    a.partials = static_cast<double *>(ws);
+    a.sums = sums;
+    return hip_fail(launch_stats(q->cfg.format, q->cfg.scale, x_dtype, q->cfg.rht != UFP4_RHT_NONE, a,
+                                 (hipStream_t)stream));
+}
+
+void ufp4_stats_finalize(const double *s, ufp4_stats_report *r)
+{
+    memset(r, 0, sizeof(*r));
+    const double n = s[0];
+    r->n = n;
+    r->sqnr_db = s[2] > 0 ? 10.0 * log10(s[1] / s[2]) : INFINITY;
+    r->alpha = s[1] > 0 ? s[5] / s[1] : NAN;
+    r->mse = n > 0 ? s[2] / n : 0.0;
+    r->mean_err = n > 0 ? s[3] / n : 0.0;
+    r->mean_shrink = n > 0 ? s[4] / n : 0.0;
+    r->int4_share = s[7] > 0 ? s[8] / s[7] : 0.0;
+    for (int t = 0; t < 2; ++t)
+        for (int k = 0; k < 8; ++k) {
+            const double c = s[16 + 8 * t + k];
+            r->counts[t][k] = c;
+            r->bucket_bias[t][k] = c > 0 ? s[32 + 8 * t + k] / c : NAN;
+        }
+}
+
+int ufp4_gemm_bf16(const void *a, const void *b, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, float *c,
+                   int64_t ldc, void *stream)
+{
+    if ((!a || !b || !c) && M * N * K > 0) return UFP4_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return UFP4_ERR_SHAPE;
+    if (M % 256 || N % 256 || K % 64) return UFP4_ERR_SHAPE;
+    if (lda < K || ldb < K || ldc < N) return UFP4_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(c) || lda % 8 || ldb % 8 || ldc % 4) return UFP4_ERR_ALIGN;
+    if (M == 0 || N == 0) return UFP4_OK;
+    return hip_fail(launch_gemm_bf16(static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), M, N, K, lda,
+                                     ldb, c, ldc, (hipStream_t)stream));
+}
+
+int ufp4_qgemm(const ufp4_qtensor *a, const ufp4_qtensor *b, int mode, float *c, int64_t ldc, void *ws,
+               size_t ws_bytes, void *stream)
+{
+    int rc = check_qtensor(a);
+    if (rc) return rc;
+    rc = check_qtensor(b);
+    if (rc) return rc;
+    if (!c) return UFP4_ERR_INVALID_ARG;
+    if (a->cfg.axis != UFP4_ROW || b->cfg.axis != UFP4_ROW) return UFP4_ERR_UNSUPPORTED;
+    const int64_t M = a->rows, N = b->rows, K = a->cols;
+    if (b->cols != K) return UFP4_ERR_SHAPE;
+    if (a->cfg.rht != b->cfg.rht || (a->cfg.rht == UFP4_RHT_RANDOM && a->cfg.rht_seed != b->cfg.rht_seed))
+        return UFP4_ERR_UNSUPPORTED;
+    if (M % 256 || N % 256 || K % 128) return UFP4_ERR_SHAPE;
+    if (ldc < N || ldc % 4) return UFP4_ERR_SHAPE;
+    if (!aligned16(c)) return UFP4_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (mode == UFP4_GEMM_NATIVE_MXFP4) {
+        if (a->cfg.format != UFP4_E2M1 || a->cfg.scale != UFP4_SCALE_E8M0 || b->cfg.format != UFP4_E2M1 ||
+            b->cfg.scale != UFP4_SCALE_E8M0)
+            return UFP4_ERR_UNSUPPORTED;
+        if (!aligned16(a->codes) || !aligned16(b->codes)) return UFP4_ERR_ALIGN;
+        if (M == 0 || N == 0) return UFP4_OK;
+        return hip_fail(launch_gemm_mxfp4(a->codes, static_cast<const uint8_t *>(a->scales), b->codes,
+                                          static_cast<const uint8_t *>(b->scales), M, N, K, c, ldc, st));
+    }
+    if (mode != UFP4_GEMM_DEQUANT_BF16) return UFP4_ERR_INVALID_ARG;
+    if (a->cfg.format == UFP4_IF4 || b->cfg.format == UFP4_IF4) return UFP4_ERR_UNSUPPORTED;
+    const size_t need = (size_t)((M + N) * K * 2);
+    if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
+    if (!aligned16(ws)) return UFP4_ERR_ALIGN;
+    if (M == 0 || N == 0) return UFP4_OK;
+    uint16_t *da = static_cast<uint16_t *>(ws);
+    uint16_t *db = da + M * K;
+    // x_hat of each operand in bf16 (nearest even), in the rotated domain
+    rc = ufp4_dequantize(a, 0, da, UFP4_BF16, K, stream);
+    if (rc) return rc;
+    rc = ufp4_dequantize(b, 0, db, UFP4_BF16, K, stream);
+    if (rc) return rc;
+    return hip_fail(launch_gemm_bf16(da, db, M, N, K, K, K, c, ldc, st));
+}
+
+int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, double *sums, void *ws, size_t ws_bytes,
+             void *stream)
+{
+    if (!zq || !z || !sums) return UFP4_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || ld < N) return UFP4_ERR_SHAPE;
+    if (N % 4 || ld % 4) return UFP4_ERR_SHAPE;
+    if (!aligned16(zq) || !aligned16(z) || (uintptr_t)sums & 7u) return UFP4_ERR_ALIGN;
+    const size_t need = ufp4_workspace_size(UFP4_OP_ETA, M, N, nullptr);
+    if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
+    return hip_fail(launch_eta(zq, z, M, N, ld, static_cast<double *>(ws), sums, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+// device.hpp -- gfx950 device helpers of the 4-bit block quantizer.
+//
+// Number formats: E2M1 {0,.5,1,1.5,2,3,4,6} and E1M2 {0,.5,...,3.5}
+// ("当你的 GPU 学不会算账" sections "E2M1：一块刻度不均的尺子" and "UFP4：换一把
+// 尺子"); INT4 {0..7} and the E4M3 / UE8M0 scale formats (IF4 page, section 2.2
+// format table; MXFP4 page, section on MXFP4).  Philox4x32-10 from Salmon et al.,
+// "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11).
+//
+// Every function here computes exactly (bit for bit) the binary32 result the
+// ABI header defines; the faster formulations are justified next to them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ufp4 {
+
+enum : int { FMT_E2M1 = 0, FMT_E1M2 = 1, FMT_INT4 = 2, FMT_IF4 = 3 };
+enum : int { SC_FP32 = 0, SC_E4M3 = 1, SC_E8M0 = 2 };
+enum : int { IN_BF16 = 0, IN_F32 = 1 };
+
+__host__ __device__ constexpr float grid_max(int f)
+{
+    return f == FMT_E1M2 ? 3.5f : (f == FMT_INT4 ? 7.0f : 6.0f);
+}
+__host__ __device__ constexpr int block_of(int scl) { return scl == SC_E8M0 ? 32 : 16; }
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane moves (DPP, wave64).  quad_perm [1,0,3,2] = lane ^ 1,
+// quad_perm [2,3,0,1] = lane ^ 2, row_ror:8 = lane ^ 8 inside 16-lane rows.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xor1(float v)
+{
+    return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float xor2(float v)
+{
+    return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float xor8(float v)
+{
+    return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(v), 0x128, 0xF, 0xF, true));
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10: ten rounds of two 32x32->64 multiplies by the SC'11
+// constants; the key advances by the two Weyl increments between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1,
+                       (uint32_t)p0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Four SR words for view elements n0..n0+3 (n0 a multiple of 4).
+__device__ __forceinline__ uint4 sr_words4(uint64_t n0, uint64_t seed, uint32_t stream)
+{
+    const uint64_t q = n0 >> 2;
+    return philox10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), stream, 0u), (uint32_t)seed,
+                    (uint32_t)(seed >> 32));
+}
+
+// ---------------------------------------------------------------------------
+// 16-point Walsh-Hadamard butterflies, spans 1, 2, 4 inside 8 registers.
+// (a, b) -> (a + b, a - b), the same additions in the same order as the
+// definition, so the results are identical whatever the lane layout.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fwht8(float *v)
+{
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+}
+
+// Full 16-point transform in registers (span 8 last), then x 1/4.
+__device__ __forceinline__ void fwht16_local(float *v)
+{
+    fwht8(v);
+    fwht8(v + 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float a = v[i], b = v[i + 8];
+        v[i] = a + b;
+        v[i + 8] = a - b;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] * 0.25f;
+}
+
+// ---------------------------------------------------------------------------
+// Division.  z = RN(a / s) for a >= 0 as  q = a*inv, r = fma(-q, s, a),
+// z = fma(r, inv, q)  with inv = RN(1/s): Markstein's correction step, exact
+// when the residual r does not underflow.  Conditions used here: s in
+// [2^-75, 2^125] and a >= 2^-100 (r is then a normal number); for a < 2^-100
+// the quotient is below 2^-25, where only z == 0 vs z > 0 can matter (RTNE
+// gives code 0 either way); callers that care (stochastic rounding) re-divide
+// when the fast quotient is 0 for a > 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool fast_div_ok(float s) { return s >= 0x1p-75f && s <= 0x1p125f; }
+
+__device__ __forceinline__ float div_fast(float a, float s, float inv)
+{
+    const float q = a * inv;
+    const float r = __builtin_fmaf(-q, s, a);
+    return __builtin_fmaf(r, inv, q);
+}
+
+// RN(m / G) for a constant G (the grid maximum), m >= 0.
+template <int F>
+__device__ __forceinline__ float div_by_gridmax(float m)
+{
+    constexpr float G = grid_max(F);
+    constexpr float INV = 1.0f / G;
+    if (m >= 0x1p-100f) return div_fast(m, G, INV);
+    return m / G;
+}
+
+// ---------------------------------------------------------------------------
+// E4M3FN (bias 7, max 448, subnormal step 2^-9): nearest, ties to even,
+// saturating.  Input v >= 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float v)
+{
+    if (!(v < 448.0f)) return 0x7Eu;
+    if (v < 0x1p-6f) {
+        // subnormal range: multiples of 2^-9; x 512 is exact, rint is RNE;
+        // q = 8 is 2^-6, whose encoding 0x08 is the same integer
+        return (uint32_t)__builtin_rintf(v * 512.0f);
+    }
+    // normal range: round the binary32 significand to 3 bits (nearest even)
+    const uint32_t b = f2u(v);
+    const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+    const uint32_t code = (r >> 20) - (120u << 3);
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t b)
+{
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 0) return (float)m * 0x1p-9f;
+    return u2f(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------------------
+// Magnitude codes, round to nearest even.  a >= 0 (a = |z|).
+//   E1M2: k = rint(2a), clamped to 7: min(a, 3.5) * 2 + 2^23 rounds 2a to an
+//         integer (RNE) in the low mantissa bits.
+//   INT4: k = rint(a) clamped to 7, the same way.
+//   E2M1: below 1 the step is 0.5 (k = rint(2a) in {0,1,2}); from 1 up the
+//         code is the binary32 value rounded to one mantissa bit (RNE), read
+//         off the exponent and that bit; clamped to 7 (saturation at 6).
+// Each equals the nearest-grid-point definition with ties to the even code.
+// ---------------------------------------------------------------------------
+template <int F>
+__device__ __forceinline__ uint32_t rtne_code(float a)
+{
+    if constexpr (F == FMT_E1M2) {
+        return f2u(__builtin_fmaf(fminf(a, 3.5f), 2.0f, 0x1p23f)) & 7u;
+    } else if constexpr (F == FMT_INT4) {
+        return f2u(fminf(a, 7.0f) + 0x1p23f) & 7u;
+    } else {
+        const uint32_t lo = f2u(__builtin_fmaf(fminf(a, 1.0f), 2.0f, 0x1p23f)) & 7u;
+        const uint32_t b = f2u(fminf(a, 8.0f));
+        const uint32_t r = b + 0x1FFFFFu + ((b >> 22) & 1u);
+        const uint32_t hi = min((r >> 22) - 252u, 7u);
+        return a < 1.0f ? lo : hi;
+    }
+}
+
+// Stochastic rounding of a >= 0 on format F with one Philox word w:
+// k = k_lo + (u < frac), u = (w >> 8) 2^-24.  frac is exact (the cell widths
+// are powers of two), and u < frac is evaluated as (w >> 8) < frac 2^24 in
+// binary32, where both sides are exact.
+template <int F>
+__device__ __forceinline__ uint32_t sr_code(float a, uint32_t w)
+{
+    const float fu = (float)(w >> 8);
+    if constexpr (F == FMT_E1M2 || F == FMT_INT4) {
+        constexpr float G = grid_max(F);
+        const float t = (F == FMT_E1M2) ? a * 2.0f : a;  // grid units (step 1)
+        const float kl = __builtin_floorf(t);
+        const float frac = t - kl;
+        const uint32_t k = (uint32_t)kl + (fu < frac * 0x1p24f ? 1u : 0u);
+        return a >= G ? 7u : k;
+    } else {
+        if (a >= 6.0f) return 7u;
+        if (a < 1.0f) {
+            const float t = a * 2.0f;
+            const float kl = __builtin_floorf(t);
+            const float frac = t - kl;
+            return (uint32_t)kl + (fu < frac * 0x1p24f ? 1u : 0u);
+        }
+        // a in [1, 6): truncate to one mantissa bit for the lower grid point
+        const uint32_t b = f2u(a);
+        const uint32_t glo_bits = b & 0xFFC00000u;
+        const uint32_t klo = (b >> 22) - 252u;
+        // cell width = 2^(e-1) with e = unbiased exponent of a; frac = (a - g) / width
+        const float inv_w = u2f((255u - (b >> 23)) << 23);  // 2^(128 - biased exponent)
+        const float frac = (a - u2f(glo_bits)) * inv_w;
+        return klo + (fu < frac * 0x1p24f ? 1u : 0u);
+    }
+}
+
+// Grid value of a magnitude code.
+template <int F>
+__device__ __forceinline__ float grid_value(uint32_t k)
+{
+    if constexpr (F == FMT_E1M2) return (float)k * 0.5f;
+    if constexpr (F == FMT_INT4) return (float)k;
+    // E2M1: 0, .5, 1, 1.5, 2, 3, 4, 6
+    const uint32_t e = k >> 1, m = k & 1u;
+    return e == 0 ? (float)m * 0.5f : u2f(((e + 126u) << 23) | (m << 22));
+}
+
+// bf16 bits -> binary32
+__device__ __forceinline__ float bf16lo(uint32_t w) { return u2f(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return u2f(w & 0xFFFF0000u); }
+
+// binary32 -> bf16 bits, nearest even (finite inputs)
+__device__ __forceinline__ uint32_t to_bf16(float f)
+{
+    const uint32_t u = f2u(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace ufp4

@@ -1,0 +1,596 @@
+// quantize.hip -- fused RHT + block quantization kernels for gfx950.
+//
+// What is computed: the 4-bit block quantizer of the pages -- an optional
+// 16-wide random or deterministic Hadamard transform ("蚂蚁集团揭秘" section 四
+// and section 六: Hadamard block = quantization block = 16, fused without
+// intermediate storage; MXFP4 page: deterministic H16), a per-block amax
+// scale (FP32 single level -- UFP4 recipe table of "当你的 GPU 学不会算账";
+// E4M3 with an FP32 tensor scale and IF4's type flag -- IF4 page 3.1-3.2;
+// E8M0 -- MXFP4 page), and rounding to E2M1 / E1M2 / INT4 by round-to-nearest-
+// even or stochastic rounding (IF4 page 6.1; UFP4 recipe: dY only).
+//
+// Layout on the chip.  Row kernel: each lane owns 8 consecutive view elements
+// (one 16-byte bf16 load); the two halves of a 16-chunk sit in lanes 2i and
+// 2i+1, so the span-8 butterfly and the block max cross lanes through DPP
+// (quad_perm), and the 32-element E8M0 blocks use lanes 4i..4i+3.  A 256-lane
+// workgroup handles 4 x 256 consecutive octets (16 KiB of bf16), every wave
+// instruction reading 1 KiB contiguous; codes leave as one 32-bit store per
+// lane.  Column kernel (the transposed bwd_dw operand): each lane loads 16
+// rows x 8 columns (16 loads of 16 bytes, each wave instruction covering eight
+// full 128-byte row segments), transforms and quantizes its 8 column blocks in
+// registers and writes 8 bytes of codes per column; the 4 waves of a
+// workgroup cover 512 rows of 64 columns, so every 128-byte line of the
+// transposed code array is written by one workgroup.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace ufp4 {
+
+constexpr int RT = 256;  // row kernel: threads per workgroup
+constexpr int RU = 4;    // row kernel: octets per lane
+constexpr int CT = 256;  // column kernel: threads per workgroup
+constexpr int CTR = 512; // column kernel: source rows per workgroup
+constexpr int CTC = 64;  // column kernel: source columns per workgroup
+
+enum : int { MODE_QUANT = 0, MODE_AMAX = 1, MODE_RHT = 2 };
+
+// ---------------------------------------------------------------------------
+// Block pipeline shared by both kernels: per-block constants and the element
+// encoder.
+// ---------------------------------------------------------------------------
+struct TensorConst {
+    float alpha;   // two-level tensor scale
+    float den;     // alpha * gridmax
+    float inv_den; // RN(1 / den)
+    bool den_fast;
+};
+
+template <int F, int S>
+__device__ __forceinline__ TensorConst tensor_const(const float *amax)
+{
+    TensorConst t{0.f, 0.f, 0.f, false};
+    if constexpr (S == SC_E4M3) {
+        const float A = *amax;
+        t.alpha = A / (grid_max(F) * 448.0f);
+        t.den = t.alpha * grid_max(F);
+        t.inv_den = t.den == 0.0f ? 0.0f : 1.0f / t.den;
+        t.den_fast = fast_div_ok(t.den);
+    }
+    return t;
+}
+
+struct BlockScale {
+    float s;        // effective scale
+    float inv;      // RN(1/s) (E8M0: exact 2^-E)
+    uint32_t byte;  // stored byte (E4M3 / E8M0)
+    bool fast;      // fast division valid
+};
+
+template <int F, int S>
+__device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
+{
+    BlockScale b;
+    if constexpr (S == SC_FP32) {
+        b.s = div_by_gridmax<F>(m);
+        b.byte = 0;
+        b.inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
+        b.fast = fast_div_ok(b.s);
+    } else if constexpr (S == SC_E4M3) {
+        float delta;
+        if (t.den == 0.0f)
+            delta = 0.0f;
+        else if (t.den_fast && m >= 0x1p-100f)
+            delta = div_fast(m, t.den, t.inv_den);
+        else
+            delta = m / t.den;
+        b.byte = e4m3_encode(delta);
+        b.s = t.alpha * e4m3_decode(b.byte);
+        b.inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
+        b.fast = fast_div_ok(b.s);
+    } else {
+        int e = m == 0.0f ? -127 : __builtin_amdgcn_frexp_expf(m) - 3;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        b.s = __builtin_amdgcn_ldexpf(1.0f, e);
+        b.inv = __builtin_amdgcn_ldexpf(1.0f, -e);
+        b.byte = (uint32_t)(e + 127);
+        b.fast = true;
+    }
+    return b;
+}
+
+// |z| = RN(a / s) for a = |y|.
+template <int S, bool SR>
+__device__ __forceinline__ float scaled_abs(float a, const BlockScale &b)
+{
+    if constexpr (S == SC_E8M0) {
+        return a * b.inv;  // power of two: the product is the rounded quotient
+    } else {
+        float z = b.fast ? div_fast(a, b.s, b.inv) : a / b.s;
+        if constexpr (SR) {
+            if (z == 0.0f && a > 0.0f) z = a / b.s;
+        }
+        return z;
+    }
+}
+
+// Magnitude code of one element (not IF4).
+template <int F, int S, bool SR>
+__device__ __forceinline__ uint32_t elem_code(float a, const BlockScale &b, uint32_t w)
+{
+    const float z = scaled_abs<S, SR>(a, b);
+    if constexpr (SR)
+        return sr_code<F>(z, w);
+    else
+        return rtne_code<F>(z);
+}
+
+// IF4: both candidates for one element; returns the two magnitude codes and
+// the two binary32 squared errors.
+__device__ __forceinline__ void if4_candidates(float a, const BlockScale &b, uint32_t &kf, uint32_t &ki,
+                                               float &ef, float &ei)
+{
+    constexpr float C76 = 7.0f / 6.0f;
+    constexpr float C67 = 6.0f / 7.0f;
+    const float zf = scaled_abs<SC_E4M3, false>(a, b);
+    const float t = a * C76;
+    const float zi = b.fast ? div_fast(t, b.s, b.inv) : t / b.s;
+    kf = rtne_code<FMT_E2M1>(zf);
+    ki = rtne_code<FMT_INT4>(zi);
+    const float xf = grid_value<FMT_E2M1>(kf) * b.s;
+    const float xi = ((float)ki * b.s) * C67;
+    const float df = xf - a, di = xi - a;
+    ef = df * df;
+    ei = di * di;
+}
+
+// ---------------------------------------------------------------------------
+// Row kernel
+// ---------------------------------------------------------------------------
+template <int IN>
+__device__ __forceinline__ int64_t row_offset(const RowArgs &a, int64_t o)
+{
+    if (a.contiguous) return o * 8;
+    const int64_t L8 = a.L >> 3;
+    const int64_t vr = o / L8;
+    return vr * a.ldx + (o - vr * L8) * 8;
+}
+
+template <int IN>
+struct Raw8;
+template <>
+struct Raw8<IN_BF16> {
+    uint4 w;
+};
+template <>
+struct Raw8<IN_F32> {
+    float4 a, b;
+};
+
+template <int IN>
+__device__ __forceinline__ Raw8<IN> load_raw(const RowArgs &a, int64_t o)
+{
+    Raw8<IN> r;
+    const int64_t off = row_offset<IN>(a, o);
+    if constexpr (IN == IN_BF16) {
+        r.w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + off);
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + off);
+        r.a = p[0];
+        r.b = p[1];
+    }
+    return r;
+}
+
+template <int IN>
+__device__ __forceinline__ void unpack(const Raw8<IN> &r, float *v)
+{
+    if constexpr (IN == IN_BF16) {
+        v[0] = bf16lo(r.w.x); v[1] = bf16hi(r.w.x);
+        v[2] = bf16lo(r.w.y); v[3] = bf16hi(r.w.y);
+        v[4] = bf16lo(r.w.z); v[5] = bf16hi(r.w.z);
+        v[6] = bf16lo(r.w.w); v[7] = bf16hi(r.w.w);
+    } else {
+        v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+        v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+    }
+}
+
+// Signs, spans 1/2/4 in registers, span 8 with the partner lane, x 1/4.
+// Lane half 0 holds chunk positions 0..7, half 1 positions 8..15; the span-8
+// butterfly gives half 0 v_i + v_{i+8} and half 1 v_i - v_{i+8} = (-own) + partner.
+template <bool RHT>
+__device__ __forceinline__ void row_transform(float *v, const uint32_t *sgn, uint32_t neg_own)
+{
+    if constexpr (RHT) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = u2f(f2u(v[i]) ^ sgn[i]);
+        fwht8(v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = xor1(v[i]);
+            v[i] = u2f(f2u(v[i]) ^ neg_own) + p;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] * 0.25f;
+    }
+}
+
+template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
+__device__ __forceinline__ void row_octet(const RowArgs &a, int64_t o, float *v, const uint32_t *sgn,
+                                          uint32_t neg_own, const TensorConst &tc, float &lmax)
+{
+    row_transform<RHT>(v, sgn, neg_own);
+    if constexpr (MODE == MODE_AMAX) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
+        return;
+    } else if constexpr (MODE == MODE_RHT) {
+        int64_t off;
+        if (a.ldy == a.L) {
+            off = o * 8;
+        } else {
+            const int64_t L8 = a.L >> 3, vr = o / L8;
+            off = vr * a.ldy + (o - vr * L8) * 8;
+        }
+        if constexpr (OUT == IN_F32) {
+            float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.y) + off);
+            p[0] = make_float4(v[0], v[1], v[2], v[3]);
+            p[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+            uint4 w;
+            w.x = to_bf16(v[0]) | (to_bf16(v[1]) << 16);
+            w.y = to_bf16(v[2]) | (to_bf16(v[3]) << 16);
+            w.z = to_bf16(v[4]) | (to_bf16(v[5]) << 16);
+            w.w = to_bf16(v[6]) | (to_bf16(v[7]) << 16);
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + off) = w;
+        }
+        return;
+    } else {
+        // block amax over 16 (two lanes) or 32 (four lanes)
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        m = fmaxf(m, xor1(m));
+        if constexpr (S == SC_E8M0) m = fmaxf(m, xor2(m));
+        const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S>(m, tc);
+
+        uint32_t packed = 0;
+        uint32_t sbyte = bs.byte;
+        if constexpr (F == FMT_IF4) {
+            uint32_t kf[8], ki[8];
+            float ef[8], ei[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) if4_candidates(fabsf(v[i]), bs, kf[i], ki[i], ef[i], ei[i]);
+            // pairwise sums: (0+1),(2+3),... then pairs of pairs; the span-8
+            // level pairs this lane's sum with the partner's (commutative)
+            float sf = ((ef[0] + ef[1]) + (ef[2] + ef[3])) + ((ef[4] + ef[5]) + (ef[6] + ef[7]));
+            float si = ((ei[0] + ei[1]) + (ei[2] + ei[3])) + ((ei[4] + ei[5]) + (ei[6] + ei[7]));
+            sf = sf + xor1(sf);
+            si = si + xor1(si);
+            const bool use_int = bs.s != 0.0f && si < sf;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t k = use_int ? ki[i] : kf[i];
+                packed |= ((f2u(v[i]) >> 28 & 8u) | k) << (4 * i);
+            }
+            if (bs.s == 0.0f) packed = 0;
+            sbyte |= use_int ? 0x80u : 0u;
+        } else {
+            uint32_t w[8];
+            if constexpr (SR) {
+                const uint4 w0 = sr_words4((uint64_t)o * 8, a.sr_seed, a.sr_stream);
+                const uint4 w1 = sr_words4((uint64_t)o * 8 + 4, a.sr_seed, a.sr_stream);
+                w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+                w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t k = elem_code<F, S, SR>(fabsf(v[i]), bs, SR ? w[i] : 0u);
+                packed |= ((f2u(v[i]) >> 28 & 8u) | k) << (4 * i);
+            }
+            if (bs.s == 0.0f) packed = 0;
+        }
+        reinterpret_cast<uint32_t *>(a.codes)[o] = packed;
+        if constexpr (S == SC_E8M0) {
+            if ((o & 3) == 0) static_cast<uint8_t *>(a.scales)[o >> 2] = (uint8_t)sbyte;
+        } else if constexpr (S == SC_E4M3) {
+            if ((o & 1) == 0) static_cast<uint8_t *>(a.scales)[o >> 1] = (uint8_t)sbyte;
+        } else {
+            if ((o & 1) == 0) static_cast<float *>(a.scales)[o >> 1] = bs.s;
+        }
+    }
+}
+
+template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
+__global__ __launch_bounds__(RT) void row_kernel(const RowArgs a)
+{
+    const int tid = threadIdx.x;
+    const uint32_t half = tid & 1;
+    uint32_t sgn[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sgn[i] = ((a.smask >> (8 * half + i)) & 1u) << 31;
+    const uint32_t neg_own = half << 31;
+    TensorConst tc{0.f, 0.f, 0.f, false};
+    if constexpr (MODE == MODE_QUANT) tc = tensor_const<F == FMT_IF4 ? FMT_E2M1 : F, S>(a.amax);
+    if constexpr (MODE == MODE_QUANT && S == SC_E4M3) {
+        if (blockIdx.x == 0 && tid == 0) *a.tensor_scale = tc.alpha;
+    }
+
+    const int64_t base = (int64_t)blockIdx.x * (RT * RU) + tid;
+    float lmax = 0.0f;
+    Raw8<IN> raw[RU];
+    if (base + (RU - 1) * RT < a.n_oct) {
+#pragma unroll
+        for (int u = 0; u < RU; ++u) raw[u] = load_raw<IN>(a, base + u * RT);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            float v[8];
+            unpack<IN>(raw[u], v);
+            row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, sgn, neg_own, tc, lmax);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+            if (base + u * RT < a.n_oct) raw[u] = load_raw<IN>(a, base + u * RT);
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+            if (base + u * RT < a.n_oct) {
+                float v[8];
+                unpack<IN>(raw[u], v);
+                row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, sgn, neg_own, tc, lmax);
+            }
+    }
+    if constexpr (MODE == MODE_AMAX) {
+        __shared__ float red[RT / 64];
+        float m = lmax;
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        if (tid == 0) {
+            float w = red[0];
+            for (int i = 1; i < RT / 64; ++i) w = fmaxf(w, red[i]);
+            atomicMax(a.amax_out, f2u(w));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Column kernel: the view is the transpose of the source.
+// ---------------------------------------------------------------------------
+template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
+__global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane & 7, b = lane >> 3;
+    const int64_t r0 = (int64_t)blockIdx.y * CTR + wave * 128 + b * 16;  // first source row of this lane
+    const int64_t c0 = (int64_t)blockIdx.x * CTC + g * 8;                // first source column
+    const bool active = r0 < a.R && c0 < a.C;
+
+    TensorConst tc{0.f, 0.f, 0.f, false};
+    if constexpr (MODE == MODE_QUANT) tc = tensor_const<F == FMT_IF4 ? FMT_E2M1 : F, S>(a.amax);
+    if constexpr (MODE == MODE_QUANT && S == SC_E4M3) {
+        if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *a.tensor_scale = tc.alpha;
+    }
+    float lmax = 0.0f;
+
+    // 16 rows x 8 columns, kept as loaded (bf16 pairs / binary32) until each
+    // column is processed
+    uint4 raw[16];
+    if (active) {
+        if constexpr (IN == IN_BF16) {
+            const uint16_t *xp = static_cast<const uint16_t *>(a.x) + r0 * a.ldx + c0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4 *>(xp + i * a.ldx);
+        }
+    }
+
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float v[16];
+        if (active) {
+            if constexpr (IN == IN_BF16) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t w = (j >> 1) == 0 ? raw[i].x : (j >> 1) == 1 ? raw[i].y : (j >> 1) == 2 ? raw[i].z : raw[i].w;
+                    v[i] = (j & 1) ? bf16hi(w) : bf16lo(w);
+                }
+            } else {
+                const float *xp = static_cast<const float *>(a.x) + r0 * a.ldx + c0 + j;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = xp[i * a.ldx];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+        }
+        if (active && RHT) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = u2f(f2u(v[i]) ^ (((a.smask >> i) & 1u) << 31));
+            fwht16_local(v);
+        }
+        const int64_t c = c0 + j;  // view row
+        if constexpr (MODE == MODE_AMAX) {
+            if (active)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
+        } else if constexpr (MODE == MODE_RHT) {
+            if (active) {
+                const int64_t off = c * a.ldy + r0;
+                if constexpr (OUT == IN_F32) {
+                    float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.y) + off);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+                } else {
+                    uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + off);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        p[q] = make_uint4(to_bf16(v[8 * q]) | (to_bf16(v[8 * q + 1]) << 16),
+                                          to_bf16(v[8 * q + 2]) | (to_bf16(v[8 * q + 3]) << 16),
+                                          to_bf16(v[8 * q + 4]) | (to_bf16(v[8 * q + 5]) << 16),
+                                          to_bf16(v[8 * q + 6]) | (to_bf16(v[8 * q + 7]) << 16));
+                }
+            }
+        } else {
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+            if constexpr (S == SC_E8M0) m = fmaxf(m, xor8(m));  // partner lane holds the other 16 rows
+            if (!active) continue;
+            const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S>(m, tc);
+            uint32_t lo = 0, hi = 0;
+            uint32_t sbyte = bs.byte;
+            if constexpr (F == FMT_IF4) {
+                uint32_t kf[16], ki[16];
+                float ef[16], ei[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) if4_candidates(fabsf(v[i]), bs, kf[i], ki[i], ef[i], ei[i]);
+#pragma unroll
+                for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+                    for (int i = 0; i < 16; i += 2 * w) {
+                        ef[i] = ef[i] + ef[i + w];
+                        ei[i] = ei[i] + ei[i + w];
+                    }
+                const bool use_int = bs.s != 0.0f && ei[0] < ef[0];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t code = (f2u(v[i]) >> 28 & 8u) | (use_int ? ki[i] : kf[i]);
+                    if (i < 8) lo |= code << (4 * i); else hi |= code << (4 * (i - 8));
+                }
+                sbyte |= use_int ? 0x80u : 0u;
+            } else {
+                uint32_t w[16];
+                if constexpr (SR) {
+                    const uint64_t n0 = (uint64_t)c * (uint64_t)a.R + (uint64_t)r0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint4 ww = sr_words4(n0 + 4 * q, a.sr_seed, a.sr_stream);
+                        w[4 * q] = ww.x; w[4 * q + 1] = ww.y; w[4 * q + 2] = ww.z; w[4 * q + 3] = ww.w;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t code = (f2u(v[i]) >> 28 & 8u) |
+                                          elem_code<F, S, SR>(fabsf(v[i]), bs, SR ? w[i] : 0u);
+                    if (i < 8) lo |= code << (4 * i); else hi |= code << (4 * (i - 8));
+                }
+            }
+            if (bs.s == 0.0f) lo = hi = 0;
+            *reinterpret_cast<uint2 *>(a.codes + c * (a.R >> 1) + (r0 >> 1)) = make_uint2(lo, hi);
+            if constexpr (S == SC_E8M0) {
+                if ((b & 1) == 0) static_cast<uint8_t *>(a.scales)[c * (a.R >> 5) + (r0 >> 5)] = (uint8_t)sbyte;
+            } else if constexpr (S == SC_E4M3) {
+                static_cast<uint8_t *>(a.scales)[c * (a.R >> 4) + (r0 >> 4)] = (uint8_t)sbyte;
+            } else {
+                static_cast<float *>(a.scales)[c * (a.R >> 4) + (r0 >> 4)] = bs.s;
+            }
+        }
+    }
+    if constexpr (MODE == MODE_AMAX) {
+        __shared__ float red[CT / 64];
+        float m = lmax;
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        if (tid == 0) {
+            float w = red[0];
+            for (int i = 1; i < CT / 64; ++i) w = fmaxf(w, red[i]);
+            atomicMax(a.amax_out, f2u(w));
+        }
+    }
+}
+
+__global__ void fill_u32_kernel(unsigned int *p, unsigned int v) { *p = v; }
+
+// ---------------------------------------------------------------------------
+// Launch helpers: runtime options -> template instance.
+// ---------------------------------------------------------------------------
+template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
+static hipError_t launch_one(int axis, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+{
+    if (axis == 0) {
+        if (ra.n_oct == 0) return hipSuccess;
+        const int64_t wgs = (ra.n_oct + RT * RU - 1) / (RT * RU);
+        hipLaunchKernelGGL((row_kernel<MODE, F, S, SR, IN, RHT, OUT>), dim3((unsigned)wgs), dim3(RT), 0, st, ra);
+    } else {
+        if (ca.R == 0 || ca.C == 0) return hipSuccess;
+        const dim3 grid((unsigned)((ca.C + CTC - 1) / CTC), (unsigned)((ca.R + CTR - 1) / CTR));
+        hipLaunchKernelGGL((col_kernel<MODE, F, S, SR, IN, RHT, OUT>), grid, dim3(CT), 0, st, ca);
+    }
+    return hipGetLastError();
+}
+
+template <int F, int S, bool SR, int IN, bool RHT>
+static hipError_t pick_quant(int axis, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+{
+    return launch_one<MODE_QUANT, F, S, SR, IN, RHT, 0>(axis, ra, ca, st);
+}
+
+template <int F, int S, bool SR>
+static hipError_t pick_in_rht(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+{
+    const bool rht = sp.rht != 0;
+    if (sp.in_dtype == IN_BF16)
+        return rht ? pick_quant<F, S, SR, IN_BF16, true>(sp.axis, ra, ca, st)
+                   : pick_quant<F, S, SR, IN_BF16, false>(sp.axis, ra, ca, st);
+    return rht ? pick_quant<F, S, SR, IN_F32, true>(sp.axis, ra, ca, st)
+               : pick_quant<F, S, SR, IN_F32, false>(sp.axis, ra, ca, st);
+}
+
+template <int F>
+static hipError_t pick_scale_sr(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+{
+    if constexpr (F == FMT_IF4) {
+        return pick_in_rht<FMT_IF4, SC_E4M3, false>(sp, ra, ca, st);
+    } else {
+        if (sp.scale == SC_E8M0) {
+            if constexpr (F == FMT_E2M1) return pick_in_rht<F, SC_E8M0, false>(sp, ra, ca, st);
+            return hipErrorInvalidValue;
+        }
+        if (sp.scale == SC_FP32)
+            return sp.sr ? pick_in_rht<F, SC_FP32, true>(sp, ra, ca, st) : pick_in_rht<F, SC_FP32, false>(sp, ra, ca, st);
+        return sp.sr ? pick_in_rht<F, SC_E4M3, true>(sp, ra, ca, st) : pick_in_rht<F, SC_E4M3, false>(sp, ra, ca, st);
+    }
+}
+
+hipError_t launch_quantize(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+{
+    switch (sp.format) {
+    case FMT_E2M1: return pick_scale_sr<FMT_E2M1>(sp, ra, ca, st);
+    case FMT_E1M2: return pick_scale_sr<FMT_E1M2>(sp, ra, ca, st);
+    case FMT_INT4: return pick_scale_sr<FMT_INT4>(sp, ra, ca, st);
+    case FMT_IF4: return pick_scale_sr<FMT_IF4>(sp, ra, ca, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+{
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, st, sp.axis == 0 ? ra.amax_out : ca.amax_out, 0u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const bool rht = sp.rht != 0;
+    if (sp.in_dtype == IN_BF16)
+        return rht ? launch_one<MODE_AMAX, 0, 0, false, IN_BF16, true, 0>(sp.axis, ra, ca, st)
+                   : launch_one<MODE_AMAX, 0, 0, false, IN_BF16, false, 0>(sp.axis, ra, ca, st);
+    return rht ? launch_one<MODE_AMAX, 0, 0, false, IN_F32, true, 0>(sp.axis, ra, ca, st)
+               : launch_one<MODE_AMAX, 0, 0, false, IN_F32, false, 0>(sp.axis, ra, ca, st);
+}
+
+hipError_t launch_rht(const LaunchSpec &sp, int out_dtype, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+{
+    const bool rht = sp.rht != 0;
+#define UFP4_RHT_CASE(INT, OUTT)                                                                     \
+    if (sp.in_dtype == INT && out_dtype == OUTT)                                                     \
+        return rht ? launch_one<MODE_RHT, 0, 0, false, INT, true, OUTT>(sp.axis, ra, ca, st)         \
+                   : launch_one<MODE_RHT, 0, 0, false, INT, false, OUTT>(sp.axis, ra, ca, st);
+    UFP4_RHT_CASE(IN_BF16, IN_F32)
+    UFP4_RHT_CASE(IN_BF16, IN_BF16)
+    UFP4_RHT_CASE(IN_F32, IN_F32)
+    UFP4_RHT_CASE(IN_F32, IN_BF16)
+#undef UFP4_RHT_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ufp4

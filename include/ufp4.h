@@ -1,0 +1,238 @@
+/*
+ * ufp4.h -- C ABI of libufp4, a 4-bit block quantizer and block-scaled GEMM
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes follows these pages:
+ *   [UFP4-ZC] "当你的 GPU 学不会算账：FP4 训练里那个被忽视了 30 年的几何陷阱"
+ *             (zhichai.net): the E2M1 and E1M2 grids (sections "E2M1：一块刻度
+ *             不均的尺子", "UFP4：换一把尺子"), the UFP4 recipe table (RHT on
+ *             fwd_y/bwd_dx/bwd_dw, stochastic rounding on dY, 1x16 blocks,
+ *             single FP32 scale), the attenuation identity Z_q = a_A a_B Z + noise
+ *             (section "复利效应的反向版本").
+ *   [UFP4-TW] "蚂蚁集团揭秘：为什么给AI'降精度省电'会悄悄让它越来越笨？"
+ *             (techwalker.com): RTNE rounding (section 二), RHT (section 四),
+ *             the recipe (section 五), fused 16-wide RHT + quantize (section 六).
+ *   [MXFP4]   "AMD全新研究揭示：FP4训练不稳定性源于结构误差而非随机性不足"
+ *             (cannews.ca): MXFP4 = 32-element blocks sharing an E8M0 exponent;
+ *             deterministic Hadamard H16.
+ *   [IF4]     "低精度量化技术：IF4自适应数据类型的原理与应用" (bxzpzcl.cn):
+ *             block scaling (2.1), the format table (2.2), IF4's type flag in
+ *             the E4M3 scale's sign bit with 7/6 and 6/7 INT4 scaling (3.1.1),
+ *             the two-level scale alpha = max|X|/(6x448),
+ *             Delta = max|X_block|/(alpha x 6) (3.2), stochastic rounding (6.1).
+ *   [UQ]      "FP4 训练 vs FP4 推理" (reports.10n1j.top): FP4 tensors with UE8M0
+ *             group scales on CDNA4's native scaled-MFMA path (UltraQuant).
+ *
+ * Conventions shared by every call
+ *   - Device pointers are HIP device memory owned by the caller; the library
+ *     allocates nothing, keeps no pointer after a call returns and has no
+ *     global state except the per-thread last HIP error.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; results are ordered by the stream.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     validation error nothing is written and a negative code is returned.
+ *   - Inputs must be finite.  Outputs for NaN/Inf inputs are unspecified.
+ *   - Element types: UFP4_BF16 (bfloat16) or UFP4_F32 (binary32).
+ *
+ * Quantization view
+ *   A quantization runs along rows (UFP4_ROW) or down columns (UFP4_COL) of a
+ *   row-major source x[rows][ldx].  Its "view" has V rows of L elements and the
+ *   blocks run along view rows:
+ *     UFP4_ROW: V = rows, L = cols, view(v, l) = x[v][l]
+ *     UFP4_COL: V = cols, L = rows, view(v, l) = x[l][v]   (the transpose)
+ *   so a column quantization of x is bit-identical to the row quantization of
+ *   x^T.  Each GEMM operand is quantized along its contraction axis.
+ *   Stored layout (row-major, contiguous):
+ *     codes  uint8[V][L/2]: byte j holds elements 2j (low nibble) and 2j+1
+ *            (high nibble); a nibble is sign<<3 | magnitude code k (0..7)
+ *     scales float[V][L/16] (UFP4_SCALE_FP32), uint8[V][L/16] (UFP4_SCALE_E4M3,
+ *            E4M3FN byte; for IF4 bit 7 is the type flag, 1 = INT4), or
+ *            uint8[V][L/32] (UFP4_SCALE_E8M0, biased exponent, value 2^(b-127))
+ *     tensor_scale float[1]: alpha of the two-level scale (E4M3 only)
+ *   Magnitude codes: E2M1 k -> {0,.5,1,1.5,2,3,4,6}; E1M2 k -> k/2; INT4 k -> k.
+ *
+ * Arithmetic (identical to the CPU oracle, bit for bit)
+ *   binary32 with round-to-nearest-even, no contraction, denormals kept.
+ *   y    = RHT(x): per 16-element chunk of a view row, v = d (.) x, a 16-point
+ *          Walsh-Hadamard butterfly with spans 1,2,4,8 in that order, then x 1/4.
+ *          d_i = -1 iff bit i of Philox4x32-10 word 0 at key = rht_seed,
+ *          counter = (0, 0, 0x52485400, 0); d = +1 for UFP4_RHT_DETERMINISTIC.
+ *   m    = max |y| over the block.
+ *   FP32 scale: s = m / gridmax (gridmax 6, 3.5, 7 for E2M1, E1M2, INT4).
+ *   E4M3 scale: alpha = A / (gridmax x 448), A = max |y| over the tensor;
+ *          Delta = m / (alpha x gridmax) rounded to E4M3FN (nearest, ties to
+ *          even, saturating at 448); s = alpha x Delta_q.
+ *   E8M0 scale: s = 2^E, E = floor(log2 m) - 2 clamped to [-127, 127]
+ *          (m = 0 gives E = -127).
+ *   z    = y / s (correctly rounded); s = 0 gives code 0.
+ *   RTNE: nearest grid point, ties to the even code, saturating at gridmax.
+ *   SR:   k = k_lo + (u < frac) with u = (w >> 8) 2^-24, w = Philox4x32-10 word
+ *          n mod 4 at key = sr_seed, counter = (lo32(n/4), hi32(n/4), sr_stream, 0),
+ *          n = v L + l the element's index in the view.
+ *   IF4:  FP4 candidate = RTNE of y/s on E2M1; INT4 candidate k = rint((y x 7/6)/s)
+ *          clamped to 7, dequantized as (k x s) x 6/7; the candidate with the
+ *          smaller binary32 squared error (pairwise sum) wins, ties to FP4.
+ *   Dequantization: x_hat = v x s (IF4 INT4 blocks: (k x s) x 6/7).
+ */
+#ifndef UFP4_H
+#define UFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ------------------------------------------------------- */
+#define UFP4_OK 0
+#define UFP4_ERR_INVALID_ARG (-1) /* null pointer, unknown enum value, bad dtype     */
+#define UFP4_ERR_SHAPE (-2)       /* sizes not multiples of the block / tile rules  */
+#define UFP4_ERR_ALIGN (-3)       /* pointer not 16-byte aligned, ld not multiple of 8 */
+#define UFP4_ERR_UNSUPPORTED (-4) /* combination of options the library does not run */
+#define UFP4_ERR_WORKSPACE (-5)   /* workspace missing or smaller than required      */
+#define UFP4_ERR_HIP (-6)         /* a HIP launch failed; see ufp4_last_hip_error()  */
+
+/* ---- enumerations ------------------------------------------------------ */
+enum { UFP4_E2M1 = 0, UFP4_E1M2 = 1, UFP4_INT4 = 2, UFP4_IF4 = 3 };
+enum { UFP4_SCALE_FP32 = 0, UFP4_SCALE_E4M3 = 1, UFP4_SCALE_E8M0 = 2 };
+enum { UFP4_RHT_NONE = 0, UFP4_RHT_RANDOM = 1, UFP4_RHT_DETERMINISTIC = 2 };
+enum { UFP4_RTNE = 0, UFP4_SR = 1 };
+enum { UFP4_ROW = 0, UFP4_COL = 1 };
+enum { UFP4_BF16 = 0, UFP4_F32 = 1 };
+enum { UFP4_GEMM_NATIVE_MXFP4 = 0, UFP4_GEMM_DEQUANT_BF16 = 1 };
+enum { UFP4_OP_STATS = 0, UFP4_OP_QGEMM = 1, UFP4_OP_ETA = 2 };
+
+/* Supported combinations (anything else returns UFP4_ERR_UNSUPPORTED):
+ *   E2M1 with FP32/16, E4M3/16 or E8M0/32; E1M2 and INT4 with FP32/16 or E4M3/16;
+ *   IF4 with E4M3/16 only.  SR with E2M1, E1M2, INT4 under FP32 or E4M3 scales.
+ *   The RHT is 16 wide; a 32-element block holds two transformed chunks. */
+typedef struct ufp4_config {
+    int32_t format;     /* UFP4_E2M1 / UFP4_E1M2 / UFP4_INT4 / UFP4_IF4          */
+    int32_t scale;      /* UFP4_SCALE_*                                        */
+    int32_t block;      /* 16 (FP32, E4M3) or 32 (E8M0)                        */
+    int32_t rht;        /* UFP4_RHT_*                                          */
+    int32_t rounding;   /* UFP4_RTNE / UFP4_SR                                 */
+    int32_t axis;       /* UFP4_ROW / UFP4_COL                                 */
+    uint64_t rht_seed;  /* key of the sign diagonal                            */
+    uint64_t sr_seed;   /* key of the stochastic-rounding stream               */
+    uint32_t sr_stream; /* third Philox counter word (0 row, 1 column by convention) */
+    uint32_t reserved;  /* must be 0                                           */
+} ufp4_config;
+
+/* A quantized tensor.  rows/cols are the LOGICAL SOURCE shape; buffers hold
+ * the view layout described above.  All pointers are device memory owned by
+ * the caller. */
+typedef struct ufp4_qtensor {
+    uint8_t *codes;
+    void *scales;
+    float *tensor_scale; /* required for UFP4_SCALE_E4M3, ignored otherwise */
+    int64_t rows;
+    int64_t cols;
+    ufp4_config cfg;
+} ufp4_qtensor;
+
+/* Statistics report ([UFP4-ZC] SQNR and signal factor; [UFP4-TW] 二 per-cell
+ * bias; [IF4] 6.2 FP4/INT4 shares).  Filled on the host from the sums. */
+typedef struct ufp4_stats_report {
+    double n;             /* elements                                          */
+    double sqnr_db;       /* 10 log10(sum y^2 / sum (x_hat - y)^2)                */
+    double alpha;         /* sum x_hat y / sum y^2 (signal factor)                */
+    double mse;           /* sum (x_hat - y)^2 / n                                */
+    double mean_err;      /* sum (x_hat - y) / n                                  */
+    double mean_shrink;   /* sum sign(y)(x_hat - y) / n (< 0: shrinkage)          */
+    double int4_share;    /* IF4: INT4 blocks / blocks                            */
+    double counts[2][8];  /* [type][k]: magnitude-code counts (type 1 = IF4 INT4)  */
+    double bucket_bias[2][8]; /* mean (g[k] - |z|) per code, grid units (NaN if empty) */
+} ufp4_stats_report;
+
+#define UFP4_NSUMS 48
+/* Layout of the 48 binary64 sums written by ufp4_stats:
+ *  [0] n  [1] sum y^2  [2] sum e^2  [3] sum e  [4] sum sign(y) e  [5] sum x_hat y
+ *  [6] sum |e|  [7] blocks  [8] INT4 blocks
+ *  [16 + 8t + k] count of code k in blocks of type t; [32 + 8t + k] sum (g_t[k] - |z|)
+ *  with e = x_hat - y (binary64 of binary32 values). */
+
+/* ---- calls --------------------------------------------------------------- */
+
+/* Standalone 16-wide RHT ([UFP4-TW] 六: the unfused variant, transform then
+ * quantize).  Writes y = view of RHT(x) as y[V][ldy] in y_dtype (UFP4_F32 keeps
+ * every bit; UFP4_BF16 rounds to nearest even).  Sizes: L multiple of 16;
+ * x, y 16-byte aligned; ldx, ldy multiples of 8 (element counts); for UFP4_COL
+ * also cols multiple of 8.  rht_kind UFP4_RHT_NONE copies (and converts). */
+int ufp4_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int axis, int rht_kind,
+             uint64_t rht_seed, void *y, int y_dtype, int64_t ldy, void *stream);
+
+/* Tensor amax after the transform named by cfg (rht, rht_seed, axis): writes
+ * max |y| to amax[0] (device float).  Needed before a UFP4_SCALE_E4M3
+ * quantization ([IF4] 3.2: alpha = max|X| / (6 x 448)).  Several devices can
+ * combine their amax with a MAX all-reduce before quantizing their shards. */
+int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+              float *amax, void *stream);
+
+/* Block quantization (all steps fused in one kernel: load, signs, FWHT, block
+ * amax, scale, RTNE/SR or IF4 selection, nibble packing, stores).
+ * out->codes, out->scales (and out->tensor_scale for E4M3) must point to
+ * buffers of the sizes above; out->rows/cols/cfg are filled in by the call.
+ * amax: device float from ufp4_amax (required for E4M3, ignored otherwise).
+ * Shapes: L multiple of the block; UFP4_COL also needs cols multiple of 8;
+ * x 16-byte aligned, ldx multiple of 8 and >= cols. */
+int ufp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+                  const float *amax, ufp4_qtensor *out, void *stream);
+
+/* Dequantization ([IF4] 3.1.1: code x scale, x 6/7 for INT4 blocks) of the
+ * view: y[V][ldy] in y_dtype.  inverse_rht != 0 undoes the transform (FWHT x
+ * 1/4, then the signs), giving the source orientation of each view row. */
+int ufp4_dequantize(const ufp4_qtensor *q, int inverse_rht, void *y, int y_dtype, int64_t ldy, void *stream);
+
+/* Quantization statistics of q against the source x it was made from (same
+ * dtype/ldx as the quantize call).  Writes UFP4_NSUMS doubles to sums (device).
+ * ws: device workspace of ufp4_workspace_size(UFP4_OP_STATS, ...) bytes. */
+int ufp4_stats(const void *x, int x_dtype, int64_t ldx, const ufp4_qtensor *q, double *sums, void *ws,
+               size_t ws_bytes, void *stream);
+
+/* Host-only: derive the report from sums copied to the host. */
+void ufp4_stats_finalize(const double *sums_host, ufp4_stats_report *report);
+
+/* Block-scaled GEMM Z = deq(A) deq(B)^T, fp32 output c[M][ldc].
+ * a: M x K and b: N x K, both quantized along K (UFP4_ROW of the K-major
+ * matrices), same rht kind and seed (a shared sign diagonal keeps A B^T).
+ * mode UFP4_GEMM_NATIVE_MXFP4: E2M1/E8M0/32 operands on CDNA4's scaled MFMA
+ *   ([UQ]; [MXFP4]); products exact, fp32 accumulation.
+ * mode UFP4_GEMM_DEQUANT_BF16: any non-IF4 operands; x_hat rounded to bf16
+ *   (nearest even), bf16 MFMA, fp32 accumulation ([UQ]: software E1M2/INT4).
+ * Sizes: M, N multiples of 256; K multiple of 128; ldc multiple of 4, >= N.
+ * ws: ufp4_workspace_size(UFP4_OP_QGEMM, ...) bytes (0 for NATIVE_MXFP4). */
+int ufp4_qgemm(const ufp4_qtensor *a, const ufp4_qtensor *b, int mode, float *c, int64_t ldc, void *ws,
+               size_t ws_bytes, void *stream);
+
+/* Plain bf16 GEMM Z = A B^T, fp32 accumulation and output (the unquantized
+ * product the attenuation eta is measured against).  A[M][lda], B[N][ldb] bf16;
+ * M, N multiples of 256, K multiple of 64; lda, ldb multiples of 8. */
+int ufp4_gemm_bf16(const void *a, const void *b, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                   float *c, int64_t ldc, void *stream);
+
+/* Attenuation sums ([UFP4-ZC] "复利效应的反向版本": eta = <Zq,Z>/<Z,Z>):
+ * writes sums[0] = <Zq,Z>, sums[1] = <Z,Z>, sums[2] = ||Zq - Z||^2 (binary64,
+ * device) for M x N fp32 matrices with row stride ld.
+ * ws: ufp4_workspace_size(UFP4_OP_ETA, ...) bytes. */
+int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, double *sums, void *ws,
+             size_t ws_bytes, void *stream);
+
+/* Workspace bytes for op (UFP4_OP_*) on a rows x cols source (QGEMM: rows = M+N,
+ * cols = K; ETA: rows = M, cols = N).  cfg may be NULL except for QGEMM. */
+size_t ufp4_workspace_size(int op, int64_t rows, int64_t cols, const ufp4_config *cfg);
+
+/* Text of an error code (static storage). */
+const char *ufp4_strerror(int code);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int ufp4_last_hip_error(void);
+
+/* Library version, (major << 16) | minor. */
+int ufp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UFP4_H */

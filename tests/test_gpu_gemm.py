@@ -1,0 +1,82 @@
+"""GPU parity of the block-scaled GEMMs, the bf16 GEMM and the attenuation
+sums against the oracle's binary64 products of its own dequantized operands
+(relative Frobenius error within 1e-3), through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+from helpers import host, oracle_cfg, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def lib():
+    import block_scaled_bit_ufp4_amd as U
+    return U
+
+
+def rel_fro(got, want):
+    return float(np.linalg.norm(got.astype(np.float64) - want) / np.linalg.norm(want))
+
+
+def oracle_operand(x_bits, ocfg, bf16=False):
+    q = O.quantize(x_bits, ocfg)
+    d = O.dequantize(q, ocfg, x_bits.shape)
+    return O.bf16_round(d) if bf16 else d
+
+
+SHAPES = [(256, 256, 128), (512, 256, 384), (256, 768, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("rht", ["none", "random"])
+def test_mxfp4_gemm_matches_oracle(M, N, K, rht):
+    U = lib()
+    a = S.normal(M, K, 1.0, 0, "gemm_a")
+    b = S.normal(N, K, 1.0, 0, "gemm_b")
+    cfg = U.Cfg("e2m1", "e8m0", 32, rht=rht, rht_seed=11)
+    qa = U.ufp4_quantize(to_device_bf16(a), cfg)
+    qb = U.ufp4_quantize(to_device_bf16(b), cfg)
+    z = host(U.ufp4_qgemm(qa, qb, "mxfp4"))
+    ocfg = oracle_cfg(cfg)
+    want = O.gemm_nt(oracle_operand(a, ocfg), oracle_operand(b, ocfg))
+    assert rel_fro(z, want) < 1e-3, rel_fro(z, want)
+    assert rel_fro(z, want) < 1e-5  # exact products, binary32 sums
+
+
+@pytest.mark.parametrize("fmt", ["e1m2", "int4", "e2m1"])
+def test_dequant_bf16_gemm_matches_oracle(fmt):
+    U = lib()
+    M, N, K = 256, 512, 256
+    a = S.normal(M, K, 1.0, 1, "gemm_a")
+    b = S.normal(N, K, 1.0, 1, "gemm_b")
+    cfg = U.Cfg(fmt, "fp32", rht="random", rht_seed=3)
+    qa = U.ufp4_quantize(to_device_bf16(a), cfg)
+    qb = U.ufp4_quantize(to_device_bf16(b), cfg)
+    z = host(U.ufp4_qgemm(qa, qb, "bf16"))
+    ocfg = oracle_cfg(cfg)
+    want = O.gemm_nt(oracle_operand(a, ocfg, bf16=True), oracle_operand(b, ocfg, bf16=True))
+    assert rel_fro(z, want) < 1e-5, rel_fro(z, want)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (512, 256, 320)])
+def test_bf16_gemm_matches_oracle(M, N, K):
+    U = lib()
+    a = S.normal(M, K, 1.0, 2, "gemm_a")
+    b = S.normal(N, K, 1.0, 2, "gemm_b")
+    z = host(U.ufp4_gemm_bf16(to_device_bf16(a), to_device_bf16(b)))
+    want = O.gemm_nt(S.bf16_bits_to_f32(a), S.bf16_bits_to_f32(b))
+    assert rel_fro(z, want) < 1e-5
+
+
+def test_eta_sums():
+    U = lib()
+    import torch
+    rng = np.random.default_rng(0)
+    z = np.float32(rng.standard_normal((256, 512)))
+    zq = np.float32(z * 0.97 + rng.standard_normal(z.shape) * 0.1)
+    sums = host(U.ufp4_eta(torch.from_numpy(zq).cuda(), torch.from_numpy(z).cuda()))
+    z64, q64 = z.astype(np.float64), zq.astype(np.float64)
+    want = [np.sum(q64 * z64), np.sum(z64 * z64), np.sum((q64 - z64) ** 2)]
+    np.testing.assert_allclose(sums, want, rtol=1e-12)

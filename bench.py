@@ -103,12 +103,13 @@ def main():
     cfgs = [U.Cfg("e2m1", "e4m3", rht="random", rht_seed=0), U.Cfg("e1m2", "e4m3", rht="random", rht_seed=0)]
     outs = [[U.alloc_qtensor(ROWS, COLS, c) for c in cfgs] for _ in range(args.copies)]
     amaxes = [[torch.zeros(1, dtype=torch.float32, device=dev) for _ in cfgs] for _ in range(args.copies)]
+    amax_ws = torch.empty(U.ufp4_workspace_size(U.OP_AMAX, ROWS, COLS, cfgs[0]), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
         j = i % args.copies
         for f, cfg in enumerate(cfgs):
-            U.ufp4_amax(xs[j], cfg, out=amaxes[j][f])
+            U.ufp4_amax(xs[j], cfg, out=amaxes[j][f], ws=amax_ws)
             if ev is not None:
                 ev[f][0].record(stream)
             U.ufp4_quantize(xs[j], cfg, amax=amaxes[j][f], out=outs[j][f])

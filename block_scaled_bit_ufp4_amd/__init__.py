@@ -29,7 +29,7 @@ RHTS = {"none": 0, "random": 1, "det": 2}
 ROUNDINGS = {"rtne": 0, "sr": 1}
 AXES = {"row": 0, "col": 1}
 GEMM_MODES = {"mxfp4": 0, "bf16": 1}
-OP_STATS, OP_QGEMM, OP_ETA = 0, 1, 2
+OP_STATS, OP_QGEMM, OP_ETA, OP_AMAX = 0, 1, 2, 3
 NSUMS = 48
 BF16, F32 = 0, 1
 
@@ -58,7 +58,7 @@ class ufp4_stats_report(C.Structure):
 _lib = C.CDLL(LIB_PATH)
 _p, _i64, _u64, _i32, _sz = C.c_void_p, C.c_int64, C.c_uint64, C.c_int, C.c_size_t
 _lib.ufp4_rht.argtypes = [_p, _i32, _i64, _i64, _i64, _i32, _i32, _u64, _p, _i32, _i64, _p]
-_lib.ufp4_amax.argtypes = [_p, _i32, _i64, _i64, _i64, C.POINTER(ufp4_config), _p, _p]
+_lib.ufp4_amax.argtypes = [_p, _i32, _i64, _i64, _i64, C.POINTER(ufp4_config), _p, _p, _sz, _p]
 _lib.ufp4_quantize.argtypes = [_p, _i32, _i64, _i64, _i64, C.POINTER(ufp4_config), _p, C.POINTER(ufp4_qtensor), _p]
 _lib.ufp4_dequantize.argtypes = [C.POINTER(ufp4_qtensor), _i32, _p, _i32, _i64, _p]
 _lib.ufp4_stats.argtypes = [_p, _i32, _i64, C.POINTER(ufp4_qtensor), _p, _p, _sz, _p]
@@ -177,12 +177,16 @@ def ufp4_rht(x: torch.Tensor, axis: str = "row", rht: str = "random", seed: int 
     return y
 
 
-def ufp4_amax(x: torch.Tensor, cfg: Cfg, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+def ufp4_amax(x: torch.Tensor, cfg: Cfg, out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(ufp4_workspace_size(OP_AMAX, x.shape[0], x.shape[1], cfg), dtype=torch.uint8,
+                         device=x.device)
     c = cfg.c()
     rc = _lib.ufp4_amax(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], _ld(x), C.byref(c), out.data_ptr(),
-                        _stream(stream))
+                        ws.data_ptr(), ws.numel(), _stream(stream))
     _check(rc, "ufp4_amax")
     return out
 

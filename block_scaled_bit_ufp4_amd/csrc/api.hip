@@ -128,6 +128,11 @@ size_t ufp4_workspace_size(int op, int64_t rows, int64_t cols, const ufp4_config
     switch (op) {
     case UFP4_OP_STATS: return (size_t)STATS_WGS * UFP4_NSUMS * sizeof(double);
     case UFP4_OP_ETA: return (size_t)ETA_WGS * 3 * sizeof(double);
+    case UFP4_OP_AMAX: {
+        const int axis = cfg ? cfg->axis : UFP4_ROW;
+        const int64_t t = amax_tiles(axis, rows, cols);
+        return (size_t)(t > 0 ? t : 1) * sizeof(float);
+    }
     case UFP4_OP_QGEMM:
         // dequantize-to-bf16 path: both operands as bf16 ((M + N) x K)
         if (cfg && cfg->scale != UFP4_SCALE_E8M0) return (size_t)(rows * cols * 2);
@@ -162,20 +167,23 @@ int ufp4_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx
 }
 
 int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
-              float *amax, void *stream)
+              float *amax, void *ws, size_t ws_bytes, void *stream)
 {
     int rc = check_config(cfg);
     if (rc) return rc;
     if (!amax) return UFP4_ERR_INVALID_ARG;
     rc = check_source(x, x_dtype, rows, cols, ldx, cfg->axis, 16);
     if (rc) return rc;
+    const size_t need = ufp4_workspace_size(UFP4_OP_AMAX, rows, cols, cfg);
+    if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
+    if ((uintptr_t)ws & 3u) return UFP4_ERR_ALIGN;
     RowArgs ra;
     ColArgs ca;
     fill_args(x, x_dtype, rows, cols, ldx, cfg->axis, sign_mask(cfg->rht, cfg->rht_seed), ra, ca);
-    ra.amax_out = reinterpret_cast<unsigned int *>(amax);
-    ca.amax_out = reinterpret_cast<unsigned int *>(amax);
+    ra.partials = static_cast<float *>(ws);
+    ca.partials = static_cast<float *>(ws);
     LaunchSpec sp{0, 0, 0, x_dtype, cfg->rht != UFP4_RHT_NONE, cfg->axis};
-    return hip_fail(launch_amax(sp, ra, ca, (hipStream_t)stream));
+    return hip_fail(launch_amax(sp, ra, ca, amax, (hipStream_t)stream));
 }
 
 int ufp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,

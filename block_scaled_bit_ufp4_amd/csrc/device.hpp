@@ -122,6 +122,16 @@ __device__ __forceinline__ float div_fast(float a, float s, float inv)
     return __builtin_fmaf(r, inv, q);
 }
 
+// Signed form: RN(y / s) for either sign, q = y*inv, r = q*s - y (exact),
+// z = q - r*inv.  Writing the correction as a subtraction keeps the sign of a
+// zero quotient (y = -0 gives -0, as the division does).
+__device__ __forceinline__ float sdiv_fast(float y, float s, float inv)
+{
+    const float q = y * inv;
+    const float r = __builtin_fmaf(q, s, -y);
+    return __builtin_fmaf(-r, inv, q);
+}
+
 // RN(m / G) for a constant G (the grid maximum), m >= 0.
 template <int F>
 __device__ __forceinline__ float div_by_gridmax(float m)
@@ -216,6 +226,46 @@ __device__ __forceinline__ uint32_t sr_code(float a, uint32_t w)
         const float frac = (a - u2f(glo_bits)) * inv_w;
         return klo + (fu < frac * 0x1p24f ? 1u : 0u);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Hardware converts (verified on gfx950 against the software definitions for
+// every finite binary32: the FP4 convert equals the nearest-even E2M1 code
+// with saturation at 6; the FP8 convert with scale 2^8 (2^9) returns
+// sign << 7 | rint(2|z|) (rint(|z|)) for |z| < 7.75 (15.5).  Both convert
+// pairs: src0 to the low field.  The scale operand only contributes its
+// power-of-two exponent (the convert divides by it).
+// ---------------------------------------------------------------------------
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+
+// 8 signed scaled values -> 8 E2M1 codes (element i in bits 4i..4i+3).
+__device__ __forceinline__ uint32_t pack8_e2m1(const float *z)
+{
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, z[0], z[1], 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, z[2], z[3], 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, z[4], z[5], 1.0f, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, z[6], z[7], 1.0f, 3);
+    return p;
+}
+
+// 8 signed scaled values on the uniform grids -> 8 codes: the FP8 convert
+// gives bytes sign<<7 | k; the sign moves to bit 3 and byte pairs fold into
+// nibble pairs.  Requires |z| <= gridmax (+ less than half a step).
+template <int F>
+__device__ __forceinline__ uint32_t pack8_uniform(const float *z)
+{
+    constexpr float SC = F == FMT_E1M2 ? 256.0f : 512.0f;
+    v2i16 w0 = {0, 0}, w1 = {0, 0};
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, z[0], z[1], SC, false);
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, z[2], z[3], SC, true);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, z[4], z[5], SC, false);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, z[6], z[7], SC, true);
+    const uint32_t d0 = __builtin_bit_cast(uint32_t, w0), d1 = __builtin_bit_cast(uint32_t, w1);
+    const uint32_t n0 = ((d0 >> 4) & 0x08080808u) | (d0 & 0x07070707u);
+    const uint32_t n1 = ((d1 >> 4) & 0x08080808u) | (d1 & 0x07070707u);
+    const uint32_t t0 = n0 | (n0 >> 4), t1 = n1 | (n1 >> 4);
+    return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
 }
 
 // Grid value of a magnitude code.

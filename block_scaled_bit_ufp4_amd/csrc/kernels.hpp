@@ -23,7 +23,7 @@ struct RowArgs {
     uint32_t sr_stream;
     void *y;              // RHT output
     int64_t ldy;
-    unsigned int *amax_out;
+    float *partials;      // amax: one partial maximum per workgroup
 };
 
 // Column kernel: the view is the transpose of x[R][C].
@@ -40,7 +40,7 @@ struct ColArgs {
     uint32_t sr_stream;
     void *y;              // [C][ldy]
     int64_t ldy;
-    unsigned int *amax_out;
+    float *partials;      // amax: one partial maximum per workgroup
 };
 
 struct LaunchSpec {
@@ -53,7 +53,8 @@ struct LaunchSpec {
 };
 
 hipError_t launch_quantize(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, hipStream_t st);
-hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, hipStream_t st);
+hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, float *amax, hipStream_t st);
+int64_t amax_tiles(int axis, int64_t rows, int64_t cols);  // partial maxima the amax pass writes
 hipError_t launch_rht(const LaunchSpec &sp, int out_dtype, const RowArgs &ra, const ColArgs &ca, hipStream_t st);
 
 // Dequantization of a view (row-major codes), optional inverse transform.

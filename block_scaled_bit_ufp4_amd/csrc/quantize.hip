@@ -21,6 +21,13 @@
 // registers and writes 8 bytes of codes per column; the 4 waves of a
 // workgroup cover 512 rows of 64 columns, so every 128-byte line of the
 // transposed code array is written by one workgroup.
+//
+// Arithmetic.  For bf16 sources the transform's final x 1/4 is exact (every
+// partial sum is a multiple of 2^-133), so it is folded into the divisor:
+// z = RN(y / s) = RN(v / 4s) with v the unscaled butterfly output.  The
+// division is Markstein's reciprocal-and-correct sequence (exact inside the
+// scale range checked per block, IEEE division outside it), and the codes come
+// from the hardware FP4/FP8 converts, which equal the nearest-even definition.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -35,8 +42,7 @@ constexpr int CTC = 64;  // column kernel: source columns per workgroup
 enum : int { MODE_QUANT = 0, MODE_AMAX = 1, MODE_RHT = 2 };
 
 // ---------------------------------------------------------------------------
-// Block pipeline shared by both kernels: per-block constants and the element
-// encoder.
+// Per-tensor and per-block constants
 // ---------------------------------------------------------------------------
 struct TensorConst {
     float alpha;   // two-level tensor scale
@@ -60,80 +66,111 @@ __device__ __forceinline__ TensorConst tensor_const(const float *amax)
 }
 
 struct BlockScale {
-    float s;        // effective scale
-    float inv;      // RN(1/s) (E8M0: exact 2^-E)
+    float s;        // effective scale (x_hat = value * s)
+    float sd;       // divisor applied to the kernel's values (4 s when x 1/4 is folded)
+    float invd;     // RN(1 / sd)
     uint32_t byte;  // stored byte (E4M3 / E8M0)
-    bool fast;      // fast division valid
+    bool fast;      // Markstein division valid (or s == 0)
 };
 
-template <int F, int S>
+// m: block amax of the transformed values y.  FOLD: the kernel holds 4y.
+template <int F, int S, bool FOLD>
 __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
 {
     BlockScale b;
-    if constexpr (S == SC_FP32) {
-        b.s = div_by_gridmax<F>(m);
-        b.byte = 0;
-        b.inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
-        b.fast = fast_div_ok(b.s);
-    } else if constexpr (S == SC_E4M3) {
-        float delta;
-        if (t.den == 0.0f)
-            delta = 0.0f;
-        else if (t.den_fast && m >= 0x1p-100f)
-            delta = div_fast(m, t.den, t.inv_den);
-        else
-            delta = m / t.den;
-        b.byte = e4m3_encode(delta);
-        b.s = t.alpha * e4m3_decode(b.byte);
-        b.inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
-        b.fast = fast_div_ok(b.s);
-    } else {
+    if constexpr (S == SC_E8M0) {
         int e = m == 0.0f ? -127 : __builtin_amdgcn_frexp_expf(m) - 3;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
         b.s = __builtin_amdgcn_ldexpf(1.0f, e);
-        b.inv = __builtin_amdgcn_ldexpf(1.0f, -e);
+        b.sd = b.s;
+        b.invd = __builtin_amdgcn_ldexpf(1.0f, -e - (FOLD ? 2 : 0));
         b.byte = (uint32_t)(e + 127);
         b.fast = true;
+        return b;
+    } else {
+        if constexpr (S == SC_FP32) {
+            b.s = div_by_gridmax<F>(m);
+            b.byte = 0;
+        } else {
+            float delta;
+            if (t.den == 0.0f)
+                delta = 0.0f;
+            else if (t.den_fast && m >= 0x1p-100f)
+                delta = div_fast(m, t.den, t.inv_den);
+            else
+                delta = m / t.den;
+            b.byte = e4m3_encode(delta);
+            b.s = t.alpha * e4m3_decode(b.byte);
+        }
+        const float inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
+        b.sd = FOLD ? b.s * 4.0f : b.s;
+        b.invd = FOLD ? inv * 0.25f : inv;
+        b.fast = b.s == 0.0f || (b.sd >= 0x1p-75f && b.sd <= 0x1p125f);
+        return b;
     }
-    return b;
 }
 
-// |z| = RN(a / s) for a = |y|.
-template <int S, bool SR>
-__device__ __forceinline__ float scaled_abs(float a, const BlockScale &b)
+// Signed scaled values z_i = RN(y_i / s) for 8 kernel values v_i (v = 4y when
+// FOLD).  SR: quotients below 2^-100 are redone by division (their only
+// influence is whether they are zero).
+template <int S, bool FOLD, bool SR>
+__device__ __forceinline__ void scaled8(const float *v, const BlockScale &b, float *z)
 {
     if constexpr (S == SC_E8M0) {
-        return a * b.inv;  // power of two: the product is the rounded quotient
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = v[i] * b.invd;
+        return;
     } else {
-        float z = b.fast ? div_fast(a, b.s, b.inv) : a / b.s;
-        if constexpr (SR) {
-            if (z == 0.0f && a > 0.0f) z = a / b.s;
+        if (b.fast) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) z[i] = sdiv_fast(v[i], b.sd, b.invd);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) z[i] = (FOLD ? v[i] * 0.25f : v[i]) / b.s;
         }
-        return z;
+        if constexpr (SR) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (fabsf(z[i]) < 0x1p-100f && v[i] != 0.0f && b.s != 0.0f) z[i] = (FOLD ? v[i] * 0.25f : v[i]) / b.s;
+        }
     }
 }
 
-// Magnitude code of one element (not IF4).
-template <int F, int S, bool SR>
-__device__ __forceinline__ uint32_t elem_code(float a, const BlockScale &b, uint32_t w)
+// Codes of 8 elements for the non-IF4 formats.
+template <int F, int S, bool FOLD, bool SR>
+__device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b, const uint32_t *w)
 {
-    const float z = scaled_abs<S, SR>(a, b);
-    if constexpr (SR)
-        return sr_code<F>(z, w);
-    else
-        return rtne_code<F>(z);
+    float z[8];
+    scaled8<S, FOLD, SR>(v, b, z);
+    uint32_t packed;
+    if constexpr (SR) {
+        packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            packed |= ((f2u(z[i]) >> 28 & 8u) | sr_code<F>(fabsf(z[i]), w[i])) << (4 * i);
+    } else if constexpr (F == FMT_E2M1) {
+        packed = pack8_e2m1(z);
+    } else {
+        if constexpr (S == SC_E4M3) {
+            // the E4M3 rounding of Delta can leave |z| above the grid maximum
+#pragma unroll
+            for (int i = 0; i < 8; ++i) z[i] = __builtin_amdgcn_fmed3f(z[i], -grid_max(F), grid_max(F));
+        }
+        packed = pack8_uniform<F>(z);
+    }
+    return b.s == 0.0f ? 0u : packed;
 }
 
 // IF4: both candidates for one element; returns the two magnitude codes and
-// the two binary32 squared errors.
+// the two binary32 squared errors.  a = |y|.
 __device__ __forceinline__ void if4_candidates(float a, const BlockScale &b, uint32_t &kf, uint32_t &ki,
                                                float &ef, float &ei)
 {
     constexpr float C76 = 7.0f / 6.0f;
     constexpr float C67 = 6.0f / 7.0f;
-    const float zf = scaled_abs<SC_E4M3, false>(a, b);
+    const float zf = b.fast ? div_fast(a, b.s, b.invd) : a / b.s;
     const float t = a * C76;
-    const float zi = b.fast ? div_fast(t, b.s, b.inv) : t / b.s;
+    const float zi = b.fast ? div_fast(t, b.s, b.invd) : t / b.s;
     kf = rtne_code<FMT_E2M1>(zf);
     ki = rtne_code<FMT_INT4>(zi);
     const float xf = grid_value<FMT_E2M1>(kf) * b.s;
@@ -146,7 +183,6 @@ __device__ __forceinline__ void if4_candidates(float a, const BlockScale &b, uin
 // ---------------------------------------------------------------------------
 // Row kernel
 // ---------------------------------------------------------------------------
-template <int IN>
 __device__ __forceinline__ int64_t row_offset(const RowArgs &a, int64_t o)
 {
     if (a.contiguous) return o * 8;
@@ -170,7 +206,7 @@ template <int IN>
 __device__ __forceinline__ Raw8<IN> load_raw(const RowArgs &a, int64_t o)
 {
     Raw8<IN> r;
-    const int64_t off = row_offset<IN>(a, o);
+    const int64_t off = row_offset(a, o);
     if constexpr (IN == IN_BF16) {
         r.w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + off);
     } else {
@@ -181,48 +217,60 @@ __device__ __forceinline__ Raw8<IN> load_raw(const RowArgs &a, int64_t o)
     return r;
 }
 
+// Unpack 8 elements, applying the sign diagonal (sgn: per-position sign bits).
 template <int IN>
-__device__ __forceinline__ void unpack(const Raw8<IN> &r, float *v)
+__device__ __forceinline__ void unpack(const Raw8<IN> &r, float *v, const uint32_t *sgn)
 {
     if constexpr (IN == IN_BF16) {
-        v[0] = bf16lo(r.w.x); v[1] = bf16hi(r.w.x);
-        v[2] = bf16lo(r.w.y); v[3] = bf16hi(r.w.y);
-        v[4] = bf16lo(r.w.z); v[5] = bf16hi(r.w.z);
-        v[6] = bf16lo(r.w.w); v[7] = bf16hi(r.w.w);
+        const uint32_t w[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = u2f((w[i] << 16) ^ sgn[2 * i]);
+            v[2 * i + 1] = u2f((w[i] & 0xFFFF0000u) ^ sgn[2 * i + 1]);
+        }
     } else {
-        v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
-        v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+        const float f[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = u2f(f2u(f[i]) ^ sgn[i]);
     }
 }
 
-// Signs, spans 1/2/4 in registers, span 8 with the partner lane, x 1/4.
-// Lane half 0 holds chunk positions 0..7, half 1 positions 8..15; the span-8
-// butterfly gives half 0 v_i + v_{i+8} and half 1 v_i - v_{i+8} = (-own) + partner.
-template <bool RHT>
-__device__ __forceinline__ void row_transform(float *v, const uint32_t *sgn, uint32_t neg_own)
+// Spans 1/2/4 in registers, span 8 with the partner lane.  Lane half 0 holds
+// chunk positions 0..7, half 1 positions 8..15; the span-8 butterfly gives
+// half 0 v_i + v_{i+8} and half 1 v_i - v_{i+8} = (-own) + partner.  The final
+// x 1/4 is applied unless FOLD.
+template <bool RHT, bool FOLD>
+__device__ __forceinline__ void row_transform(float *v, uint32_t neg_own)
 {
     if constexpr (RHT) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = u2f(f2u(v[i]) ^ sgn[i]);
         fwht8(v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float p = xor1(v[i]);
             v[i] = u2f(f2u(v[i]) ^ neg_own) + p;
         }
+        if constexpr (!FOLD) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] * 0.25f;
+            for (int i = 0; i < 8; ++i) v[i] = v[i] * 0.25f;
+        }
     }
 }
 
-template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
-__device__ __forceinline__ void row_octet(const RowArgs &a, int64_t o, float *v, const uint32_t *sgn,
-                                          uint32_t neg_own, const TensorConst &tc, float &lmax)
+__device__ __forceinline__ float absmax8(const float *v)
 {
-    row_transform<RHT>(v, sgn, neg_own);
+    return fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                 fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+}
+
+template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
+__device__ __forceinline__ void row_octet(const RowArgs &a, int64_t o, float *v, uint32_t neg_own,
+                                          const TensorConst &tc, float &lmax)
+{
+    // fold x 1/4 into the divisor for bf16 sources (exact), not for IF4
+    constexpr bool FOLD = MODE == MODE_QUANT && RHT && IN == IN_BF16 && F != FMT_IF4;
+    row_transform<RHT, FOLD>(v, neg_own);
     if constexpr (MODE == MODE_AMAX) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
+        lmax = fmaxf(lmax, absmax8(v));
         return;
     } else if constexpr (MODE == MODE_RHT) {
         int64_t off;
@@ -247,12 +295,11 @@ __device__ __forceinline__ void row_octet(const RowArgs &a, int64_t o, float *v,
         return;
     } else {
         // block amax over 16 (two lanes) or 32 (four lanes)
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        float m = absmax8(v);
         m = fmaxf(m, xor1(m));
         if constexpr (S == SC_E8M0) m = fmaxf(m, xor2(m));
-        const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S>(m, tc);
+        if constexpr (FOLD) m = m * 0.25f;
+        const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S, FOLD>(m, tc);
 
         uint32_t packed = 0;
         uint32_t sbyte = bs.byte;
@@ -283,12 +330,7 @@ __device__ __forceinline__ void row_octet(const RowArgs &a, int64_t o, float *v,
                 w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
                 w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t k = elem_code<F, S, SR>(fabsf(v[i]), bs, SR ? w[i] : 0u);
-                packed |= ((f2u(v[i]) >> 28 & 8u) | k) << (4 * i);
-            }
-            if (bs.s == 0.0f) packed = 0;
+            packed = encode8<F, S, FOLD, SR>(v, bs, w);
         }
         reinterpret_cast<uint32_t *>(a.codes)[o] = packed;
         if constexpr (S == SC_E8M0) {
@@ -308,7 +350,7 @@ __global__ __launch_bounds__(RT) void row_kernel(const RowArgs a)
     const uint32_t half = tid & 1;
     uint32_t sgn[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sgn[i] = ((a.smask >> (8 * half + i)) & 1u) << 31;
+    for (int i = 0; i < 8; ++i) sgn[i] = RHT ? ((a.smask >> (8 * half + i)) & 1u) << 31 : 0u;
     const uint32_t neg_own = half << 31;
     TensorConst tc{0.f, 0.f, 0.f, false};
     if constexpr (MODE == MODE_QUANT) tc = tensor_const<F == FMT_IF4 ? FMT_E2M1 : F, S>(a.amax);
@@ -325,8 +367,8 @@ __global__ __launch_bounds__(RT) void row_kernel(const RowArgs a)
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
             float v[8];
-            unpack<IN>(raw[u], v);
-            row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, sgn, neg_own, tc, lmax);
+            unpack<IN>(raw[u], v, sgn);
+            row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, neg_own, tc, lmax);
         }
     } else {
 #pragma unroll
@@ -336,8 +378,8 @@ __global__ __launch_bounds__(RT) void row_kernel(const RowArgs a)
         for (int u = 0; u < RU; ++u)
             if (base + u * RT < a.n_oct) {
                 float v[8];
-                unpack<IN>(raw[u], v);
-                row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, sgn, neg_own, tc, lmax);
+                unpack<IN>(raw[u], v, sgn);
+                row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, neg_own, tc, lmax);
             }
     }
     if constexpr (MODE == MODE_AMAX) {
@@ -349,7 +391,7 @@ __global__ __launch_bounds__(RT) void row_kernel(const RowArgs a)
         if (tid == 0) {
             float w = red[0];
             for (int i = 1; i < RT / 64; ++i) w = fmaxf(w, red[i]);
-            atomicMax(a.amax_out, f2u(w));
+            a.partials[blockIdx.x] = w;
         }
     }
 }
@@ -360,6 +402,7 @@ __global__ __launch_bounds__(RT) void row_kernel(const RowArgs a)
 template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
 __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
 {
+    constexpr bool FOLD = MODE == MODE_QUANT && RHT && IN == IN_BF16 && F != FMT_IF4;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane & 7, b = lane >> 3;
@@ -374,8 +417,8 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
     }
     float lmax = 0.0f;
 
-    // 16 rows x 8 columns, kept as loaded (bf16 pairs / binary32) until each
-    // column is processed
+    // 16 rows x 8 columns, kept as loaded (bf16 pairs) until each column is
+    // processed
     uint4 raw[16];
     if (active) {
         if constexpr (IN == IN_BF16) {
@@ -407,13 +450,22 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         if (active && RHT) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[i] = u2f(f2u(v[i]) ^ (((a.smask >> i) & 1u) << 31));
-            fwht16_local(v);
+            fwht8(v);
+            fwht8(v + 8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = v[i], q = v[i + 8];
+                v[i] = p + q;
+                v[i + 8] = p - q;
+            }
+            if constexpr (!FOLD) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = v[i] * 0.25f;
+            }
         }
         const int64_t c = c0 + j;  // view row
         if constexpr (MODE == MODE_AMAX) {
-            if (active)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
+            if (active) lmax = fmaxf(lmax, fmaxf(absmax8(v), absmax8(v + 8)));
         } else if constexpr (MODE == MODE_RHT) {
             if (active) {
                 const int64_t off = c * a.ldy + r0;
@@ -432,12 +484,11 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
                 }
             }
         } else {
-            float m = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+            float m = fmaxf(absmax8(v), absmax8(v + 8));
             if constexpr (S == SC_E8M0) m = fmaxf(m, xor8(m));  // partner lane holds the other 16 rows
             if (!active) continue;
-            const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S>(m, tc);
+            if constexpr (FOLD) m = m * 0.25f;
+            const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S, FOLD>(m, tc);
             uint32_t lo = 0, hi = 0;
             uint32_t sbyte = bs.byte;
             if constexpr (F == FMT_IF4) {
@@ -458,6 +509,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
                     const uint32_t code = (f2u(v[i]) >> 28 & 8u) | (use_int ? ki[i] : kf[i]);
                     if (i < 8) lo |= code << (4 * i); else hi |= code << (4 * (i - 8));
                 }
+                if (bs.s == 0.0f) lo = hi = 0;
                 sbyte |= use_int ? 0x80u : 0u;
             } else {
                 uint32_t w[16];
@@ -469,14 +521,9 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
                         w[4 * q] = ww.x; w[4 * q + 1] = ww.y; w[4 * q + 2] = ww.z; w[4 * q + 3] = ww.w;
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint32_t code = (f2u(v[i]) >> 28 & 8u) |
-                                          elem_code<F, S, SR>(fabsf(v[i]), bs, SR ? w[i] : 0u);
-                    if (i < 8) lo |= code << (4 * i); else hi |= code << (4 * (i - 8));
-                }
+                lo = encode8<F, S, FOLD, SR>(v, bs, w);
+                hi = encode8<F, S, FOLD, SR>(v + 8, bs, w + 8);
             }
-            if (bs.s == 0.0f) lo = hi = 0;
             *reinterpret_cast<uint2 *>(a.codes + c * (a.R >> 1) + (r0 >> 1)) = make_uint2(lo, hi);
             if constexpr (S == SC_E8M0) {
                 if ((b & 1) == 0) static_cast<uint8_t *>(a.scales)[c * (a.R >> 5) + (r0 >> 5)] = (uint8_t)sbyte;
@@ -496,12 +543,31 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         if (tid == 0) {
             float w = red[0];
             for (int i = 1; i < CT / 64; ++i) w = fmaxf(w, red[i]);
-            atomicMax(a.amax_out, f2u(w));
+            a.partials[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = w;
         }
     }
 }
 
-__global__ void fill_u32_kernel(unsigned int *p, unsigned int v) { *p = v; }
+// One workgroup: the max of the per-tile partial maxima (exact, any order).
+__global__ __launch_bounds__(256) void amax_final_kernel(const float *partials, int64_t n, float *amax)
+{
+    __shared__ float red[256];
+    float m = 0.0f;
+    for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, partials[i]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *amax = red[0];
+}
+
+int64_t amax_tiles(int axis, int64_t rows, int64_t cols)
+{
+    if (axis == 0) return (rows * cols / 8 + RT * RU - 1) / (RT * RU);
+    return ((cols + CTC - 1) / CTC) * ((rows + CTR - 1) / CTR);
+}
 
 // ---------------------------------------------------------------------------
 // Launch helpers: runtime options -> template instance.
@@ -565,17 +631,24 @@ hipError_t launch_quantize(const LaunchSpec &sp, const RowArgs &ra, const ColArg
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
+hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, float *amax, hipStream_t st)
 {
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, st, sp.axis == 0 ? ra.amax_out : ca.amax_out, 0u);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const bool rht = sp.rht != 0;
-    if (sp.in_dtype == IN_BF16)
-        return rht ? launch_one<MODE_AMAX, 0, 0, false, IN_BF16, true, 0>(sp.axis, ra, ca, st)
-                   : launch_one<MODE_AMAX, 0, 0, false, IN_BF16, false, 0>(sp.axis, ra, ca, st);
-    return rht ? launch_one<MODE_AMAX, 0, 0, false, IN_F32, true, 0>(sp.axis, ra, ca, st)
-               : launch_one<MODE_AMAX, 0, 0, false, IN_F32, false, 0>(sp.axis, ra, ca, st);
+    const int64_t tiles = sp.axis == 0 ? (ra.n_oct + RT * RU - 1) / (RT * RU)
+                                       : ((ca.C + CTC - 1) / CTC) * ((ca.R + CTR - 1) / CTR);
+    hipError_t e = hipSuccess;
+    if (tiles > 0) {
+        const bool rht = sp.rht != 0;
+        if (sp.in_dtype == IN_BF16)
+            e = rht ? launch_one<MODE_AMAX, 0, 0, false, IN_BF16, true, 0>(sp.axis, ra, ca, st)
+                    : launch_one<MODE_AMAX, 0, 0, false, IN_BF16, false, 0>(sp.axis, ra, ca, st);
+        else
+            e = rht ? launch_one<MODE_AMAX, 0, 0, false, IN_F32, true, 0>(sp.axis, ra, ca, st)
+                    : launch_one<MODE_AMAX, 0, 0, false, IN_F32, false, 0>(sp.axis, ra, ca, st);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(256), 0, st, sp.axis == 0 ? ra.partials : ca.partials, tiles,
+                       amax);
+    return hipGetLastError();
 }
 
 hipError_t launch_rht(const LaunchSpec &sp, int out_dtype, const RowArgs &ra, const ColArgs &ca, hipStream_t st)

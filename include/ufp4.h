@@ -101,7 +101,7 @@ enum { UFP4_RTNE = 0, UFP4_SR = 1 };
 enum { UFP4_ROW = 0, UFP4_COL = 1 };
 enum { UFP4_BF16 = 0, UFP4_F32 = 1 };
 enum { UFP4_GEMM_NATIVE_MXFP4 = 0, UFP4_GEMM_DEQUANT_BF16 = 1 };
-enum { UFP4_OP_STATS = 0, UFP4_OP_QGEMM = 1, UFP4_OP_ETA = 2 };
+enum { UFP4_OP_STATS = 0, UFP4_OP_QGEMM = 1, UFP4_OP_ETA = 2, UFP4_OP_AMAX = 3 };
 
 /* Supported combinations (anything else returns UFP4_ERR_UNSUPPORTED):
  *   E2M1 with FP32/16, E4M3/16 or E8M0/32; E1M2 and INT4 with FP32/16 or E4M3/16;
@@ -165,10 +165,13 @@ int ufp4_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx
 
 /* Tensor amax after the transform named by cfg (rht, rht_seed, axis): writes
  * max |y| to amax[0] (device float).  Needed before a UFP4_SCALE_E4M3
- * quantization ([IF4] 3.2: alpha = max|X| / (6 x 448)).  Several devices can
- * combine their amax with a MAX all-reduce before quantizing their shards. */
+ * quantization ([IF4] 3.2: alpha = max|X| / (6 x 448)).  Two launches: one
+ * partial maximum per workgroup into ws, then one workgroup reduces them (no
+ * atomics; the result is exact and order-free).  ws: device workspace of
+ * ufp4_workspace_size(UFP4_OP_AMAX, rows, cols, cfg) bytes.  Several devices
+ * can combine their amax with a MAX all-reduce before quantizing their shards. */
 int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
-              float *amax, void *stream);
+              float *amax, void *ws, size_t ws_bytes, void *stream);
 
 /* Block quantization (all steps fused in one kernel: load, signs, FWHT, block
  * amax, scale, RTNE/SR or IF4 selection, nibble packing, stores).
@@ -220,7 +223,8 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
              size_t ws_bytes, void *stream);
 
 /* Workspace bytes for op (UFP4_OP_*) on a rows x cols source (QGEMM: rows = M+N,
- * cols = K; ETA: rows = M, cols = N).  cfg may be NULL except for QGEMM. */
+ * cols = K; ETA: rows = M, cols = N).  cfg may be NULL except for QGEMM and
+ * AMAX (whose size depends on the axis). */
 size_t ufp4_workspace_size(int op, int64_t rows, int64_t cols, const ufp4_config *cfg);
 
 /* Text of an error code (static storage). */

@@ -86,7 +86,8 @@ def test_other_calls_validate():
     assert L.ufp4_rht(FAKE, 0, 16, 32, 32, 0, 1, 0, FAKE, 1, 16, None) == -2
     assert L.ufp4_rht(FAKE, 0, 16, 32, 32, 0, 7, 0, FAKE, 1, 32, None) == -1
     cfg = U.Cfg("e2m1").c()
-    assert L.ufp4_amax(FAKE, 0, 16, 32, 32, C.byref(cfg), None, None) == -1
+    assert L.ufp4_amax(FAKE, 0, 16, 32, 32, C.byref(cfg), None, FAKE, 64, None) == -1
+    assert L.ufp4_amax(FAKE, 0, 16, 32, 32, C.byref(cfg), FAKE, None, 0, None) == -5
     q = U.ufp4_qtensor(FAKE, FAKE, None, 16, 24, U.Cfg("e2m1").c())
     assert L.ufp4_dequantize(C.byref(q), 0, FAKE, 1, 24, None) == -2
     q = U.ufp4_qtensor(FAKE, FAKE, None, 16, 32, U.Cfg("e2m1").c())
@@ -116,6 +117,8 @@ def test_empty_inputs_are_no_ops():
 def test_workspace_sizes():
     assert U.ufp4_workspace_size(U.OP_STATS, 100, 64) == 1024 * 48 * 8
     assert U.ufp4_workspace_size(U.OP_ETA, 100, 64) == 1024 * 3 * 8
+    assert U.ufp4_workspace_size(U.OP_AMAX, 8192, 8192, U.Cfg()) == 8192 * 4      # one per 1024 octets
+    assert U.ufp4_workspace_size(U.OP_AMAX, 16384, 4096, U.Cfg(axis="col")) == 64 * 32 * 4
     assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, U.Cfg("e1m2")) == 512 * 256 * 2
     assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, U.Cfg("e2m1", "e8m0", 32)) == 0
 

@@ -93,7 +93,7 @@ static void fill_args(const void *x, int dtype, int64_t rows, int64_t cols, int6
     ra.x = x;
     ra.ldx = ldx;
     ra.L = cols;
-    ra.n_oct = axis == UFP4_ROW ? rows * cols / 8 : 0;
+    ra.n_ch = axis == UFP4_ROW ? rows * cols / 16 : 0;
     ra.contiguous = ldx == cols;
     ra.smask = smask;
     ca.x = x;

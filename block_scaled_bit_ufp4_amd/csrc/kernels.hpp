@@ -7,12 +7,12 @@
 
 namespace ufp4 {
 
-// Row kernel: one lane per 8 consecutive view elements ("octet").
+// Row kernel: one lane per 16-element chunk of a view row.
 struct RowArgs {
     const void *x;        // source (ROW axis: the view itself)
     int64_t ldx;          // source row stride (elements)
     int64_t L;            // view row length
-    int64_t n_oct;        // V * L / 8
+    int64_t n_ch;         // V * L / 16
     int contiguous;       // ldx == L
     uint32_t smask;       // RHT sign mask (bit i: d_i = -1)
     uint8_t *codes;       // [V][L/2]

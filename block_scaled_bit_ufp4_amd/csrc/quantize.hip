@@ -9,14 +9,13 @@
 // E8M0 -- MXFP4 page), and rounding to E2M1 / E1M2 / INT4 by round-to-nearest-
 // even or stochastic rounding (IF4 page 6.1; UFP4 recipe: dY only).
 //
-// Layout on the chip.  Row kernel: each lane owns 8 consecutive view elements
-// (one 16-byte bf16 load); the two halves of a 16-chunk sit in lanes 2i and
-// 2i+1, so the span-8 butterfly and the block max cross lanes through DPP
-// (quad_perm), and the 32-element E8M0 blocks use lanes 4i..4i+3.  A 256-lane
-// workgroup handles 4 x 256 consecutive octets (16 KiB of bf16), every wave
-// instruction reading 1 KiB contiguous; codes leave as one 32-bit store per
-// lane.  Column kernel (the transposed bwd_dw operand): each lane loads 16
-// rows x 8 columns (16 loads of 16 bytes, each wave instruction covering eight
+// Layout on the chip.  Row kernel: each lane owns one 16-element chunk of a
+// view row per step (two 16-byte bf16 loads), so the butterflies, the block
+// max and the scale stay in the lane; only E8M0's 32-element blocks combine a
+// lane pair through DPP.  A 256-lane workgroup handles 2 x 256 consecutive
+// chunks (16 KiB of bf16); codes leave as one 8-byte store per lane.
+// Column kernel (the transposed bwd_dw operand): each lane loads 16 rows x 8
+// columns (16 loads of 16 bytes, each wave instruction covering eight
 // full 128-byte row segments), transforms and quantizes its 8 column blocks in
 // registers and writes 8 bytes of codes per column; the 4 waves of a
 // workgroup cover 512 rows of 64 columns, so every 128-byte line of the
@@ -34,7 +33,8 @@
 namespace ufp4 {
 
 constexpr int RT = 256;  // row kernel: threads per workgroup
-constexpr int RU = 4;    // row kernel: octets per lane
+constexpr int RU = 2;    // row kernel: 16-element chunks per lane (quantize, transform)
+constexpr int RUA = 8;   // row kernel: chunks per lane in the amax pass
 constexpr int CT = 256;  // column kernel: threads per workgroup
 constexpr int CTR = 512; // column kernel: source rows per workgroup
 constexpr int CTC = 64;  // column kernel: source columns per workgroup
@@ -99,8 +99,8 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
                 delta = div_fast(m, t.den, t.inv_den);
             else
                 delta = m / t.den;
-            b.byte = e4m3_encode(delta);
-            b.s = t.alpha * e4m3_decode(b.byte);
+            b.byte = e4m3_encode_hw(delta);
+            b.s = t.alpha * e4m3_decode_hw(b.byte);
         }
         const float inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
         b.sd = FOLD ? b.s * 4.0f : b.s;
@@ -181,205 +181,229 @@ __device__ __forceinline__ void if4_candidates(float a, const BlockScale &b, uin
 }
 
 // ---------------------------------------------------------------------------
-// Row kernel
+// Row kernel: one lane per 16-element chunk of a view row (two 16-byte bf16
+// loads; each wave instruction covers 2 KiB, the pair of instructions all of
+// it).  The transform and the block max stay in the lane; only the 32-element
+// E8M0 blocks combine two lanes (DPP).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t row_offset(const RowArgs &a, int64_t o)
+__device__ __forceinline__ int64_t row_offset(const RowArgs &a, int64_t ch)
 {
-    if (a.contiguous) return o * 8;
-    const int64_t L8 = a.L >> 3;
-    const int64_t vr = o / L8;
-    return vr * a.ldx + (o - vr * L8) * 8;
+    if (a.contiguous) return ch * 16;
+    const int64_t L16 = a.L >> 4;
+    const int64_t vr = ch / L16;
+    return vr * a.ldx + (ch - vr * L16) * 16;
 }
 
 template <int IN>
-struct Raw8;
+struct Raw16;
 template <>
-struct Raw8<IN_BF16> {
-    uint4 w;
+struct Raw16<IN_BF16> {
+    uint4 a, b;
 };
 template <>
-struct Raw8<IN_F32> {
-    float4 a, b;
+struct Raw16<IN_F32> {
+    float4 a, b, c, d;
 };
 
 template <int IN>
-__device__ __forceinline__ Raw8<IN> load_raw(const RowArgs &a, int64_t o)
+__device__ __forceinline__ Raw16<IN> load_raw(const RowArgs &a, int64_t ch)
 {
-    Raw8<IN> r;
-    const int64_t off = row_offset(a, o);
+    Raw16<IN> r;
+    const int64_t off = row_offset(a, ch);
     if constexpr (IN == IN_BF16) {
-        r.w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + off);
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + off);
+        r.a = p[0];
+        r.b = p[1];
     } else {
         const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + off);
         r.a = p[0];
         r.b = p[1];
+        r.c = p[2];
+        r.d = p[3];
     }
     return r;
 }
 
-// Unpack 8 elements, applying the sign diagonal (sgn: per-position sign bits).
+// Unpack 16 elements, applying the sign diagonal (sgn: sign bit per position).
 template <int IN>
-__device__ __forceinline__ void unpack(const Raw8<IN> &r, float *v, const uint32_t *sgn)
+__device__ __forceinline__ void unpack16(const Raw16<IN> &r, float *v, const uint32_t *sgn)
 {
     if constexpr (IN == IN_BF16) {
-        const uint32_t w[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+        const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+        // sign bits: adding 0x80000000 flips bit 31 only (the low half of w << 16 is zero)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = u2f((w[i] << 16) ^ sgn[2 * i]);
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = u2f((w[i] << 16) + sgn[2 * i]);
             v[2 * i + 1] = u2f((w[i] & 0xFFFF0000u) ^ sgn[2 * i + 1]);
         }
     } else {
-        const float f[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+        const float f[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
+                             r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = u2f(f2u(f[i]) ^ sgn[i]);
+        for (int i = 0; i < 16; ++i) v[i] = u2f(f2u(f[i]) ^ sgn[i]);
     }
 }
 
-// Spans 1/2/4 in registers, span 8 with the partner lane.  Lane half 0 holds
-// chunk positions 0..7, half 1 positions 8..15; the span-8 butterfly gives
-// half 0 v_i + v_{i+8} and half 1 v_i - v_{i+8} = (-own) + partner.  The final
-// x 1/4 is applied unless FOLD.
+// 16-point butterflies (spans 1, 2, 4, 8); the final x 1/4 unless FOLD.
 template <bool RHT, bool FOLD>
-__device__ __forceinline__ void row_transform(float *v, uint32_t neg_own)
+__device__ __forceinline__ void transform16(float *v)
 {
     if constexpr (RHT) {
         fwht8(v);
+        fwht8(v + 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float p = xor1(v[i]);
-            v[i] = u2f(f2u(v[i]) ^ neg_own) + p;
+            const float p = v[i], q = v[i + 8];
+            v[i] = p + q;
+            v[i + 8] = p - q;
         }
         if constexpr (!FOLD) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = v[i] * 0.25f;
+            for (int i = 0; i < 16; ++i) v[i] = v[i] * 0.25f;
         }
     }
 }
 
-__device__ __forceinline__ float absmax8(const float *v)
+__device__ __forceinline__ float absmax16(const float *v)
 {
-    return fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
-                 fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+    float m = fmaxf(fabsf(v[0]), fabsf(v[1]));
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) m = fmaxf(fmaxf(m, fabsf(v[i])), fabsf(v[i + 1]));
+    return m;
 }
 
-template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
-__device__ __forceinline__ void row_octet(const RowArgs &a, int64_t o, float *v, uint32_t neg_own,
-                                          const TensorConst &tc, float &lmax)
+// Quantize one transformed 16-element chunk held by this lane; returns the
+// codes (low word: elements 0..7) and sets the scale byte / value.
+template <int F, int S, bool SR, bool FOLD>
+__device__ __forceinline__ uint2 quant_chunk(const float *v, const TensorConst &tc, uint64_t n0, uint64_t sr_seed,
+                                             uint32_t sr_stream, bool pair_max, uint32_t &sbyte, float &sval)
+{
+    float m = absmax16(v);
+    if constexpr (S == SC_E8M0) {
+        if (pair_max) m = fmaxf(m, xor1(m));  // the partner lane holds the other half of the block
+    }
+    if constexpr (FOLD) m = m * 0.25f;
+    const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S, FOLD>(m, tc);
+    sbyte = bs.byte;
+    sval = bs.s;
+    uint32_t lo = 0, hi = 0;
+    if constexpr (F == FMT_IF4) {
+        uint32_t kf[16], ki[16];
+        float ef[16], ei[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) if4_candidates(fabsf(v[i]), bs, kf[i], ki[i], ef[i], ei[i]);
+        // pairwise: (0+1),(2+3),..., then pairs of pairs, four levels
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2 * w) {
+                ef[i] = ef[i] + ef[i + w];
+                ei[i] = ei[i] + ei[i + w];
+            }
+        const bool use_int = bs.s != 0.0f && ei[0] < ef[0];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t code = (f2u(v[i]) >> 28 & 8u) | (use_int ? ki[i] : kf[i]);
+            if (i < 8) lo |= code << (4 * i); else hi |= code << (4 * (i - 8));
+        }
+        if (bs.s == 0.0f) lo = hi = 0;
+        sbyte |= use_int ? 0x80u : 0u;
+    } else {
+        uint32_t w[16];
+        if constexpr (SR) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 ww = sr_words4(n0 + 4 * q, sr_seed, sr_stream);
+                w[4 * q] = ww.x; w[4 * q + 1] = ww.y; w[4 * q + 2] = ww.z; w[4 * q + 3] = ww.w;
+            }
+        }
+        lo = encode8<F, S, FOLD, SR>(v, bs, w);
+        hi = encode8<F, S, FOLD, SR>(v + 8, bs, w + 8);
+    }
+    return make_uint2(lo, hi);
+}
+
+template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT, int U>
+__device__ __forceinline__ void row_chunk(const RowArgs &a, int64_t ch, float *v, const TensorConst &tc,
+                                          float &lmax)
 {
     // fold x 1/4 into the divisor for bf16 sources (exact), not for IF4
     constexpr bool FOLD = MODE == MODE_QUANT && RHT && IN == IN_BF16 && F != FMT_IF4;
-    row_transform<RHT, FOLD>(v, neg_own);
+    transform16<RHT, FOLD>(v);
     if constexpr (MODE == MODE_AMAX) {
-        lmax = fmaxf(lmax, absmax8(v));
-        return;
+        lmax = fmaxf(lmax, absmax16(v));
     } else if constexpr (MODE == MODE_RHT) {
         int64_t off;
         if (a.ldy == a.L) {
-            off = o * 8;
+            off = ch * 16;
         } else {
-            const int64_t L8 = a.L >> 3, vr = o / L8;
-            off = vr * a.ldy + (o - vr * L8) * 8;
+            const int64_t L16 = a.L >> 4, vr = ch / L16;
+            off = vr * a.ldy + (ch - vr * L16) * 16;
         }
         if constexpr (OUT == IN_F32) {
             float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.y) + off);
-            p[0] = make_float4(v[0], v[1], v[2], v[3]);
-            p[1] = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
         } else {
-            uint4 w;
-            w.x = to_bf16(v[0]) | (to_bf16(v[1]) << 16);
-            w.y = to_bf16(v[2]) | (to_bf16(v[3]) << 16);
-            w.z = to_bf16(v[4]) | (to_bf16(v[5]) << 16);
-            w.w = to_bf16(v[6]) | (to_bf16(v[7]) << 16);
-            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + off) = w;
+            uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + off);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                p[q] = make_uint4(to_bf16(v[8 * q]) | (to_bf16(v[8 * q + 1]) << 16),
+                                  to_bf16(v[8 * q + 2]) | (to_bf16(v[8 * q + 3]) << 16),
+                                  to_bf16(v[8 * q + 4]) | (to_bf16(v[8 * q + 5]) << 16),
+                                  to_bf16(v[8 * q + 6]) | (to_bf16(v[8 * q + 7]) << 16));
         }
-        return;
     } else {
-        // block amax over 16 (two lanes) or 32 (four lanes)
-        float m = absmax8(v);
-        m = fmaxf(m, xor1(m));
-        if constexpr (S == SC_E8M0) m = fmaxf(m, xor2(m));
-        if constexpr (FOLD) m = m * 0.25f;
-        const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S, FOLD>(m, tc);
-
-        uint32_t packed = 0;
-        uint32_t sbyte = bs.byte;
-        if constexpr (F == FMT_IF4) {
-            uint32_t kf[8], ki[8];
-            float ef[8], ei[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) if4_candidates(fabsf(v[i]), bs, kf[i], ki[i], ef[i], ei[i]);
-            // pairwise sums: (0+1),(2+3),... then pairs of pairs; the span-8
-            // level pairs this lane's sum with the partner's (commutative)
-            float sf = ((ef[0] + ef[1]) + (ef[2] + ef[3])) + ((ef[4] + ef[5]) + (ef[6] + ef[7]));
-            float si = ((ei[0] + ei[1]) + (ei[2] + ei[3])) + ((ei[4] + ei[5]) + (ei[6] + ei[7]));
-            sf = sf + xor1(sf);
-            si = si + xor1(si);
-            const bool use_int = bs.s != 0.0f && si < sf;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t k = use_int ? ki[i] : kf[i];
-                packed |= ((f2u(v[i]) >> 28 & 8u) | k) << (4 * i);
-            }
-            if (bs.s == 0.0f) packed = 0;
-            sbyte |= use_int ? 0x80u : 0u;
-        } else {
-            uint32_t w[8];
-            if constexpr (SR) {
-                const uint4 w0 = sr_words4((uint64_t)o * 8, a.sr_seed, a.sr_stream);
-                const uint4 w1 = sr_words4((uint64_t)o * 8 + 4, a.sr_seed, a.sr_stream);
-                w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-                w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
-            }
-            packed = encode8<F, S, FOLD, SR>(v, bs, w);
-        }
-        reinterpret_cast<uint32_t *>(a.codes)[o] = packed;
+        uint32_t sbyte;
+        float sval;
+        const uint2 codes = quant_chunk<F, S, SR, FOLD>(v, tc, (uint64_t)ch * 16, a.sr_seed, a.sr_stream, true,
+                                                        sbyte, sval);
+        reinterpret_cast<uint2 *>(a.codes)[ch] = codes;
         if constexpr (S == SC_E8M0) {
-            if ((o & 3) == 0) static_cast<uint8_t *>(a.scales)[o >> 2] = (uint8_t)sbyte;
+            if ((ch & 1) == 0) static_cast<uint8_t *>(a.scales)[ch >> 1] = (uint8_t)sbyte;
         } else if constexpr (S == SC_E4M3) {
-            if ((o & 1) == 0) static_cast<uint8_t *>(a.scales)[o >> 1] = (uint8_t)sbyte;
+            static_cast<uint8_t *>(a.scales)[ch] = (uint8_t)sbyte;
         } else {
-            if ((o & 1) == 0) static_cast<float *>(a.scales)[o >> 1] = bs.s;
+            static_cast<float *>(a.scales)[ch] = sval;
         }
     }
 }
 
-template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
+template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT, int U>
 __global__ __launch_bounds__(RT) void row_kernel(const RowArgs a)
 {
     const int tid = threadIdx.x;
-    const uint32_t half = tid & 1;
-    uint32_t sgn[8];
+    uint32_t sgn[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sgn[i] = RHT ? ((a.smask >> (8 * half + i)) & 1u) << 31 : 0u;
-    const uint32_t neg_own = half << 31;
+    for (int i = 0; i < 16; ++i) sgn[i] = RHT ? ((a.smask >> i) & 1u) << 31 : 0u;
     TensorConst tc{0.f, 0.f, 0.f, false};
     if constexpr (MODE == MODE_QUANT) tc = tensor_const<F == FMT_IF4 ? FMT_E2M1 : F, S>(a.amax);
     if constexpr (MODE == MODE_QUANT && S == SC_E4M3) {
         if (blockIdx.x == 0 && tid == 0) *a.tensor_scale = tc.alpha;
     }
 
-    const int64_t base = (int64_t)blockIdx.x * (RT * RU) + tid;
+    const int64_t base = (int64_t)blockIdx.x * (RT * U) + tid;
     float lmax = 0.0f;
-    Raw8<IN> raw[RU];
-    if (base + (RU - 1) * RT < a.n_oct) {
+    Raw16<IN> raw[U];
+    if (base + (U - 1) * RT < a.n_ch) {
 #pragma unroll
-        for (int u = 0; u < RU; ++u) raw[u] = load_raw<IN>(a, base + u * RT);
+        for (int u = 0; u < U; ++u) raw[u] = load_raw<IN>(a, base + u * RT);
 #pragma unroll
-        for (int u = 0; u < RU; ++u) {
-            float v[8];
-            unpack<IN>(raw[u], v, sgn);
-            row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, neg_own, tc, lmax);
+        for (int u = 0; u < U; ++u) {
+            float v[16];
+            unpack16<IN>(raw[u], v, sgn);
+            row_chunk<MODE, F, S, SR, IN, RHT, OUT, U>(a, base + u * RT, v, tc, lmax);
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < RU; ++u)
-            if (base + u * RT < a.n_oct) raw[u] = load_raw<IN>(a, base + u * RT);
+        for (int u = 0; u < U; ++u)
+            if (base + u * RT < a.n_ch) raw[u] = load_raw<IN>(a, base + u * RT);
 #pragma unroll
-        for (int u = 0; u < RU; ++u)
-            if (base + u * RT < a.n_oct) {
-                float v[8];
-                unpack<IN>(raw[u], v, sgn);
-                row_octet<MODE, F, S, SR, IN, RHT, OUT>(a, base + u * RT, v, neg_own, tc, lmax);
+        for (int u = 0; u < U; ++u)
+            if (base + u * RT < a.n_ch) {
+                float v[16];
+                unpack16<IN>(raw[u], v, sgn);
+                row_chunk<MODE, F, S, SR, IN, RHT, OUT, U>(a, base + u * RT, v, tc, lmax);
             }
     }
     if constexpr (MODE == MODE_AMAX) {
@@ -465,7 +489,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         }
         const int64_t c = c0 + j;  // view row
         if constexpr (MODE == MODE_AMAX) {
-            if (active) lmax = fmaxf(lmax, fmaxf(absmax8(v), absmax8(v + 8)));
+            if (active) lmax = fmaxf(lmax, absmax16(v));
         } else if constexpr (MODE == MODE_RHT) {
             if (active) {
                 const int64_t off = c * a.ldy + r0;
@@ -484,7 +508,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
                 }
             }
         } else {
-            float m = fmaxf(absmax8(v), absmax8(v + 8));
+            float m = absmax16(v);
             if constexpr (S == SC_E8M0) m = fmaxf(m, xor8(m));  // partner lane holds the other 16 rows
             if (!active) continue;
             if constexpr (FOLD) m = m * 0.25f;
@@ -549,23 +573,24 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
 }
 
 // One workgroup: the max of the per-tile partial maxima (exact, any order).
-__global__ __launch_bounds__(256) void amax_final_kernel(const float *partials, int64_t n, float *amax)
+__global__ __launch_bounds__(1024) void amax_final_kernel(const float *partials, int64_t n, float *amax)
 {
-    __shared__ float red[256];
+    __shared__ float red[16];
     float m = 0.0f;
-    for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, partials[i]);
-    red[threadIdx.x] = m;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) m = fmaxf(m, partials[i]);
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-        __syncthreads();
+    if (threadIdx.x == 0) {
+        float w = red[0];
+        for (int i = 1; i < 16; ++i) w = fmaxf(w, red[i]);
+        *amax = w;
     }
-    if (threadIdx.x == 0) *amax = red[0];
 }
 
 int64_t amax_tiles(int axis, int64_t rows, int64_t cols)
 {
-    if (axis == 0) return (rows * cols / 8 + RT * RU - 1) / (RT * RU);
+    if (axis == 0) return (rows * cols / 16 + RT * RUA - 1) / (RT * RUA);
     return ((cols + CTC - 1) / CTC) * ((rows + CTR - 1) / CTR);
 }
 
@@ -576,9 +601,10 @@ template <int MODE, int F, int S, bool SR, int IN, bool RHT, int OUT>
 static hipError_t launch_one(int axis, const RowArgs &ra, const ColArgs &ca, hipStream_t st)
 {
     if (axis == 0) {
-        if (ra.n_oct == 0) return hipSuccess;
-        const int64_t wgs = (ra.n_oct + RT * RU - 1) / (RT * RU);
-        hipLaunchKernelGGL((row_kernel<MODE, F, S, SR, IN, RHT, OUT>), dim3((unsigned)wgs), dim3(RT), 0, st, ra);
+        if (ra.n_ch == 0) return hipSuccess;
+        constexpr int U = MODE == MODE_AMAX ? RUA : RU;
+        const int64_t wgs = (ra.n_ch + RT * U - 1) / (RT * U);
+        hipLaunchKernelGGL((row_kernel<MODE, F, S, SR, IN, RHT, OUT, U>), dim3((unsigned)wgs), dim3(RT), 0, st, ra);
     } else {
         if (ca.R == 0 || ca.C == 0) return hipSuccess;
         const dim3 grid((unsigned)((ca.C + CTC - 1) / CTC), (unsigned)((ca.R + CTR - 1) / CTR));
@@ -633,7 +659,7 @@ hipError_t launch_quantize(const LaunchSpec &sp, const RowArgs &ra, const ColArg
 
 hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &ca, float *amax, hipStream_t st)
 {
-    const int64_t tiles = sp.axis == 0 ? (ra.n_oct + RT * RU - 1) / (RT * RU)
+    const int64_t tiles = sp.axis == 0 ? (ra.n_ch + RT * RUA - 1) / (RT * RUA)
                                        : ((ca.C + CTC - 1) / CTC) * ((ca.R + CTR - 1) / CTR);
     hipError_t e = hipSuccess;
     if (tiles > 0) {
@@ -646,7 +672,7 @@ hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &c
                     : launch_one<MODE_AMAX, 0, 0, false, IN_F32, false, 0>(sp.axis, ra, ca, st);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(256), 0, st, sp.axis == 0 ? ra.partials : ca.partials, tiles,
+    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(1024), 0, st, sp.axis == 0 ? ra.partials : ca.partials, tiles,
                        amax);
     return hipGetLastError();
 }

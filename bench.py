@@ -165,26 +165,42 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _time(fn, torch, stream, reps):
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def bench_gemm(U, S, torch, dev, stream, reps=10):
+    """8192^3 block-scaled GEMMs: MXFP4 on the native scaled MFMA (the headline
+    qGEMM), the E1M2 dequantize-to-bf16 path, and the plain bf16 GEMM."""
     M = N = K = 8192
+    flop = 2.0 * M * N * K
     a = torch.from_numpy(S.gemm_a(M, K).view(np.int16)).view(torch.bfloat16).to(dev)
     b = torch.from_numpy(S.gemm_b(N, K).view(np.int16)).view(torch.bfloat16).to(dev)
     cfg = U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=0)
     qa, qb = U.ufp4_quantize(a, cfg), U.ufp4_quantize(b, cfg)
     c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    for _ in range(2):
-        U.ufp4_qgemm(qa, qb, "mxfp4", c=c)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        U.ufp4_qgemm(qa, qb, "mxfp4", c=c)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    ms = _time(lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c), torch, stream, reps)
+    cfg2 = U.Cfg("e1m2", "fp32", rht="random", rht_seed=0)
+    ea, eb = U.ufp4_quantize(a, cfg2), U.ufp4_quantize(b, cfg2)
+    ws = torch.empty(U.ufp4_workspace_size(U.OP_QGEMM, M + N, K, cfg2), dtype=torch.uint8, device=dev)
+    ms_e1m2 = _time(lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws), torch, stream, reps)
+    ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps)
+    tf = flop / (ms * 1e-3) / 1e12
     return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out", "ms": round(ms, 4),
-            "tflops": round(tflops, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tflops / FP4_PEAK_TFLOPS, 4)}
+            "tflops": round(tf, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tf / FP4_PEAK_TFLOPS, 4),
+            "e1m2_dequant_bf16": {"ms": round(ms_e1m2, 4), "tflops": round(flop / (ms_e1m2 * 1e-3) / 1e12, 1),
+                                  "note": "dequantize both operands to bf16 (workspace) + bf16 MFMA GEMM"},
+            "bf16_reference": {"ms": round(ms_bf16, 4), "tflops": round(flop / (ms_bf16 * 1e-3) / 1e12, 1),
+                               "peak_tflops": 2500.0}}
 
 
 if __name__ == "__main__":

@@ -12,10 +12,13 @@
 // pipeline stage (128 E2M1 codes or 32 bf16 values), and one 32x32 MFMA step
 // consumes 32 bytes of each of 32 rows, lane l holding row l mod 32 and the
 // 16-byte half l / 32 (32 FP4 codes of one 32-element scale block, or 8 bf16).
-// Workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 MFMA tiles of 32 x 32,
-// 256 fp32 accumulators per lane), two LDS stages of 256 rows x 64 bytes per
-// operand with the 16-byte chunks of each row XOR-swizzled so the 16-byte
-// fragment reads are free of bank conflicts.  Workgroups are ordered so that
+// Workgroup tile 256 x 256: eight waves (two per SIMD, so one wave's MFMAs
+// cover the other's LDS and barrier waits) of 128 x 64 (4 x 2 MFMA tiles of
+// 32 x 32, 128 fp32 accumulators per lane) over a ring of four LDS stages
+// (256 rows x 64 bytes per operand plus scales), filled by asynchronous
+// global -> LDS copies three stages ahead of the multiplications.  The
+// 16-byte chunks of each row are XOR-swizzled so the 16-byte fragment reads
+// are free of bank conflicts.  Workgroups are ordered so that
 // the eight XCDs each work on a compact band of output tiles.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -29,7 +32,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int GBM = 256;   // workgroup tile rows (M)
 constexpr int GBN = 256;   // workgroup tile columns (N)
 constexpr int GKB = 64;    // bytes of K per row per stage
-constexpr int GT = 256;    // threads
 constexpr int GROUP_M = 8; // tile-row group of the raster order
 
 // byte offset of 16-byte chunk c of row r in a stage (64 bytes per row)
@@ -51,142 +53,365 @@ __device__ __forceinline__ void tile_of(int bid, int MT, int NT, int &tm, int &t
     tn = r / gsz;
 }
 
-template <bool FP4>
-__global__ __launch_bounds__(GT, 1) void gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
-                                                     const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
-                                                     int M, int N, int64_t kbytes, int64_t lda, int64_t ldb,
-                                                     int64_t lds_a, int64_t lds_b, float *__restrict__ C, int64_t ldc)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS: a ring of four stage slots, each an A tile (256 rows x 64 B) then a B
+// tile, then room for the E8M0 scales of a group of four stages, used in
+// slot 0 only (it receives the first stage of every group): 16 bytes per A
+// row and per B row, byte 4 j + b scaling block b of the group's stage j.
+// They are stored row by row ([row][16 B], one 16-byte copy per row), or
+// stage by stage ([j][row][4 B]) where K is not a multiple of four stages.
+constexpr int ST_A = 0;
+constexpr int ST_B = GBM * GKB;
+constexpr int SG_A = 2 * GBM * GKB;         // 32 KiB of operand data
+constexpr int SG_B = SG_A + 16 * GBM;
+constexpr int ST_BYTES = SG_B + 16 * GBN;   // 40 KiB; four slots fill the 160 KiB of LDS
+constexpr int GNS = 4;                      // stage slots
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 64)
+#define UFP4_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// s_waitcnt: vector-memory counter at most n and no LDS access outstanding
+#define UFP4_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+// Compiler-level fence: no memory access moves across it, and no wait is
+// emitted for it (the waits are explicit).
+#define UFP4_CFENCE() asm volatile("" ::: "memory")
+#define UFP4_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Wave layout: GWM x GWN waves, each owning TM x TN MFMA tiles of 32 x 32.
+constexpr int GWM = 2, GWN = 2;
+constexpr int TM = 4, TN = 4;
+constexpr int GW = GWM * GWN;      // waves per workgroup, one per SIMD
+constexpr int GTH = 64 * GW;
+constexpr int ROWS_PER_WAVE = GBM / GW;  // tile rows of A and of B each wave copies
+static_assert(GWM * TM * 32 == GBM && GWN * TN * 32 == GBN && GBM == GBN, "tile shape");
+static_assert(ROWS_PER_WAVE == 64, "one scale row per lane");
+
+// copies each wave issues: operand data of one stage, scales of one group
+constexpr int DATA_COPIES = 2 * (ROWS_PER_WAVE / 16);
+constexpr int scale_copies(bool fp4, bool pad) { return fp4 ? (pad ? 8 : 2) : 0; }
+
+// Asynchronous global -> LDS copy of one stage's operand data, shared by the
+// waves: wave w copies tile rows 64 w .. 64 w + 63 of A and of B, 16 rows
+// (1 KiB) per instruction; lane l of the instruction for rows R0..R0+15 lands
+// at LDS byte R0 * 64 + 16 l, so it fetches the logical chunk (l mod 4) ^ f(row)
+// of row R0 + l / 4 and chunk c of row r ends up at lds_off(r, c).  The copies
+// are buffer loads: the tile's base sits in the buffer descriptor, the stage's
+// K offset in the scalar offset, and each lane's row offset in a vector
+// register that stays the same for every stage, so no vector register is
+// rewritten while a copy that reads it is in flight.
+struct CopyOffsets {
+    uint32_t a[ROWS_PER_WAVE / 16], b[ROWS_PER_WAVE / 16];  // operand data
+    uint32_t sa, sb;                                        // scale rows
+};
+
+__device__ __forceinline__ CopyOffsets copy_offsets(int64_t lda, int64_t ldb, int64_t lds_a, int64_t lds_b, int wave,
+                                                    int lane)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][GBM * GKB];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][GBN * GKB];
-    __shared__ uint32_t Ss[2][2][GBM];  // scales: [stage][A/B][row], 4 E8M0 bytes (two 64-deep steps x 2 halves)
+    CopyOffsets o;
+#pragma unroll
+    for (int i = 0; i < ROWS_PER_WAVE / 16; ++i) {
+        const int row = ROWS_PER_WAVE * wave + 16 * i + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        o.a[i] = (uint32_t)(row * lda + 16 * c);
+        o.b[i] = (uint32_t)(row * ldb + 16 * c);
+    }
+    const int srow = ROWS_PER_WAVE * wave + lane;
+    o.sa = (uint32_t)(srow * lds_a);
+    o.sb = (uint32_t)(srow * lds_b);
+    return o;
+}
+
+// raw buffer over a tile's rows: base address, no stride, no range limit
+// (every offset the kernel forms is inside the operand)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_buffer(const uint8_t *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, -1, 0x00020000);
+}
+
+// One stage's copies into slot st; with SCALES, also the scales of stages
+// s0 .. s0 + 3 (each clamped to the last stage) into the slot's scale area:
+// wave w copies the 16 bytes of rows 64 w .. 64 w + 63, one row per lane, of
+// A's and B's scale rows; stage by stage (4 bytes a row) where K is not a
+// multiple of four stages.  (All copies of a call go through one restrict
+// pointer: the compiler tells LDS copies apart by the alias scopes of their
+// destinations and tracks only a few such scopes.)
+template <bool SCALES, bool PAD>
+__device__ __forceinline__ void copy_stage(uint8_t *__restrict__ st, __amdgpu_buffer_rsrc_t At,
+                                           __amdgpu_buffer_rsrc_t Bt, __amdgpu_buffer_rsrc_t SAt,
+                                           __amdgpu_buffer_rsrc_t SBt, const CopyOffsets &o, int kb, int s0, int nk,
+                                           int wave)
+{
+#pragma unroll
+    for (int i = 0; i < ROWS_PER_WAVE / 16; ++i) {
+        const int R0 = ROWS_PER_WAVE * wave + 16 * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(At, (lds_void *)(st + ST_A + R0 * GKB), 16, o.a[i], kb, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(Bt, (lds_void *)(st + ST_B + R0 * GKB), 16, o.b[i], kb, 0, 0);
+    }
+    if constexpr (SCALES && !PAD) {
+        const int s = min(s0, nk - 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(SAt, (lds_void *)(st + SG_A + 16 * ROWS_PER_WAVE * wave), 16, o.sa,
+                                                 4 * s, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(SBt, (lds_void *)(st + SG_B + 16 * ROWS_PER_WAVE * wave), 16, o.sb,
+                                                 4 * s, 0, 0);
+    } else if constexpr (SCALES) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = min(s0 + j, nk - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                SAt, (lds_void *)(st + SG_A + 4 * GBM * j + 4 * ROWS_PER_WAVE * wave), 4, o.sa, 4 * s, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                SBt, (lds_void *)(st + SG_B + 4 * GBN * j + 4 * ROWS_PER_WAVE * wave), 4, o.sb, 4 * s, 0, 0);
+        }
+    }
+}
+
+// Operand fragments of one 32-element K step (kk = 0 or 1 of a stage): lane
+// (r32, h) holds the 16-byte chunk 2 kk + h of its row in each of the wave's
+// A and B tiles.
+struct Frags {
+    uint4 a[TM], b[TN];
+};
+
+__device__ __forceinline__ void read_frags(Frags &f, const uint8_t *__restrict__ st, int kk, int wm, int wn, int r32,
+                                           int h)
+{
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        f.a[i] = *reinterpret_cast<const uint4 *>(st + ST_A + lds_off((wm * TM + i) * 32 + r32, 2 * kk + h));
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+        f.b[j] = *reinterpret_cast<const uint4 *>(st + ST_B + lds_off((wn * TN + j) * 32 + r32, 2 * kk + h));
+}
+
+// keep (m = ~0) or zero (m = 0) the A fragments: a product with zero A adds
+// exact zeros
+__device__ __forceinline__ void mask_frags(Frags &f, uint32_t m)
+{
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        f.a[i].x &= m;
+        f.a[i].y &= m;
+        f.a[i].z &= m;
+        f.a[i].w &= m;
+    }
+}
+
+// Scale words of a group for the lane's rows, word j for the group's stage j,
+// shifted right by 8 h: the MFMA of step kk then takes byte 2 kk of it (block
+// 2 kk + h of the stage), chosen by the scale operand's byte select.
+struct ScaleGroup {
+    uint4 a[TM], b[TN];
+};
+
+__device__ __forceinline__ uint4 shr4(uint4 v, int sh) { return uint4{v.x >> sh, v.y >> sh, v.z >> sh, v.w >> sh}; }
+
+template <bool PAD>
+__device__ __forceinline__ void read_scales(ScaleGroup &g, const uint8_t *__restrict__ sg, int wm, int wn, int r32,
+                                            int h)
+{
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int row = (wm * TM + i) * 32 + r32;
+        if constexpr (!PAD) {
+            g.a[i] = *reinterpret_cast<const uint4 *>(sg + SG_A + 16 * row);
+        } else {
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(sg + SG_A) + row;
+            g.a[i] = uint4{p[0], p[GBM], p[2 * GBM], p[3 * GBM]};
+        }
+        g.a[i] = shr4(g.a[i], 8 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int row = (wn * TN + j) * 32 + r32;
+        if constexpr (!PAD) {
+            g.b[j] = *reinterpret_cast<const uint4 *>(sg + SG_B + 16 * row);
+        } else {
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(sg + SG_B) + row;
+            g.b[j] = uint4{p[0], p[GBN], p[2 * GBN], p[3 * GBN]};
+        }
+        g.b[j] = shr4(g.b[j], 8 * h);
+    }
+}
+
+__device__ __forceinline__ int word_of(const uint4 &v, int j)
+{
+    return (int)(j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w);
+}
+
+// the MFMAs of K step KK of the group's stage j
+template <bool FP4, int KK>
+__device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags &f, const ScaleGroup &g, int j)
+{
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) {
+            if constexpr (FP4) {
+                const v8i a8 = {(int)f.a[i].x, (int)f.a[i].y, (int)f.a[i].z, (int)f.a[i].w, 0, 0, 0, 0};
+                const v8i b8 = {(int)f.b[n].x, (int)f.b[n].y, (int)f.b[n].z, (int)f.b[n].w, 0, 0, 0, 0};
+                acc[i][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][n], 4, 4, 2 * KK,
+                                                                             word_of(g.a[i], j), 2 * KK,
+                                                                             word_of(g.b[n], j));
+            } else {
+                acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, f.a[i]),
+                                                                   __builtin_bit_cast(v8bf, f.b[n]), acc[i][n], 0, 0,
+                                                                   0);
+            }
+        }
+}
+
+// The main loop over a ring of four LDS stages.  Step k multiplies stage k in
+// two K steps.  The first runs on fragments read during the previous step
+// while the second's fragments are read; between the two, the wave waits for
+// those reads and for its own copies of stage k + 1, and meets the other
+// waves at the barrier: stage k + 1 is then complete in LDS and no wave reads
+// stage k any more, so its slot takes the copy of stage k + 4 (three steps of
+// copy latency hidden) while stage k + 1's first fragments are read under the
+// second K step.  Slot 0 receives the first stage of each group of four, and
+// with it the group's scales, which the wave reads into registers one step
+// ahead of the group.  Every step has the same shape: past the last stage,
+// the copy re-reads the last stage into the free slot and the reads of
+// "stage k + 1" go unused; the steps that round the count up to a multiple
+// of four multiply zeroed fragments.  So the body has no branches around
+// matrix work and the scheduling barriers hold the order within it.  Restrict
+// slot pointers tell the compiler which slot each access touches, so the
+// copies into the other slots stay in flight.
+template <bool FP4, bool PAD>
+__device__ __forceinline__ void gemm_step(v16f (&acc)[TM][TN], Frags &f0, Frags &f1, ScaleGroup &g,
+                                          uint8_t *__restrict__ cur, const uint8_t *__restrict__ nx,
+                                          __amdgpu_buffer_rsrc_t At, __amdgpu_buffer_rsrc_t Bt,
+                                          __amdgpu_buffer_rsrc_t SAt, __amdgpu_buffer_rsrc_t SBt, const CopyOffsets &o,
+                                          int k, int nk, int j, int wave, int wm, int wn, int r32, int h)
+{
+    // j = k mod 4, a constant at each call (one function for the four
+    // positions: the compiler then keeps the slots' alias scopes apart)
+    constexpr int SC = scale_copies(FP4, PAD);
+    read_frags(f1, cur, 1, wm, wn, r32, h);
+    if constexpr (PAD) mask_frags(f1, k < nk ? ~0u : 0u);  // a step past the end adds exact zeros
+    mfma_step<FP4, 0>(acc, f0, g, j);
+    // the second K step's fragment reads go out first, under these MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+    UFP4_SCHED_FENCE();
+    // the copies issued at the two previous steps (stages k + 2, k + 3) may
+    // still be in flight; the group's scales went with the copy at position 0
+    if (j == 1 || j == 2)
+        UFP4_WAIT_VM_LDS(2 * DATA_COPIES + SC);
+    else
+        UFP4_WAIT_VM_LDS(2 * DATA_COPIES);
+    UFP4_CFENCE();
+    __builtin_amdgcn_s_barrier();
+    UFP4_CFENCE();
+    UFP4_SCHED_FENCE();
+    if (FP4 && j == 0)
+        copy_stage<true, PAD>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, k + 4, nk, wave);
+    else
+        copy_stage<false, PAD>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, 0, nk, wave);
+    read_frags(f0, nx, 0, wm, wn, r32, h);
+    ScaleGroup gn;
+    if (FP4 && j == 3) read_scales<PAD>(gn, nx, wm, wn, r32, h);
+    if constexpr (PAD) mask_frags(f0, k + 1 < nk ? ~0u : 0u);
+    mfma_step<FP4, 1>(acc, f1, g, j);
+    UFP4_SCHED_FENCE();
+    if (FP4 && j == 3) g = gn;
+}
+
+template <bool FP4, bool PAD>
+__device__ __forceinline__ void gemm_main(v16f (&acc)[TM][TN], uint8_t *__restrict__ P0, uint8_t *__restrict__ P1,
+                                          uint8_t *__restrict__ P2, uint8_t *__restrict__ P3, const uint8_t *A, const uint8_t *B, const uint8_t *SA, const uint8_t *SB,
+                                          int64_t lda, int64_t ldb, int64_t lds_a, int64_t lds_b, int64_t m0,
+                                          int64_t n0, int nk, int wave, int lane, int wm, int wn, int r32, int h)
+{
+    const CopyOffsets o = copy_offsets(lda, ldb, lds_a, lds_b, wave, lane);
+    // wave-uniform tile bases
+    const __amdgpu_buffer_rsrc_t At = tile_buffer(A + m0 * lda), Bt = tile_buffer(B + n0 * ldb);
+    const __amdgpu_buffer_rsrc_t SAt = tile_buffer(FP4 ? SA + m0 * lds_a : A);
+    const __amdgpu_buffer_rsrc_t SBt = tile_buffer(FP4 ? SB + n0 * lds_b : B);
+    // prologue: stages 0 .. 3 (the last stage again where there are fewer)
+    // and the scales of the first group
+    copy_stage<FP4, PAD>(P0, At, Bt, SAt, SBt, o, 0, 0, nk, wave);
+    copy_stage<false, PAD>(P1, At, Bt, SAt, SBt, o, min(1, nk - 1) * GKB, 0, nk, wave);
+    copy_stage<false, PAD>(P2, At, Bt, SAt, SBt, o, min(2, nk - 1) * GKB, 0, nk, wave);
+    copy_stage<false, PAD>(P3, At, Bt, SAt, SBt, o, min(3, nk - 1) * GKB, 0, nk, wave);
+    UFP4_WAIT_VM(3 * DATA_COPIES);
+    UFP4_CFENCE();
+    __builtin_amdgcn_s_barrier();
+    UFP4_CFENCE();
+    Frags f0, f1;
+    ScaleGroup g{};
+    read_frags(f0, P0, 0, wm, wn, r32, h);
+    if constexpr (FP4) read_scales<PAD>(g, P0, wm, wn, r32, h);
+#define UFP4_STEP(J, CUR, NX) \
+    gemm_step<FP4, PAD>(acc, f0, f1, g, CUR, NX, At, Bt, SAt, SBt, o, kt + (J), nk, J, wave, wm, wn, r32, h)
+    // whole groups of four steps; the steps past the end multiply zeros
+    for (int kt = 0; kt < nk; kt += 4) {
+        UFP4_STEP(0, P0, P1);
+        UFP4_STEP(1, P1, P2);
+        UFP4_STEP(2, P2, P3);
+        UFP4_STEP(3, P3, P0);
+    }
+#undef UFP4_STEP
+    // no copy may still be writing LDS when the workgroup ends
+    UFP4_WAIT_VM(0);
+}
+
+template <bool FP4, bool PAD>
+__global__ __launch_bounds__(GTH, 1) void gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
+                                                      const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                                                      int M, int N, int64_t kbytes, int64_t lda, int64_t ldb,
+                                                      int64_t lds_a, int64_t lds_b, float *__restrict__ C, int64_t ldc)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t ring[GNS][ST_BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / GWN, wn = wave % GWN;
     const int r32 = lane & 31, h = lane >> 5;
     int tm, tn;
     tile_of(blockIdx.x, M / GBM, N / GBN, tm, tn);
     const int64_t m0 = (int64_t)tm * GBM, n0 = (int64_t)tn * GBN;
 
-    // global -> register staging: 4 chunks of A and 4 of B per thread; thread
-    // t handles chunk q = t + 256 i (row q / 4, 16-byte chunk q % 4)
-    const int srow = tid >> 2, sc = tid & 3;
-    const uint8_t *ga = A + (m0 + srow) * lda + sc * 16;
-    const uint8_t *gb = B + (n0 + srow) * ldb + sc * 16;
-    const int64_t a_step = 64 * lda, b_step = 64 * ldb;  // rows advance by 64 per i
-    const uint8_t *gsa = FP4 ? SA + (m0 + tid) * lds_a : nullptr;
-    const uint8_t *gsb = FP4 ? SB + (n0 + tid) * lds_b : nullptr;
-
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-    uint32_t rsa = 0, rsb = 0;
-#define UFP4_GLOAD(kb)                                                              \
-    do {                                                                            \
-        ra0 = *reinterpret_cast<const uint4 *>(ga + (kb));                          \
-        ra1 = *reinterpret_cast<const uint4 *>(ga + a_step + (kb));                 \
-        ra2 = *reinterpret_cast<const uint4 *>(ga + 2 * a_step + (kb));             \
-        ra3 = *reinterpret_cast<const uint4 *>(ga + 3 * a_step + (kb));             \
-        rb0 = *reinterpret_cast<const uint4 *>(gb + (kb));                          \
-        rb1 = *reinterpret_cast<const uint4 *>(gb + b_step + (kb));                 \
-        rb2 = *reinterpret_cast<const uint4 *>(gb + 2 * b_step + (kb));             \
-        rb3 = *reinterpret_cast<const uint4 *>(gb + 3 * b_step + (kb));             \
-        if constexpr (FP4) {                                                        \
-            rsa = *reinterpret_cast<const uint32_t *>(gsa + ((kb) >> 4));           \
-            rsb = *reinterpret_cast<const uint32_t *>(gsb + ((kb) >> 4));           \
-        }                                                                           \
-    } while (0)
-#define UFP4_LSTORE(st)                                                                             \
-    do {                                                                                            \
-        *reinterpret_cast<uint4 *>(&As[st][lds_off(srow, sc)]) = ra0;                               \
-        *reinterpret_cast<uint4 *>(&As[st][lds_off(srow + 64, sc)]) = ra1;                          \
-        *reinterpret_cast<uint4 *>(&As[st][lds_off(srow + 128, sc)]) = ra2;                         \
-        *reinterpret_cast<uint4 *>(&As[st][lds_off(srow + 192, sc)]) = ra3;                         \
-        *reinterpret_cast<uint4 *>(&Bs[st][lds_off(srow, sc)]) = rb0;                               \
-        *reinterpret_cast<uint4 *>(&Bs[st][lds_off(srow + 64, sc)]) = rb1;                          \
-        *reinterpret_cast<uint4 *>(&Bs[st][lds_off(srow + 128, sc)]) = rb2;                         \
-        *reinterpret_cast<uint4 *>(&Bs[st][lds_off(srow + 192, sc)]) = rb3;                         \
-        if constexpr (FP4) {                                                                        \
-            Ss[st][0][tid] = rsa;                                                                   \
-            Ss[st][1][tid] = rsb;                                                                   \
-        }                                                                                           \
-    } while (0)
-
-    v16f acc[4][4];
+    v16f acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+        for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
 
     const int nk = (int)(kbytes / GKB);
-    UFP4_GLOAD(0);
-    UFP4_LSTORE(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & 1;
-        if (kt + 1 < nk) UFP4_GLOAD((int64_t)(kt + 1) * GKB);
-        // scale words of this wave's rows: byte b holds the E8M0 scale of the
-        // stage's 32-element block b; step kk, half h uses block 2 kk + h
-        uint32_t wsa[4], wsb[4];
-        if constexpr (FP4) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                wsa[i] = Ss[s][0][wm * 128 + i * 32 + r32] >> (8 * h);
-                wsb[i] = Ss[s][1][wn * 128 + i * 32 + r32] >> (8 * h);
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            uint4 fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ra_ = wm * 128 + i * 32 + r32;
-                const int rb_ = wn * 128 + i * 32 + r32;
-                fa[i] = *reinterpret_cast<const uint4 *>(&As[s][lds_off(ra_, 2 * kk + h)]);
-                fb[i] = *reinterpret_cast<const uint4 *>(&Bs[s][lds_off(rb_, 2 * kk + h)]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (FP4) {
-                        const v8i a8 = {(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0};
-                        const v8i b8 = {(int)fb[j].x, (int)fb[j].y, (int)fb[j].z, (int)fb[j].w, 0, 0, 0, 0};
-                        const int sa_ = (int)((wsa[i] >> (16 * kk)) & 0xFFu);
-                        const int sb_ = (int)((wsb[j] >> (16 * kk)) & 0xFFu);
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0, sa_,
-                                                                                     0, sb_);
-                    } else {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fa[i]),
-                                                                           __builtin_bit_cast(v8bf, fb[j]),
-                                                                           acc[i][j], 0, 0, 0);
-                    }
-                }
-        }
-        if (kt + 1 < nk) UFP4_LSTORE(s ^ 1);
-        __syncthreads();
-    }
-
-#undef UFP4_GLOAD
-#undef UFP4_LSTORE
+    if (nk > 0)
+        gemm_main<FP4, PAD>(acc, ring[0], ring[1], ring[2], ring[3], A, B, SA, SB, lda, ldb, lds_a, lds_b, m0, n0, nk, wave, lane, wm, wn,
+                            r32, h);
 
     // epilogue: accumulator element e of lane l is C[8(e/4) + 4h + e%4][l%32]
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t rbase = m0 + wm * 128 + i * 32 + 4 * h;
-            const int64_t col = n0 + wn * 128 + j * 32 + r32;
+        for (int j = 0; j < TN; ++j) {
+            const int64_t rbase = m0 + (wm * TM + i) * 32 + 4 * h;
+            const int64_t col = n0 + (wn * TN + j) * 32 + r32;
 #pragma unroll
             for (int e = 0; e < 16; ++e) C[(rbase + 8 * (e >> 2) + (e & 3)) * ldc + col] = acc[i][j][e];
         }
 }
+#undef UFP4_WAIT_VM
+#undef UFP4_WAIT_VM_LDS
+#undef UFP4_CFENCE
+#undef UFP4_SCHED_FENCE
 
 hipError_t launch_gemm_mxfp4(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb, int64_t M,
                              int64_t N, int64_t K, float *c, int64_t ldc, hipStream_t st)
 {
     const dim3 grid((unsigned)((M / GBM) * (N / GBN)));
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(GT), 0, st, a, sa, b, sb, (int)M, (int)N, K / 2, K / 2, K / 2,
-                       K / 32, K / 32, c, ldc);
+    const int64_t nk = K / 2 / GKB;
+    // whole groups of four stages with 16-byte aligned scale rows take the
+    // 16-byte scale copies; any other K the per-stage ones
+    const bool pad = (nk % 4) != 0 || ((uintptr_t)sa | (uintptr_t)sb | (uint64_t)(K / 32)) % 16 != 0;
+    if (pad)
+        hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(GTH), 0, st, a, sa, b, sb, (int)M, (int)N, K / 2,
+                           K / 2, K / 2, K / 32, K / 32, c, ldc);
+    else
+        hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(GTH), 0, st, a, sa, b, sb, (int)M, (int)N, K / 2,
+                           K / 2, K / 2, K / 32, K / 32, c, ldc);
     return hipGetLastError();
 }
 
@@ -194,9 +419,13 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t M, int
                             int64_t ldb, float *c, int64_t ldc, hipStream_t st)
 {
     const dim3 grid((unsigned)((M / GBM) * (N / GBN)));
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(GT), 0, st, reinterpret_cast<const uint8_t *>(a), nullptr,
-                       reinterpret_cast<const uint8_t *>(b), nullptr, (int)M, (int)N, K * 2, lda * 2, ldb * 2,
-                       (int64_t)0, (int64_t)0, c, ldc);
+    const uint8_t *a8 = reinterpret_cast<const uint8_t *>(a), *b8 = reinterpret_cast<const uint8_t *>(b);
+    if (((K * 2 / GKB) % 4) != 0)
+        hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(GTH), 0, st, a8, nullptr, b8, nullptr, (int)M,
+                           (int)N, K * 2, lda * 2, ldb * 2, (int64_t)0, (int64_t)0, c, ldc);
+    else
+        hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(GTH), 0, st, a8, nullptr, b8, nullptr, (int)M,
+                           (int)N, K * 2, lda * 2, ldb * 2, (int64_t)0, (int64_t)0, c, ldc);
     return hipGetLastError();
 }
 

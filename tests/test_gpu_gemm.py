@@ -26,7 +26,7 @@ def oracle_operand(x_bits, ocfg, bf16=False):
     return O.bf16_round(d) if bf16 else d
 
 
-SHAPES = [(256, 256, 128), (512, 256, 384), (256, 768, 1024)]
+SHAPES = [(256, 256, 128), (512, 256, 384), (256, 768, 1024), (512, 512, 640), (256, 512, 2560)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

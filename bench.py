@@ -12,8 +12,9 @@ than the 256 MB Infinity Cache) so that every step reads HBM.
 value = bf16 input bytes quantized per second (2 bytes x 2 quantizations x n
 per step / step time).  The roofline object is for the dominant kernel, the
 fused RHT + quantize kernel: algorithmic bytes per launch (bf16 in + packed
-codes + E4M3 scales = 171,966,464 B) over its average launch time from HIP
-events on the stream it runs on.  The secondary `qgemm` object times the
+codes + E4M3 scales = 171,966,464 B) over its average duration in the timed
+steps, from HIP events that the launch itself timestamps (hipExtLaunchKernel,
+through ufp4_time_next_launch) on the stream it runs on.  The secondary `qgemm` object times the
 MXFP4 block-scaled GEMM at 8192^3 (A, B: N(0,1) bf16 -> RHT -> MXFP4).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
@@ -47,7 +48,8 @@ def parse():
     p.add_argument("--copies", type=int, default=8)
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--no-gemm", action="store_true", help="skip the qgemm leg")
-    p.add_argument("--cpu-rows", type=int, default=4096)
+    p.add_argument("--cpu-rows", type=int, default=ROWS)
+    p.add_argument("--cpu-reps", type=int, default=2)
     return p.parse_args()
 
 
@@ -67,17 +69,21 @@ def traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x_bits, rows):
+def cpu_baseline(x_bits, rows, reps):
+    """The oracle, as it is, on the host: the bench step (amax + quantize for
+    E2M1 and E1M2) over the first `rows` rows, `reps` times."""
     import oracle as O
     sample = np.ascontiguousarray(x_bits[:rows])
     t0 = time.perf_counter()
-    for fmt in ("e2m1", "e1m2"):
-        cfg = O.Cfg(fmt, "e4m3", rht="random", rht_seed=0)
-        a = O.amax(sample, cfg)
-        O.quantize(sample, cfg, amax_value=a)
+    for _ in range(reps):
+        for fmt in ("e2m1", "e1m2"):
+            cfg = O.Cfg(fmt, "e4m3", rht="random", rht_seed=0)
+            a = O.amax(sample, cfg)
+            O.quantize(sample, cfg, amax_value=a)
     dt = time.perf_counter() - t0
-    return {"value": round(2 * 2 * sample.size / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of 8192 rows (two-level E2M1 and E1M2, amax + quantize, RHT), "
+    what = "the whole step" if rows == ROWS else f"the step on the first {rows} of {ROWS} rows"
+    return {"value": round(reps * 2 * 2 * sample.size / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what} (two-level E2M1 and E1M2, amax + quantize, RHT) x {reps}, "
                       f"{dt:.1f} s single-threaded plain C",
             "seconds": round(dt, 2)}
 
@@ -111,15 +117,16 @@ def main():
         for f, cfg in enumerate(cfgs):
             U.ufp4_amax(xs[j], cfg, out=amaxes[j][f], ws=amax_ws)
             if ev is not None:
-                ev[f][0].record(stream)
+                # the quantize kernel timestamps its own dispatch on these events
+                U.ufp4_time_next_launch(ev[f][0], ev[f][1])
             U.ufp4_quantize(xs[j], cfg, amax=amaxes[j][f], out=outs[j][f])
-            if ev is not None:
-                ev[f][1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in cfgs] for _ in range(args.steps)]
+    for e in (e for step_ev in evs for pair in step_ev for e in pair):
+        e.record(stream)  # create the events before the timed region
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -161,21 +168,34 @@ def main():
     if not args.no_gemm:
         out["qgemm"] = bench_gemm(U, S, torch, dev, stream)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x_bits, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(x_bits, args.cpu_rows, args.cpu_reps)
     print(json.dumps(out), flush=True)
 
 
-def _time(fn, torch, stream, reps):
+def _time(fn, torch, stream, reps, U=None):
+    """Milliseconds per call over reps back-to-back calls; with U, also the
+    mean duration of the first kernel each call launches, from events that
+    launch timestamps itself."""
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ks:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(reps):
+    for a, b in ks:
+        if U is not None:
+            U.ufp4_time_next_launch(a, b)
         fn()
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    per_call = e0.elapsed_time(e1) / reps
+    if U is None:
+        return per_call
+    return per_call, float(np.mean([a.elapsed_time(b) for a, b in ks]))
 
 
 def bench_gemm(U, S, torch, dev, stream, reps=10):
@@ -188,14 +208,15 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
     cfg = U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=0)
     qa, qb = U.ufp4_quantize(a, cfg), U.ufp4_quantize(b, cfg)
     c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ms = _time(lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c), torch, stream, reps)
+    ms_call, ms = _time(lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c), torch, stream, reps, U)
     cfg2 = U.Cfg("e1m2", "fp32", rht="random", rht_seed=0)
     ea, eb = U.ufp4_quantize(a, cfg2), U.ufp4_quantize(b, cfg2)
     ws = torch.empty(U.ufp4_workspace_size(U.OP_QGEMM, M + N, K, cfg2), dtype=torch.uint8, device=dev)
     ms_e1m2 = _time(lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws), torch, stream, reps)
-    ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps)
+    _, ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps, U)
     tf = flop / (ms * 1e-3) / 1e12
     return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out", "ms": round(ms, 4),
+            "ms_per_call_back_to_back": round(ms_call, 4),
             "tflops": round(tf, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tf / FP4_PEAK_TFLOPS, 4),
             "e1m2_dequant_bf16": {"ms": round(ms_e1m2, 4), "tflops": round(flop / (ms_e1m2 * 1e-3) / 1e12, 1),
                                   "note": "dequantize both operands to bf16 (workspace) + bf16 MFMA GEMM"},

@@ -73,10 +73,11 @@ _lib.ufp4_strerror.argtypes = [_i32]
 _lib.ufp4_strerror.restype = C.c_char_p
 _lib.ufp4_last_hip_error.restype = _i32
 _lib.ufp4_version.restype = _i32
+_lib.ufp4_time_next_launch.argtypes = [_p, _p]
 
 EXPORTS = ["ufp4_rht", "ufp4_amax", "ufp4_quantize", "ufp4_dequantize", "ufp4_stats", "ufp4_stats_finalize",
            "ufp4_qgemm", "ufp4_gemm_bf16", "ufp4_eta", "ufp4_workspace_size", "ufp4_strerror",
-           "ufp4_last_hip_error", "ufp4_version"]
+           "ufp4_last_hip_error", "ufp4_version", "ufp4_time_next_launch"]
 
 
 def lib():
@@ -302,3 +303,19 @@ def ufp4_last_hip_error() -> int:
 
 def ufp4_version() -> int:
     return int(_lib.ufp4_version())
+
+
+def ufp4_time_next_launch(start=None, stop=None) -> None:
+    """Make the next kernel the library launches from this thread timestamp
+    its own dispatch on two torch.cuda.Event objects (created with
+    enable_timing=True); start.elapsed_time(stop) is then that kernel's
+    duration.  No arguments clears a pending request."""
+    handles = []
+    for e in (start, stop):
+        if e is None:
+            handles.append(None)
+            continue
+        if not e.cuda_event:
+            e.record()  # torch creates the underlying event lazily
+        handles.append(e.cuda_event)
+    _check(_lib.ufp4_time_next_launch(handles[0], handles[1]), "ufp4_time_next_launch")

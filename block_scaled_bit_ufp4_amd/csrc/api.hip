@@ -17,6 +17,14 @@ using namespace ufp4;
 
 static thread_local int g_last_hip_error = 0;
 
+namespace ufp4 {
+LaunchTiming &launch_timing()
+{
+    static thread_local LaunchTiming t;
+    return t;
+}
+}  // namespace ufp4
+
 static int hip_fail(hipError_t e)
 {
     if (e == hipSuccess) return UFP4_OK;
@@ -122,6 +130,13 @@ const char *ufp4_strerror(int code)
 }
 
 int ufp4_last_hip_error(void) { return g_last_hip_error; }
+
+int ufp4_time_next_launch(void *start_event, void *stop_event)
+{
+    if ((start_event == nullptr) != (stop_event == nullptr)) return UFP4_ERR_INVALID_ARG;
+    launch_timing() = LaunchTiming{(hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return UFP4_OK;
+}
 
 size_t ufp4_workspace_size(int op, int64_t rows, int64_t cols, const ufp4_config *cfg)
 {

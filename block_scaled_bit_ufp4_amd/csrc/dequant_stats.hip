@@ -100,14 +100,14 @@ static hipError_t deq_pick(int inverse_rht, int out_dtype, const DeqArgs &a, hip
     const dim3 grid((unsigned)((a.n_oct + DT * DU - 1) / (DT * DU)));
     if (inverse_rht) {
         if (out_dtype == IN_F32)
-            hipLaunchKernelGGL((dequant_kernel<F, S, true, IN_F32>), grid, dim3(DT), 0, st, a);
+            launch_kernel((dequant_kernel<F, S, true, IN_F32>), grid, dim3(DT), st, a);
         else
-            hipLaunchKernelGGL((dequant_kernel<F, S, true, IN_BF16>), grid, dim3(DT), 0, st, a);
+            launch_kernel((dequant_kernel<F, S, true, IN_BF16>), grid, dim3(DT), st, a);
     } else {
         if (out_dtype == IN_F32)
-            hipLaunchKernelGGL((dequant_kernel<F, S, false, IN_F32>), grid, dim3(DT), 0, st, a);
+            launch_kernel((dequant_kernel<F, S, false, IN_F32>), grid, dim3(DT), st, a);
         else
-            hipLaunchKernelGGL((dequant_kernel<F, S, false, IN_BF16>), grid, dim3(DT), 0, st, a);
+            launch_kernel((dequant_kernel<F, S, false, IN_BF16>), grid, dim3(DT), st, a);
     }
     return hipGetLastError();
 }
@@ -289,18 +289,18 @@ static hipError_t stats_pick(int in_dtype, int rht, const StatsArgs &a, hipStrea
     const dim3 grid((unsigned)g);
     if (in_dtype == IN_BF16) {
         if (rht)
-            hipLaunchKernelGGL((stats_kernel<F, S, IN_BF16, true>), grid, dim3(256), 0, st, a);
+            launch_kernel((stats_kernel<F, S, IN_BF16, true>), grid, dim3(256), st, a);
         else
-            hipLaunchKernelGGL((stats_kernel<F, S, IN_BF16, false>), grid, dim3(256), 0, st, a);
+            launch_kernel((stats_kernel<F, S, IN_BF16, false>), grid, dim3(256), st, a);
     } else {
         if (rht)
-            hipLaunchKernelGGL((stats_kernel<F, S, IN_F32, true>), grid, dim3(256), 0, st, a);
+            launch_kernel((stats_kernel<F, S, IN_F32, true>), grid, dim3(256), st, a);
         else
-            hipLaunchKernelGGL((stats_kernel<F, S, IN_F32, false>), grid, dim3(256), 0, st, a);
+            launch_kernel((stats_kernel<F, S, IN_F32, false>), grid, dim3(256), st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_partials_kernel<NS>, dim3(1), dim3(256), 0, st, a.partials, (int)g, a.sums);
+    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(256), st, a.partials, (int)g, a.sums);
     return hipGetLastError();
 }
 
@@ -347,10 +347,10 @@ __global__ __launch_bounds__(256) void eta_kernel(const float *zq, const float *
 hipError_t launch_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, double *partials,
                       double *sums, hipStream_t st)
 {
-    hipLaunchKernelGGL(eta_kernel, dim3(ETA_WGS), dim3(256), 0, st, zq, z, M, N, ld, partials);
+    launch_kernel(eta_kernel, dim3(ETA_WGS), dim3(256), st, zq, z, M, N, ld, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_partials_kernel<3>, dim3(1), dim3(256), 0, st, partials, ETA_WGS, sums);
+    launch_kernel(reduce_partials_kernel<3>, dim3(1), dim3(256), st, partials, ETA_WGS, sums);
     return hipGetLastError();
 }
 

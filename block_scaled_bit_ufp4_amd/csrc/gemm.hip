@@ -407,10 +407,10 @@ hipError_t launch_gemm_mxfp4(const uint8_t *a, const uint8_t *sa, const uint8_t 
     // 16-byte scale copies; any other K the per-stage ones
     const bool pad = (nk % 4) != 0 || ((uintptr_t)sa | (uintptr_t)sb | (uint64_t)(K / 32)) % 16 != 0;
     if (pad)
-        hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(GTH), 0, st, a, sa, b, sb, (int)M, (int)N, K / 2,
+        launch_kernel((gemm_kernel<true, true>), grid, dim3(GTH), st, a, sa, b, sb, (int)M, (int)N, K / 2,
                            K / 2, K / 2, K / 32, K / 32, c, ldc);
     else
-        hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(GTH), 0, st, a, sa, b, sb, (int)M, (int)N, K / 2,
+        launch_kernel((gemm_kernel<true, false>), grid, dim3(GTH), st, a, sa, b, sb, (int)M, (int)N, K / 2,
                            K / 2, K / 2, K / 32, K / 32, c, ldc);
     return hipGetLastError();
 }
@@ -421,10 +421,10 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t M, int
     const dim3 grid((unsigned)((M / GBM) * (N / GBN)));
     const uint8_t *a8 = reinterpret_cast<const uint8_t *>(a), *b8 = reinterpret_cast<const uint8_t *>(b);
     if (((K * 2 / GKB) % 4) != 0)
-        hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(GTH), 0, st, a8, nullptr, b8, nullptr, (int)M,
+        launch_kernel((gemm_kernel<false, true>), grid, dim3(GTH), st, a8, nullptr, b8, nullptr, (int)M,
                            (int)N, K * 2, lda * 2, ldb * 2, (int64_t)0, (int64_t)0, c, ldc);
     else
-        hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(GTH), 0, st, a8, nullptr, b8, nullptr, (int)M,
+        launch_kernel((gemm_kernel<false, false>), grid, dim3(GTH), st, a8, nullptr, b8, nullptr, (int)M,
                            (int)N, K * 2, lda * 2, ldb * 2, (int64_t)0, (int64_t)0, c, ldc);
     return hipGetLastError();
 }

@@ -2,10 +2,33 @@
 // the kernel files of libufp4 (internal; the public interface is ufp4.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace ufp4 {
+
+// A pending request of ufp4_time_next_launch on this thread (both null when
+// none); the next launch_kernel takes and clears it.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming &launch_timing();
+
+// Every library kernel starts here: a plain launch, or one that timestamps
+// its own dispatch on the requested events.
+template <typename... Params, typename... Args>
+inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t st, Args... args)
+{
+    LaunchTiming &t = launch_timing();
+    if (t.start) {
+        const LaunchTiming req = t;
+        t = LaunchTiming{};
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, req.start, req.stop, 0, static_cast<Params>(args)...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, static_cast<Params>(args)...);
+    }
+}
 
 // Row kernel: one lane per 16-element chunk of a view row.
 struct RowArgs {

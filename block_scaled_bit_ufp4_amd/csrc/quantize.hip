@@ -604,11 +604,11 @@ static hipError_t launch_one(int axis, const RowArgs &ra, const ColArgs &ca, hip
         if (ra.n_ch == 0) return hipSuccess;
         constexpr int U = MODE == MODE_AMAX ? RUA : RU;
         const int64_t wgs = (ra.n_ch + RT * U - 1) / (RT * U);
-        hipLaunchKernelGGL((row_kernel<MODE, F, S, SR, IN, RHT, OUT, U>), dim3((unsigned)wgs), dim3(RT), 0, st, ra);
+        launch_kernel((row_kernel<MODE, F, S, SR, IN, RHT, OUT, U>), dim3((unsigned)wgs), dim3(RT), st, ra);
     } else {
         if (ca.R == 0 || ca.C == 0) return hipSuccess;
         const dim3 grid((unsigned)((ca.C + CTC - 1) / CTC), (unsigned)((ca.R + CTR - 1) / CTR));
-        hipLaunchKernelGGL((col_kernel<MODE, F, S, SR, IN, RHT, OUT>), grid, dim3(CT), 0, st, ca);
+        launch_kernel((col_kernel<MODE, F, S, SR, IN, RHT, OUT>), grid, dim3(CT), st, ca);
     }
     return hipGetLastError();
 }
@@ -672,7 +672,7 @@ hipError_t launch_amax(const LaunchSpec &sp, const RowArgs &ra, const ColArgs &c
                     : launch_one<MODE_AMAX, 0, 0, false, IN_F32, false, 0>(sp.axis, ra, ca, st);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(1024), 0, st, sp.axis == 0 ? ra.partials : ca.partials, tiles,
+    launch_kernel(amax_final_kernel, dim3(1), dim3(1024), st, sp.axis == 0 ? ra.partials : ca.partials, tiles,
                        amax);
     return hipGetLastError();
 }

@@ -236,6 +236,17 @@ int ufp4_last_hip_error(void);
 /* Library version, (major << 16) | minor. */
 int ufp4_version(void);
 
+/* Timing aid.  The next kernel this library launches from the calling thread
+ * records its own start and end on start_event and stop_event (hipEvent_t
+ * handles the caller created; hipExtLaunchKernel timestamps the dispatch
+ * itself, so hipEventElapsedTime between them is the kernel's duration
+ * without the gaps around it).  For ufp4_quantize that kernel is the
+ * quantize kernel, for ufp4_amax the amax pass, for ufp4_qgemm in
+ * UFP4_GEMM_NATIVE_MXFP4 mode the GEMM.  The request is consumed by that
+ * launch; passing two NULLs clears a pending one.  Per thread, no other
+ * effect.  Returns UFP4_OK, or UFP4_ERR_INVALID_ARG if exactly one is NULL. */
+int ufp4_time_next_launch(void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

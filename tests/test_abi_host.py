@@ -136,3 +136,13 @@ def test_stats_finalize_matches_oracle_report():
     np.testing.assert_array_equal(a["counts"], b["counts"])
     np.testing.assert_allclose(a["bucket_bias"], b["bucket_bias"], rtol=1e-15)
     assert np.isnan(a["bucket_bias"][0, 4])
+
+
+def test_time_next_launch_needs_both_events_or_none():
+    import ctypes
+    import block_scaled_bit_ufp4_amd as U
+    lib = U.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.ufp4_time_next_launch(fake, None) == -1
+    assert lib.ufp4_time_next_launch(None, fake) == -1
+    assert lib.ufp4_time_next_launch(None, None) == 0   # clears; launches nothing

@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--copies", type=int, default=8)
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--no-gemm", action="store_true", help="skip the qgemm leg")
+    p.add_argument("--no-configs", action="store_true", help="skip the per-workload kernel timings")
     p.add_argument("--cpu-rows", type=int, default=ROWS)
     p.add_argument("--cpu-reps", type=int, default=2)
     return p.parse_args()
@@ -167,6 +168,8 @@ def main():
     }
     if not args.no_gemm:
         out["qgemm"] = bench_gemm(U, S, torch, dev, stream)
+    if not args.no_configs:
+        out["configs"] = bench_configs(U, S, torch, dev, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x_bits, args.cpu_rows, args.cpu_reps)
     print(json.dumps(out), flush=True)
@@ -222,6 +225,107 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
                                   "note": "dequantize both operands to bf16 (workspace) + bf16 MFMA GEMM"},
             "bf16_reference": {"ms": round(ms_bf16, 4), "tflops": round(flop / (ms_bf16 * 1e-3) / 1e12, 1),
                                "peak_tflops": 2500.0}}
+
+
+def _ktime(U, torch, stream, fn, reps=10):
+    """Mean duration (ms) of the first kernel fn launches, over reps calls,
+    from events that kernel's dispatch timestamps itself."""
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for a, b in evs:
+        U.ufp4_time_next_launch(a, b)
+        fn()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def _qbytes(n, cfg):
+    """Algorithmic bytes of one quantize pass over n bf16 elements."""
+    scale = 4 * n // cfg.block if cfg.scale == "fp32" else n // cfg.block
+    return 2 * n + n // 2 + scale
+
+
+def _leg(U, torch, stream, x, cfg, amax=None):
+    """Kernel time and HBM rate of one quantize call (amax given for E4M3)."""
+    q = U.alloc_qtensor(x.shape[0], x.shape[1], cfg)
+    ms = _ktime(U, torch, stream, lambda: U.ufp4_quantize(x, cfg, amax=amax, out=q))
+    b = _qbytes(x.numel(), cfg)
+    return {"us": round(ms * 1e3, 2), "bytes": b, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}, q
+
+
+def bench_configs(U, S, torch, dev, stream):
+    """Kernel times of every workload: the quantizations of the five
+    configurations, with each kernel's algorithmic bytes and HBM rate."""
+    def dev_bf16(h):
+        return torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    out = {}
+    # quantize_x: 256x1024, FP32 1x16, no RHT (launch-bound; correctness config)
+    x = dev_bf16(S.quantize_x(256, 1024, seed=0))
+    c1 = {}
+    for fmt in ("e2m1", "e1m2"):
+        cfg = U.Cfg(fmt, "fp32")
+        leg, q = _leg(U, torch, stream, x, cfg)
+        leg["dequant_us"] = round(_ktime(U, torch, stream, lambda: U.ufp4_dequantize(q)) * 1e3, 2)
+        leg["stats_us"] = round(_ktime(U, torch, stream, lambda: U.ufp4_stats(x, q)) * 1e3, 2)
+        c1[fmt] = leg
+    out["quantize_x_256x1024"] = c1
+    # activations 8192^2: two-level E4M3, with and without RHT, and INT4
+    x = dev_bf16(S.activations_t3(ROWS, COLS, seed=0))
+    c2 = {}
+    for fmt, rht in (("e2m1", "random"), ("e2m1", "none"), ("e1m2", "random"), ("int4", "random")):
+        cfg = U.Cfg(fmt, "e4m3", rht=rht, rht_seed=0)
+        amax = U.ufp4_amax(x, cfg)
+        c2[f"{fmt}_{rht}"] = _leg(U, torch, stream, x, cfg, amax)[0]
+    cfg = U.Cfg("e2m1", "e4m3", rht="random", rht_seed=0)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(U.ufp4_workspace_size(U.OP_AMAX, ROWS, COLS, cfg), dtype=torch.uint8, device=dev)
+    ms = _ktime(U, torch, stream, lambda: U.ufp4_amax(x, cfg, out=amax, ws=ws))
+    c2["amax_pass"] = {"us": round(ms * 1e3, 2), "GBps": round(2 * x.numel() / (ms * 1e-3) / 1e9, 1)}
+    c2["rht_overhead_e2m1"] = round(c2["e2m1_random"]["us"] / c2["e2m1_none"]["us"] - 1, 4)
+    out["activations_8192x8192"] = c2
+    del x
+    # llama linear: E1M2, FP32 1x16, RHT-16 on all; SR (stream 0 row, 1 col) on dY
+    c3 = {}
+    for name, gen, shape in (("x", S.llama_x, (16384, 4096)), ("w", S.llama_w, (14336, 4096)),
+                             ("dy", S.llama_dy, (16384, 14336))):
+        x = dev_bf16(gen(*shape, seed=0))
+        for axis in ("row", "col"):
+            sr = name == "dy"
+            cfg = U.Cfg("e1m2", "fp32", rht="random", rht_seed=0, rounding="sr" if sr else "rtne", axis=axis,
+                        sr_seed=0, sr_stream=1 if axis == "col" else 0)
+            c3[f"{name}_{axis}"] = _leg(U, torch, stream, x, cfg)[0]
+        del x
+    tot_b = sum(v["bytes"] for v in c3.values())
+    tot_us = sum(v["us"] for v in c3.values())
+    c3["all_six"] = {"us": round(tot_us, 2), "bytes": tot_b, "GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1)}
+    out["llama_linear_e1m2"] = c3
+    # mxfp4 + if4 on 16384x8192
+    xh, _ = S.mx_if4(16384, 8192, seed=0)
+    x = dev_bf16(xh)
+    c4 = {"mxfp4_h16": _leg(U, torch, stream, x, U.Cfg("e2m1", "e8m0", 32, rht="det"))[0]}
+    for fmt in ("if4", "e2m1"):
+        cfg = U.Cfg(fmt, "e4m3")
+        c4[fmt if fmt == "if4" else "nvfp4"] = _leg(U, torch, stream, x, cfg, U.ufp4_amax(x, cfg))[0]
+    c4["if4_overhead_vs_nvfp4"] = round(c4["if4"]["us"] / c4["nvfp4"]["us"] - 1, 4)
+    out["mxfp4_if4_16384x8192"] = c4
+    del x
+    # gemm operands: 8192^2 to MXFP4 (RHT) and to E1M2 (RHT) with its bf16 dequantization
+    x = dev_bf16(S.gemm_a(ROWS, COLS, seed=0))
+    c5 = {"mxfp4_rht": _leg(U, torch, stream, x, U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=0))[0]}
+    leg, q = _leg(U, torch, stream, x, U.Cfg("e1m2", "fp32", rht="random", rht_seed=0))
+    y = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device=dev)
+    ms = _ktime(U, torch, stream, lambda: U.ufp4_dequantize(q, y=y))
+    leg["dequant_bf16_us"] = round(ms * 1e3, 2)
+    c5["e1m2_rht"] = leg
+    out["gemm_operands_8192x8192"] = c5
+    return out
 
 
 if __name__ == "__main__":

@@ -57,8 +57,9 @@ __device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1)
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1,
-                       (uint32_t)p0);
+        // three-way xors in one instruction each (v_bitop3_b32, truth table 0x96)
+        c = make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96), (uint32_t)p1,
+                       __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96), (uint32_t)p0);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
@@ -261,6 +262,19 @@ __device__ __forceinline__ uint32_t pack8_e2m1(const float *z)
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, z[4], z[5], 1.0f, 2);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, z[6], z[7], 1.0f, 3);
     return p;
+}
+
+// Two E2M1 codes (byte b of w: low nibble first) -> their values (exact;
+// the scale operand 1.0 leaves them unscaled).
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2f decode2_e2m1(uint32_t w, int b)
+{
+    switch (b) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    }
 }
 
 // 8 signed scaled values on the uniform grids -> 8 codes: the FP8 convert

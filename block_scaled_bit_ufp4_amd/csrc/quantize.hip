@@ -129,9 +129,17 @@ __device__ __forceinline__ void scaled8(const float *v, const BlockScale &b, flo
             for (int i = 0; i < 8; ++i) z[i] = (FOLD ? v[i] * 0.25f : v[i]) / b.s;
         }
         if constexpr (SR) {
+            // rare: a branch the whole wave takes or skips, so the common
+            // case pays no division
+            bool tiny = false;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (fabsf(z[i]) < 0x1p-100f && v[i] != 0.0f && b.s != 0.0f) z[i] = (FOLD ? v[i] * 0.25f : v[i]) / b.s;
+            for (int i = 0; i < 8; ++i) tiny |= fabsf(z[i]) < 0x1p-100f && v[i] != 0.0f && b.s != 0.0f;
+            if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (fabsf(z[i]) < 0x1p-100f && v[i] != 0.0f && b.s != 0.0f)
+                        z[i] = (FOLD ? v[i] * 0.25f : v[i]) / b.s;
+            }
         }
     }
 }
@@ -159,25 +167,6 @@ __device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b,
         packed = pack8_uniform<F>(z);
     }
     return b.s == 0.0f ? 0u : packed;
-}
-
-// IF4: both candidates for one element; returns the two magnitude codes and
-// the two binary32 squared errors.  a = |y|.
-__device__ __forceinline__ void if4_candidates(float a, const BlockScale &b, uint32_t &kf, uint32_t &ki,
-                                               float &ef, float &ei)
-{
-    constexpr float C76 = 7.0f / 6.0f;
-    constexpr float C67 = 6.0f / 7.0f;
-    const float zf = b.fast ? div_fast(a, b.s, b.invd) : a / b.s;
-    const float t = a * C76;
-    const float zi = b.fast ? div_fast(t, b.s, b.invd) : t / b.s;
-    kf = rtne_code<FMT_E2M1>(zf);
-    ki = rtne_code<FMT_INT4>(zi);
-    const float xf = grid_value<FMT_E2M1>(kf) * b.s;
-    const float xi = ((float)ki * b.s) * C67;
-    const float df = xf - a, di = xi - a;
-    ef = df * df;
-    ei = di * di;
 }
 
 // ---------------------------------------------------------------------------
@@ -274,6 +263,65 @@ __device__ __forceinline__ float absmax16(const float *v)
 
 // Quantize one transformed 16-element chunk held by this lane; returns the
 // codes (low word: elements 0..7) and sets the scale byte / value.
+// IF4 for one 16-element block: both candidates on signed values (each
+// error is odd in y, so its square equals the one of the |y| form): FP4
+// codes from the FP4 convert and their values from the FP4 decode; INT4 from
+// a clamp, RTNE to an integer and the FP8-convert packing.  Squared errors
+// summed pairwise, spans 1, 2, 4, 8; INT4 iff strictly smaller.  Sets the
+// flag in bit 7 of sbyte.
+__device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, uint32_t &lo, uint32_t &hi,
+                                          uint32_t &sbyte)
+{
+    constexpr float C76 = 7.0f / 6.0f;
+    constexpr float C67 = 6.0f / 7.0f;
+    float zf[16], zi[16];
+    if (bs.fast) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            zf[i] = sdiv_fast(v[i], bs.s, bs.invd);
+            zi[i] = sdiv_fast(v[i] * C76, bs.s, bs.invd);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            zf[i] = v[i] / bs.s;
+            zi[i] = (v[i] * C76) / bs.s;
+        }
+    }
+    const uint32_t lof = pack8_e2m1(zf), hif = pack8_e2m1(zf + 8);
+    float ef[16], ei[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const v2f g = decode2_e2m1(j < 4 ? lof : hif, j & 3);
+        const float d0 = g.x * bs.s - v[2 * j], d1 = g.y * bs.s - v[2 * j + 1];
+        ef[2 * j] = d0 * d0;
+        ef[2 * j + 1] = d1 * d1;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        zi[i] = __builtin_amdgcn_fmed3f(zi[i], -7.0f, 7.0f);
+        const float d = (__builtin_rintf(zi[i]) * bs.s) * C67 - v[i];
+        ei[i] = d * d;
+    }
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * w) {
+            ef[i] = ef[i] + ef[i + w];
+            ei[i] = ei[i] + ei[i + w];
+        }
+    const bool use_int = bs.s != 0.0f && ei[0] < ef[0];
+    if (use_int) {
+        lo = pack8_uniform<FMT_INT4>(zi);
+        hi = pack8_uniform<FMT_INT4>(zi + 8);
+    } else {
+        lo = lof;
+        hi = hif;
+    }
+    if (bs.s == 0.0f) lo = hi = 0;
+    sbyte |= use_int ? 0x80u : 0u;
+}
+
 template <int F, int S, bool SR, bool FOLD>
 __device__ __forceinline__ uint2 quant_chunk(const float *v, const TensorConst &tc, uint64_t n0, uint64_t sr_seed,
                                              uint32_t sr_stream, bool pair_max, uint32_t &sbyte, float &sval)
@@ -288,26 +336,7 @@ __device__ __forceinline__ uint2 quant_chunk(const float *v, const TensorConst &
     sval = bs.s;
     uint32_t lo = 0, hi = 0;
     if constexpr (F == FMT_IF4) {
-        uint32_t kf[16], ki[16];
-        float ef[16], ei[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) if4_candidates(fabsf(v[i]), bs, kf[i], ki[i], ef[i], ei[i]);
-        // pairwise: (0+1),(2+3),..., then pairs of pairs, four levels
-#pragma unroll
-        for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2 * w) {
-                ef[i] = ef[i] + ef[i + w];
-                ei[i] = ei[i] + ei[i + w];
-            }
-        const bool use_int = bs.s != 0.0f && ei[0] < ef[0];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t code = (f2u(v[i]) >> 28 & 8u) | (use_int ? ki[i] : kf[i]);
-            if (i < 8) lo |= code << (4 * i); else hi |= code << (4 * (i - 8));
-        }
-        if (bs.s == 0.0f) lo = hi = 0;
-        sbyte |= use_int ? 0x80u : 0u;
+        if4_chunk(v, bs, lo, hi, sbyte);
     } else {
         uint32_t w[16];
         if constexpr (SR) {
@@ -516,25 +545,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
             uint32_t lo = 0, hi = 0;
             uint32_t sbyte = bs.byte;
             if constexpr (F == FMT_IF4) {
-                uint32_t kf[16], ki[16];
-                float ef[16], ei[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) if4_candidates(fabsf(v[i]), bs, kf[i], ki[i], ef[i], ei[i]);
-#pragma unroll
-                for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2 * w) {
-                        ef[i] = ef[i] + ef[i + w];
-                        ei[i] = ei[i] + ei[i + w];
-                    }
-                const bool use_int = bs.s != 0.0f && ei[0] < ef[0];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint32_t code = (f2u(v[i]) >> 28 & 8u) | (use_int ? ki[i] : kf[i]);
-                    if (i < 8) lo |= code << (4 * i); else hi |= code << (4 * (i - 8));
-                }
-                if (bs.s == 0.0f) lo = hi = 0;
-                sbyte |= use_int ? 0x80u : 0u;
+                if4_chunk(v, bs, lo, hi, sbyte);
             } else {
                 uint32_t w[16];
                 if constexpr (SR) {

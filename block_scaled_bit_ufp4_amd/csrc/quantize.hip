@@ -38,6 +38,7 @@ constexpr int RUA = 8;   // row kernel: chunks per lane in the amax pass
 constexpr int CT = 256;  // column kernel: threads per workgroup
 constexpr int CTR = 512; // column kernel: source rows per workgroup
 constexpr int CTC = 64;  // column kernel: source columns per workgroup
+constexpr int COL_GROUP = 8;  // column kernel: row tiles dispatched together
 
 enum : int { MODE_QUANT = 0, MODE_AMAX = 1, MODE_RHT = 2 };
 
@@ -459,16 +460,42 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane & 7, b = lane >> 3;
-    const int64_t r0 = (int64_t)blockIdx.y * CTR + wave * 128 + b * 16;  // first source row of this lane
-    const int64_t c0 = (int64_t)blockIdx.x * CTC + g * 8;                // first source column
+    // Tile order: groups of COL_GROUP row tiles, row tile fastest, so the
+    // workgroups in flight write COL_GROUP x 256 contiguous code bytes of each
+    // view row while still sharing the source rows they read.
+    int ty, tx;
+    {
+        const int nx = (int)gridDim.x, ny = (int)gridDim.y;
+        const int bid = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        const int grp = bid / (COL_GROUP * nx), in = bid - grp * (COL_GROUP * nx);
+        const int gy = min(COL_GROUP, ny - grp * COL_GROUP);
+        ty = grp * COL_GROUP + in % gy;
+        tx = in / gy;
+    }
+    const int64_t r0 = (int64_t)ty * CTR + wave * 128 + b * 16;  // first source row of this lane
+    const int64_t c0 = (int64_t)tx * CTC + g * 8;                // first source column
     const bool active = r0 < a.R && c0 < a.C;
 
     TensorConst tc{0.f, 0.f, 0.f, false};
     if constexpr (MODE == MODE_QUANT) tc = tensor_const<F == FMT_IF4 ? FMT_E2M1 : F, S>(a.amax);
     if constexpr (MODE == MODE_QUANT && S == SC_E4M3) {
-        if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *a.tensor_scale = tc.alpha;
+        if (tx == 0 && ty == 0 && tid == 0) *a.tensor_scale = tc.alpha;
     }
     float lmax = 0.0f;
+
+    // A whole tile (in bounds, with 16-byte aligned output rows) stages its
+    // codes and scales in LDS; after a barrier the workgroup writes each view
+    // row's 256 bytes of codes and its scales as whole lines (written per
+    // lane, they would go out as scattered 32- and 16-byte pieces).
+    constexpr bool STAGE = MODE == MODE_QUANT;
+    constexpr int NB = CTR / 16;  // 16-row blocks in a tile
+    constexpr int CP = NB + 1;    // padded pitch (in uint2) of a view row's codes
+    __shared__ uint2 st_codes[STAGE ? CTC * CP : 1];
+    __shared__ float st_scale[STAGE && S == SC_FP32 ? CTC * CP : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t st_sbyte[STAGE && S != SC_FP32 ? CTC * NB : 16];
+    const bool staged = STAGE && (a.R % CTR) == 0 && (int64_t)(ty + 1) * CTR <= a.R &&
+                        (int64_t)(tx + 1) * CTC <= a.C &&
+                        (((uintptr_t)a.codes | (uintptr_t)a.scales) & 15) == 0;  // uniform in the workgroup
 
     // 16 rows x 8 columns, kept as loaded (bf16 pairs) until each column is
     // processed
@@ -559,6 +586,18 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
                 lo = encode8<F, S, FOLD, SR>(v, bs, w);
                 hi = encode8<F, S, FOLD, SR>(v + 8, bs, w + 8);
             }
+            if (staged) {
+                const int cl = g * 8 + j, rb = wave * 8 + b;  // tile-local view row, 16-row block
+                st_codes[cl * CP + rb] = make_uint2(lo, hi);
+                if constexpr (S == SC_E8M0) {
+                    if ((b & 1) == 0) st_sbyte[cl * NB + (rb >> 1)] = (uint8_t)sbyte;
+                } else if constexpr (S == SC_E4M3) {
+                    st_sbyte[cl * NB + rb] = (uint8_t)sbyte;
+                } else {
+                    st_scale[cl * CP + rb] = bs.s;
+                }
+                continue;
+            }
             *reinterpret_cast<uint2 *>(a.codes + c * (a.R >> 1) + (r0 >> 1)) = make_uint2(lo, hi);
             if constexpr (S == SC_E8M0) {
                 if ((b & 1) == 0) static_cast<uint8_t *>(a.scales)[c * (a.R >> 5) + (r0 >> 5)] = (uint8_t)sbyte;
@@ -567,6 +606,41 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
             } else {
                 static_cast<float *>(a.scales)[c * (a.R >> 4) + (r0 >> 4)] = bs.s;
             }
+        }
+    }
+    if (staged) {
+        __syncthreads();
+        const int64_t cv0 = (int64_t)tx * CTC;  // first view row of the tile
+        const int64_t rs0 = (int64_t)ty * CTR;  // first source row
+        // codes: 64 view rows x 256 bytes, 16 lanes of 16 bytes per view row
+#pragma unroll
+        for (int q = 0; q < CTC * 16 / CT; ++q) {
+            const int idx = q * CT + tid, cl = idx >> 4, part = idx & 15;
+            const uint2 u = st_codes[cl * CP + 2 * part], w = st_codes[cl * CP + 2 * part + 1];
+            *reinterpret_cast<uint4 *>(a.codes + (cv0 + cl) * (a.R >> 1) + (rs0 >> 1) + 16 * part) =
+                make_uint4(u.x, u.y, w.x, w.y);
+        }
+        if constexpr (S == SC_FP32) {
+            // 64 view rows x 32 scales (128 bytes), 8 lanes of 16 bytes per view row
+#pragma unroll
+            for (int q = 0; q < CTC * 8 / CT; ++q) {
+                const int idx = q * CT + tid, cl = idx >> 3, part = idx & 7;
+                const float *p = st_scale + cl * CP + 4 * part;
+                *reinterpret_cast<float4 *>(static_cast<float *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) +
+                                            4 * part) = make_float4(p[0], p[1], p[2], p[3]);
+            }
+        } else if constexpr (S == SC_E4M3) {
+            // 64 view rows x 32 bytes, 2 lanes per view row
+            if (tid < CTC * 2) {
+                const int cl = tid >> 1, part = tid & 1;
+                *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) +
+                                           16 * part) = *reinterpret_cast<const uint4 *>(st_sbyte + cl * NB + 16 * part);
+            }
+        } else {
+            // E8M0: 64 view rows x 16 bytes, one lane per view row
+            if (tid < CTC)
+                *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.scales) + (cv0 + tid) * (a.R >> 5) + (rs0 >> 5)) =
+                    *reinterpret_cast<const uint4 *>(st_sbyte + tid * NB);
         }
     }
     if constexpr (MODE == MODE_AMAX) {
@@ -578,7 +652,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         if (tid == 0) {
             float w = red[0];
             for (int i = 1; i < CT / 64; ++i) w = fmaxf(w, red[i]);
-            a.partials[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = w;
+            a.partials[(int64_t)ty * gridDim.x + tx] = w;
         }
     }
 }

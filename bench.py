@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--no-gemm", action="store_true", help="skip the qgemm leg")
     p.add_argument("--no-configs", action="store_true", help="skip the per-workload kernel timings")
+    p.add_argument("--no-linear", action="store_true", help="skip the 4-bit linear-layer GEMMs")
     p.add_argument("--cpu-rows", type=int, default=ROWS)
     p.add_argument("--cpu-reps", type=int, default=2)
     return p.parse_args()
@@ -170,6 +171,8 @@ def main():
         out["qgemm"] = bench_gemm(U, S, torch, dev, stream)
     if not args.no_configs:
         out["configs"] = bench_configs(U, S, torch, dev, stream)
+    if not args.no_linear:
+        out["linear"] = bench_linear(U, S, torch, dev, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x_bits, args.cpu_rows, args.cpu_reps)
     print(json.dumps(out), flush=True)
@@ -225,6 +228,48 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
                                   "note": "dequantize both operands to bf16 (workspace) + bf16 MFMA GEMM"},
             "bf16_reference": {"ms": round(ms_bf16, 4), "tflops": round(flop / (ms_bf16 * 1e-3) / 1e12, 1),
                                "peak_tflops": 2500.0}}
+
+
+def bench_linear(U, S, torch, dev, stream, reps=3):
+    """The llama-shaped linear layer's three GEMMs (X 16384x4096, W
+    14336x4096, dY 16384x14336) on 4-bit operands, for the UFP4 recipe (E1M2,
+    RHT on all, SR on dY) and the E2M1 baseline (RHT on bwd_dw only): time of
+    quantizing both operands, of the dequantize-to-bf16 GEMM, and the
+    attenuation eta and output SQNR against the unquantized bf16 product."""
+    import block_scaled_bit_ufp4_amd.linear as lin
+
+    def dev_bf16(h):
+        return torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def transposed(a):  # the column kernel without rotation: an exact transpose
+        return U.ufp4_rht(a, axis="col", rht="none", out_dtype=torch.bfloat16)
+
+    T, K, N = 16384, 4096, 14336
+    x, w, dy = dev_bf16(S.llama_x(T, K)), dev_bf16(S.llama_w(N, K)), dev_bf16(S.llama_dy(T, N))
+    z = {"fwd_y": U.ufp4_gemm_bf16(x, w), "bwd_dx": U.ufp4_gemm_bf16(dy, transposed(w)),
+         "bwd_dw": U.ufp4_gemm_bf16(transposed(dy), transposed(x))}
+    ms_ref = _time(lambda: U.ufp4_gemm_bf16(x, w, c=z["fwd_y"]), torch, stream, reps)
+    out = {"workload": "linear layer X 16384x4096, W 14336x4096, dY 16384x14336; three GEMMs of 1.924 TFLOP each",
+           "bf16_reference_gemm_ms": round(ms_ref, 4)}
+    for name, r in (("ufp4", lin.UFP4), ("e2m1_baseline", lin.E2M1_BASELINE)):
+        makers = {"fwd_y": lambda: lin.operands_fwd(x, w, r), "bwd_dx": lambda: lin.operands_dx(dy, w, r),
+                  "bwd_dw": lambda: lin.operands_dw(dy, x, r)}
+        res = {}
+        for g, mk in makers.items():
+            qa, qb = mk()
+            M, Nn = z[g].shape
+            Kk = qa.cfg.view_shape(qa.rows, qa.cols)[1]
+            c = torch.empty_like(z[g])
+            ws = torch.empty(U.ufp4_workspace_size(U.OP_QGEMM, M + Nn, Kk, qa.cfg), dtype=torch.uint8, device=dev)
+            ms = _time(lambda: U.ufp4_qgemm(qa, qb, "bf16", c=c, ws=ws), torch, stream, reps)
+            ms_q = _time(mk, torch, stream, reps)
+            sm = U.ufp4_eta(c, z[g]).cpu().numpy()
+            res[g] = {"quantize_operands_ms": round(ms_q, 4), "gemm_ms": round(ms, 4),
+                      "tflops": round(2.0 * M * Nn * Kk / (ms * 1e-3) / 1e12, 1),
+                      "eta": round(float(sm[0] / sm[1]), 6),
+                      "sqnr_db": round(float(10 * np.log10(sm[1] / sm[2])), 3)}
+        out[name] = res
+    return out
 
 
 def _ktime(U, torch, stream, fn, reps=10):

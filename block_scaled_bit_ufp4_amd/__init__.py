@@ -254,10 +254,11 @@ def ufp4_stats_finalize(sums) -> dict:
 
 def ufp4_qgemm(a: QTensor, b: QTensor, mode: str = "mxfp4", c: Optional[torch.Tensor] = None,
                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    M, N = a.rows, b.rows
+    M, K = a.cfg.view_shape(a.rows, a.cols)
+    N = b.cfg.view_shape(b.rows, b.cols)[0]
     if c is None:
         c = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
-    need = ufp4_workspace_size(OP_QGEMM, M + N, a.cols, a.cfg) if mode == "bf16" else 0
+    need = ufp4_workspace_size(OP_QGEMM, M + N, K, a.cfg) if mode == "bf16" else 0
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=a.codes.device)
     ac, bc = a.c(), b.c()

@@ -337,9 +337,12 @@ int ufp4_qgemm(const ufp4_qtensor *a, const ufp4_qtensor *b, int mode, float *c,
     rc = check_qtensor(b);
     if (rc) return rc;
     if (!c) return UFP4_ERR_INVALID_ARG;
-    if (a->cfg.axis != UFP4_ROW || b->cfg.axis != UFP4_ROW) return UFP4_ERR_UNSUPPORTED;
-    const int64_t M = a->rows, N = b->rows, K = a->cols;
-    if (b->cols != K) return UFP4_ERR_SHAPE;
+    // the GEMM runs on the views: a row quantization's view is the matrix, a
+    // column quantization's its transpose (both stored K-major)
+    const int64_t M = a->cfg.axis == UFP4_ROW ? a->rows : a->cols;
+    const int64_t N = b->cfg.axis == UFP4_ROW ? b->rows : b->cols;
+    const int64_t K = a->cfg.axis == UFP4_ROW ? a->cols : a->rows;
+    if ((b->cfg.axis == UFP4_ROW ? b->cols : b->rows) != K) return UFP4_ERR_SHAPE;
     if (a->cfg.rht != b->cfg.rht || (a->cfg.rht == UFP4_RHT_RANDOM && a->cfg.rht_seed != b->cfg.rht_seed))
         return UFP4_ERR_UNSUPPORTED;
     if (M % 256 || N % 256 || K % 128) return UFP4_ERR_SHAPE;

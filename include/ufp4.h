@@ -197,9 +197,12 @@ int ufp4_stats(const void *x, int x_dtype, int64_t ldx, const ufp4_qtensor *q, d
 /* Host-only: derive the report from sums copied to the host. */
 void ufp4_stats_finalize(const double *sums_host, ufp4_stats_report *report);
 
-/* Block-scaled GEMM Z = deq(A) deq(B)^T, fp32 output c[M][ldc].
- * a: M x K and b: N x K, both quantized along K (UFP4_ROW of the K-major
- * matrices), same rht kind and seed (a shared sign diagonal keeps A B^T).
+/* Block-scaled GEMM Z = deq(A) deq(B)^T, fp32 output c[M][ldc], on the
+ * operands' views: A is a's view (M x K) and B is b's view (N x K), so both
+ * are quantized along K -- a row quantization of an M x K matrix, or a
+ * column quantization of a K x M one (the transposed operands of the
+ * backward GEMMs [UFP4-ZC] recipe table).  Same rht kind and seed (a shared
+ * sign diagonal keeps A B^T).
  * mode UFP4_GEMM_NATIVE_MXFP4: E2M1/E8M0/32 operands on CDNA4's scaled MFMA
  *   ([UQ]; [MXFP4]); products exact, fp32 accumulation.
  * mode UFP4_GEMM_DEQUANT_BF16: any non-IF4 operands; x_hat rounded to bf16

@@ -20,7 +20,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-FORMATS = {"e2m1": 0, "e1m2": 1, "int4": 2, "if4": 3}
+FORMATS = {"e2m1": 0, "e1m2": 1, "int4": 2, "if4": 3, "e2m1_max4": 4, "e2m1_max3": 5, "e2m1_max2": 6}
 SCALES = {"fp32": 0, "e4m3": 1, "e8m0": 2}
 RHTS = {"none": 0, "random": 1, "det": 2}
 ROUNDINGS = {"rtne": 0, "sr": 1}

@@ -38,7 +38,7 @@
 /* Configuration: the same field meanings as the library's ufp4_config, but   */
 /* an independent declaration (the oracle includes no header of the library). */
 /* ------------------------------------------------------------------------ */
-enum { ORC_E2M1 = 0, ORC_E1M2 = 1, ORC_INT4 = 2, ORC_IF4 = 3 };
+enum { ORC_E2M1 = 0, ORC_E1M2 = 1, ORC_INT4 = 2, ORC_IF4 = 3, ORC_E2M1_MAX4 = 4, ORC_E2M1_MAX3 = 5, ORC_E2M1_MAX2 = 6 };
 enum { ORC_SCALE_FP32 = 0, ORC_SCALE_E4M3 = 1, ORC_SCALE_E8M0 = 2 };
 enum { ORC_RHT_NONE = 0, ORC_RHT_RANDOM = 1, ORC_RHT_DET = 2 };
 enum { ORC_RTNE = 0, ORC_SR = 1 };
@@ -72,8 +72,21 @@ static const double GRID[3][8] = {
     {0.0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0},
 };
 
-double orc_grid_value(int fmt, int k) { return GRID[fmt == ORC_IF4 ? ORC_E2M1 : fmt][k & 7]; }
-float orc_gridmax(int fmt) { return (float)GRID[fmt == ORC_IF4 ? ORC_E2M1 : fmt][7]; }
+/* Restricted-range E2M1 ([UFP4-ZC] "UFP4：换一把尺子": the attempt to emulate a
+ * uniform grid on E2M1 by capping its range): the E2M1 points up to 4, 3 or
+ * 2, i.e. magnitude codes k <= 6, 5 or 4; the cap is the format's maximum.
+ * IF4's FP4 candidate uses the full E2M1 grid. */
+static const double *grid_of(int fmt)
+{
+    return GRID[(fmt == ORC_IF4 || fmt >= ORC_E2M1_MAX4) ? ORC_E2M1 : fmt];
+}
+static int kmax_of(int fmt)
+{
+    return fmt == ORC_E2M1_MAX4 ? 6 : fmt == ORC_E2M1_MAX3 ? 5 : fmt == ORC_E2M1_MAX2 ? 4 : 7;
+}
+
+double orc_grid_value(int fmt, int k) { return grid_of(fmt)[k & 7]; }
+float orc_gridmax(int fmt) { return (float)grid_of(fmt)[kmax_of(fmt)]; }
 
 static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
@@ -106,15 +119,16 @@ uint16_t orc_f32_to_bf16(float f)
  * (saturation).  The sign bit of z becomes bit 3 of the code. */
 int orc_round_rtne(float z, int fmt)
 {
-    const double *g = GRID[fmt == ORC_IF4 ? ORC_E2M1 : fmt];
+    const double *g = grid_of(fmt);
+    const int km = kmax_of(fmt);
     double a = fabs((double)z);
     /* at or above the largest point that point is nearest (saturation); the
      * explicit test keeps binary64 distances from losing their order for
      * huge |z| */
-    if (a >= g[7]) return (signbit(z) ? 8 : 0) | 7;
+    if (a >= g[km]) return (signbit(z) ? 8 : 0) | km;
     int best = 0;
     double bestd = fabs(g[0] - a);
-    for (int k = 1; k < 8; ++k) {
+    for (int k = 1; k <= km; ++k) {
         double d = fabs(g[k] - a);
         if (d < bestd || (d == bestd && (k % 2) == 0 && (best % 2) != 0)) {
             best = k;
@@ -131,14 +145,15 @@ int orc_round_rtne(float z, int fmt)
  * exactly.  |z| at or above the grid maximum gives the maximum. */
 int orc_round_sr(float z, int fmt, uint32_t w)
 {
-    const double *g = GRID[fmt == ORC_IF4 ? ORC_E2M1 : fmt];
+    const double *g = grid_of(fmt);
+    const int km = kmax_of(fmt);
     double a = fabs((double)z);
     int k;
-    if (a >= g[7]) {
-        k = 7;
+    if (a >= g[km]) {
+        k = km;
     } else {
         int lo = 0;
-        for (int j = 1; j < 8; ++j)
+        for (int j = 1; j <= km; ++j)
             if (g[j] <= a) lo = j;
         double frac = (a - g[lo]) / (g[lo + 1] - g[lo]);
         double u = (double)(w >> 8) * 0x1p-24;
@@ -481,8 +496,9 @@ static void quantize_block(const orc_config *cfg, const float *y, int B, float a
 static int config_ok(const orc_config *c)
 {
     if (c->block != 16 && c->block != 32) return 0;
-    if (c->format < 0 || c->format > 3) return 0;
+    if (c->format < 0 || c->format > 6) return 0;
     if (c->format == ORC_IF4 && (c->scale != ORC_SCALE_E4M3 || c->block != 16 || c->rounding != ORC_RTNE)) return 0;
+    if (c->format >= ORC_E2M1_MAX4 && (c->scale == ORC_SCALE_E8M0 || c->rounding != ORC_RTNE)) return 0;
     if (c->scale == ORC_SCALE_E8M0 && (c->format != ORC_E2M1 || c->block != 32)) return 0;
     if (c->scale != ORC_SCALE_E8M0 && c->block != 16) return 0;
     return 1;
@@ -597,7 +613,7 @@ int orc_stats(const void *x, int dtype, int64_t R, int64_t C, int64_t ld, const 
         for (int64_t b = 0; b < L / B; ++b) {
             quantize_block(cfg, y + b * B, B, alpha, (uint64_t)(v * L + b * B), &blk);
             int t = blk.int4;
-            const double *g = GRID[t ? ORC_INT4 : (cfg->format == ORC_IF4 ? ORC_E2M1 : cfg->format)];
+            const double *g = t ? GRID[ORC_INT4] : grid_of(cfg->format);
             sums[7] += 1.0;
             sums[8] += t;
             for (int i = 0; i < B; ++i) {

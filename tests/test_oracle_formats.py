@@ -110,6 +110,56 @@ def test_uniform_grid_has_no_cell_bias():
         assert abs(cell_average_error("e1m2", k) - GOLD["cell_bias"]["e1m2_interior"]) < 1e-6
 
 
+# ---- restricted-range E2M1 ----------------------------------------------------
+# The UFP4 page (section "UFP4：换一把尺子") tries emulating a uniform grid on
+# E2M1 by capping its range (at 2.0 the points {0, .5, 1, 1.5, 2} are uniform)
+# and finds every capped variant worse than the E2M1 baseline.
+
+RESTRICTED = {"e2m1_max4": (4.0, 6), "e2m1_max3": (3.0, 5), "e2m1_max2": (2.0, 4)}
+
+
+@pytest.mark.parametrize("fmt", sorted(RESTRICTED))
+def test_restricted_e2m1_is_nearest_capped_point(fmt):
+    """Brute force: the nearest of the E2M1 points up to the cap (ties to the
+    even code), the cap for everything above it; sign in bit 3."""
+    cap, kmax = RESTRICTED[fmt]
+    assert O.gridmax(fmt) == cap
+    np.testing.assert_array_equal(O.grid(fmt), O.grid("e2m1"))
+    pts = O.grid("e2m1")[:kmax + 1]
+    mids = (pts[1:] + pts[:-1]) / 2
+    z = np.concatenate([f32_range(0.0, 9.0, 61), near(list(mids) + [cap, 6.0]), np.float32([1e30])])
+    codes = O.round_rtne_array(z, fmt)
+    a = z.astype(np.float64)
+    d = np.abs(a[:, None] - pts[None, :])
+    best = np.argmin(d, axis=1)
+    tie = (d == d.min(axis=1, keepdims=True)).sum(axis=1) > 1
+    best[tie] = [k if k % 2 == 0 else k + 1 for k in best[tie]]  # ties: the even code
+    best[a >= cap] = kmax
+    np.testing.assert_array_equal(codes & 7, best)
+    np.testing.assert_array_equal(O.round_rtne_array(-z, fmt), codes | 8)
+
+
+def test_capped_at_two_is_the_uniform_grid():
+    """Capped at 2 the E2M1 codes 0..4 are the points k/2, the E1M2 codes 0..4:
+    below the cap both round identically; above it E2M1 saturates."""
+    z = np.concatenate([f32_range(0.0, 2.0, 211), near([0.25, 0.75, 1.25, 1.75])])
+    np.testing.assert_array_equal(O.round_rtne_array(z, "e2m1_max2"), O.round_rtne_array(z, "e1m2"))
+    assert set(O.round_rtne_array(np.float32([2.3, 3.0, 7.0]), "e2m1_max2")) == {4}
+
+
+def test_restricted_e2m1_loses_to_the_full_grid():
+    """On Gaussian blocks (what the RHT makes of a tensor) each cap costs SQNR
+    against full E2M1, the more the lower the cap, while the uniform E1M2 grid
+    beats both; the capped grids also shrink more than E1M2."""
+    x = S.normal(512, 1024, 1.0, 2, "uniform")
+    for scale in ("fp32", "e4m3"):
+        sq = {f: O.finalize(O.stats(x, O.Cfg(f, scale)))
+              for f in ("e2m1", "e2m1_max4", "e2m1_max3", "e2m1_max2", "e1m2")}
+        db = {f: r["sqnr_db"] for f, r in sq.items()}
+        assert db["e1m2"] > db["e2m1"] > db["e2m1_max4"] > db["e2m1_max3"] > db["e2m1_max2"]
+        assert sq["e2m1_max2"]["mean_shrink"] < sq["e1m2"]["mean_shrink"] < 0
+
+
 # ---- E4M3 / E8M0 scales ----------------------------------------------------
 
 def test_e4m3_decode_matches_torch_for_every_finite_byte():

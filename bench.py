@@ -370,7 +370,33 @@ def bench_configs(U, S, torch, dev, stream):
     leg["dequant_bf16_us"] = round(ms * 1e3, 2)
     c5["e1m2_rht"] = leg
     out["gemm_operands_8192x8192"] = c5
+    out["formats"] = bench_formats(U, S, torch, dev)
     return out
+
+
+def bench_formats(U, S, torch, dev):
+    """Quantization quality per format on the activation (8192x8192 t3*0.02)
+    and MXFP4 (16384x8192 N(0,1) + uniform blocks) tensors, NVFP4-style
+    two-level scale, with and without RHT: SQNR, signal factor alpha and mean
+    shrinkage, from the statistics kernel.  The capped E2M1 grids are the
+    pages' attempt to emulate a uniform grid on E2M1; int4 is NVINT4."""
+    def dev_bf16(h):
+        return torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    res = {}
+    for name, xh in (("activations_8192x8192", S.activations_t3(ROWS, COLS, seed=0)),
+                     ("mxfp4_data_16384x8192", S.mx_if4(16384, 8192, seed=0)[0])):
+        x = dev_bf16(xh)
+        d = {}
+        for rht in ("none", "random"):
+            for fmt in ("e2m1", "e2m1_max4", "e2m1_max3", "e2m1_max2", "e1m2", "int4"):
+                cfg = U.Cfg(fmt, "e4m3", rht=rht, rht_seed=0)
+                r = U.ufp4_stats_finalize(U.ufp4_stats(x, U.ufp4_quantize(x, cfg)))
+                d[f"{fmt}_{rht}"] = {"sqnr_db": round(r["sqnr_db"], 3), "alpha": round(r["alpha"], 6),
+                                     "mean_shrink": float(f"{r['mean_shrink']:.4e}")}
+        res[name] = d
+        del x
+    return res
 
 
 if __name__ == "__main__":

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libufp4.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libufp4.so not built at {LIB_PATH}; run block_scaled_bit_ufp4_amd/build.py")
 
-FORMATS = {"e2m1": 0, "e1m2": 1, "int4": 2, "if4": 3}
+FORMATS = {"e2m1": 0, "e1m2": 1, "int4": 2, "if4": 3, "e2m1_max4": 4, "e2m1_max3": 5, "e2m1_max2": 6}
 SCALES = {"fp32": 0, "e4m3": 1, "e8m0": 2}
 RHTS = {"none": 0, "random": 1, "det": 2}
 ROUNDINGS = {"rtne": 0, "sr": 1}

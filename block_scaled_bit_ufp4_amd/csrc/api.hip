@@ -60,7 +60,7 @@ static uint32_t sign_mask(int rht, uint64_t seed)
 static int check_config(const ufp4_config *c)
 {
     if (!c) return UFP4_ERR_INVALID_ARG;
-    if (c->format < UFP4_E2M1 || c->format > UFP4_IF4) return UFP4_ERR_INVALID_ARG;
+    if (c->format < UFP4_E2M1 || c->format > UFP4_E2M1_MAX2) return UFP4_ERR_INVALID_ARG;
     if (c->scale < UFP4_SCALE_FP32 || c->scale > UFP4_SCALE_E8M0) return UFP4_ERR_INVALID_ARG;
     if (c->rht < UFP4_RHT_NONE || c->rht > UFP4_RHT_DETERMINISTIC) return UFP4_ERR_INVALID_ARG;
     if (c->rounding != UFP4_RTNE && c->rounding != UFP4_SR) return UFP4_ERR_INVALID_ARG;
@@ -74,6 +74,7 @@ static int check_config(const ufp4_config *c)
     }
     if (c->format == UFP4_IF4 && (c->scale != UFP4_SCALE_E4M3 || c->rounding != UFP4_RTNE))
         return UFP4_ERR_UNSUPPORTED;
+    if (c->format >= UFP4_E2M1_MAX4 && c->rounding != UFP4_RTNE) return UFP4_ERR_UNSUPPORTED;
     return UFP4_OK;
 }
 

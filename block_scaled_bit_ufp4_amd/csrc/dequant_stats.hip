@@ -123,6 +123,9 @@ hipError_t launch_dequant(int format, int scale, int inverse_rht, int out_dtype,
     UFP4_DQ(FMT_E2M1)
     UFP4_DQ(FMT_E1M2)
     UFP4_DQ(FMT_INT4)
+    UFP4_DQ(FMT_E2M1_M4)
+    UFP4_DQ(FMT_E2M1_M3)
+    UFP4_DQ(FMT_E2M1_M2)
 #undef UFP4_DQ
     return hipErrorInvalidValue;
 }
@@ -315,6 +318,9 @@ hipError_t launch_stats(int format, int scale, int in_dtype, int rht, const Stat
     UFP4_ST(FMT_E2M1)
     UFP4_ST(FMT_E1M2)
     UFP4_ST(FMT_INT4)
+    UFP4_ST(FMT_E2M1_M4)
+    UFP4_ST(FMT_E2M1_M3)
+    UFP4_ST(FMT_E2M1_M2)
 #undef UFP4_ST
     return hipErrorInvalidValue;
 }

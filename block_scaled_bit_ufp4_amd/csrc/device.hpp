@@ -15,7 +15,7 @@
 
 namespace ufp4 {
 
-enum : int { FMT_E2M1 = 0, FMT_E1M2 = 1, FMT_INT4 = 2, FMT_IF4 = 3 };
+enum : int { FMT_E2M1 = 0, FMT_E1M2 = 1, FMT_INT4 = 2, FMT_IF4 = 3, FMT_E2M1_M4 = 4, FMT_E2M1_M3 = 5, FMT_E2M1_M2 = 6 };
 enum : int { SC_FP32 = 0, SC_E4M3 = 1, SC_E8M0 = 2 };
 enum : int { IN_BF16 = 0, IN_F32 = 1 };
 
@@ -23,8 +23,15 @@ typedef short v2i16 __attribute__((ext_vector_type(2)));
 
 __host__ __device__ constexpr float grid_max(int f)
 {
-    return f == FMT_E1M2 ? 3.5f : (f == FMT_INT4 ? 7.0f : 6.0f);
+    return f == FMT_E1M2      ? 3.5f
+           : f == FMT_INT4    ? 7.0f
+           : f == FMT_E2M1_M4 ? 4.0f
+           : f == FMT_E2M1_M3 ? 3.0f
+           : f == FMT_E2M1_M2 ? 2.0f
+                              : 6.0f;
 }
+// E2M1 codes: the full grid and the range-capped variants (points up to the cap)
+__host__ __device__ constexpr bool e2m1_codes(int f) { return f == FMT_E2M1 || f >= FMT_E2M1_M4; }
 __host__ __device__ constexpr int block_of(int scl) { return scl == SC_E8M0 ? 32 : 16; }
 
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }

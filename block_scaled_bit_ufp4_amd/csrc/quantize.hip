@@ -159,6 +159,11 @@ __device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b,
             packed |= ((f2u(z[i]) >> 28 & 8u) | sr_code<F>(fabsf(z[i]), w[i])) << (4 * i);
     } else if constexpr (F == FMT_E2M1) {
         packed = pack8_e2m1(z);
+    } else if constexpr (e2m1_codes(F)) {
+        // capped range: saturate at the cap (a grid point), then nearest even
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = __builtin_amdgcn_fmed3f(z[i], -grid_max(F), grid_max(F));
+        packed = pack8_e2m1(z);
     } else {
         if constexpr (S == SC_E4M3) {
             // the E4M3 rounding of Delta can leave |z| above the grid maximum
@@ -725,6 +730,11 @@ static hipError_t pick_scale_sr(const LaunchSpec &sp, const RowArgs &ra, const C
             if constexpr (F == FMT_E2M1) return pick_in_rht<F, SC_E8M0, false>(sp, ra, ca, st);
             return hipErrorInvalidValue;
         }
+        if constexpr (F >= FMT_E2M1_M4) {  // capped E2M1: RTNE only
+            if (sp.sr) return hipErrorInvalidValue;
+            return sp.scale == SC_FP32 ? pick_in_rht<F, SC_FP32, false>(sp, ra, ca, st)
+                                       : pick_in_rht<F, SC_E4M3, false>(sp, ra, ca, st);
+        }
         if (sp.scale == SC_FP32)
             return sp.sr ? pick_in_rht<F, SC_FP32, true>(sp, ra, ca, st) : pick_in_rht<F, SC_FP32, false>(sp, ra, ca, st);
         return sp.sr ? pick_in_rht<F, SC_E4M3, true>(sp, ra, ca, st) : pick_in_rht<F, SC_E4M3, false>(sp, ra, ca, st);
@@ -738,6 +748,9 @@ hipError_t launch_quantize(const LaunchSpec &sp, const RowArgs &ra, const ColArg
     case FMT_E1M2: return pick_scale_sr<FMT_E1M2>(sp, ra, ca, st);
     case FMT_INT4: return pick_scale_sr<FMT_INT4>(sp, ra, ca, st);
     case FMT_IF4: return pick_scale_sr<FMT_IF4>(sp, ra, ca, st);
+    case FMT_E2M1_M4: return pick_scale_sr<FMT_E2M1_M4>(sp, ra, ca, st);
+    case FMT_E2M1_M3: return pick_scale_sr<FMT_E2M1_M3>(sp, ra, ca, st);
+    case FMT_E2M1_M2: return pick_scale_sr<FMT_E2M1_M2>(sp, ra, ca, st);
     }
     return hipErrorInvalidValue;
 }

@@ -94,7 +94,12 @@ extern "C" {
 #define UFP4_ERR_HIP (-6)         /* a HIP launch failed; see ufp4_last_hip_error()  */
 
 /* ---- enumerations ------------------------------------------------------ */
-enum { UFP4_E2M1 = 0, UFP4_E1M2 = 1, UFP4_INT4 = 2, UFP4_IF4 = 3 };
+/* Formats.  UFP4_E2M1_MAX4/3/2: E2M1 codes with the range capped at 4, 3 or
+ * 2 (the grid's points up to the cap, saturating there; at 2 the points are
+ * uniform): [UFP4-ZC] "UFP4：换一把尺子", the attempt to emulate a uniform grid
+ * on E2M1.  FP32 or E4M3 block scales (gridmax = the cap), RTNE only. */
+enum { UFP4_E2M1 = 0, UFP4_E1M2 = 1, UFP4_INT4 = 2, UFP4_IF4 = 3, UFP4_E2M1_MAX4 = 4, UFP4_E2M1_MAX3 = 5,
+       UFP4_E2M1_MAX2 = 6 };
 enum { UFP4_SCALE_FP32 = 0, UFP4_SCALE_E4M3 = 1, UFP4_SCALE_E8M0 = 2 };
 enum { UFP4_RHT_NONE = 0, UFP4_RHT_RANDOM = 1, UFP4_RHT_DETERMINISTIC = 2 };
 enum { UFP4_RTNE = 0, UFP4_SR = 1 };
@@ -108,7 +113,7 @@ enum { UFP4_OP_STATS = 0, UFP4_OP_QGEMM = 1, UFP4_OP_ETA = 2, UFP4_OP_AMAX = 3 }
  *   IF4 with E4M3/16 only.  SR with E2M1, E1M2, INT4 under FP32 or E4M3 scales.
  *   The RHT is 16 wide; a 32-element block holds two transformed chunks. */
 typedef struct ufp4_config {
-    int32_t format;     /* UFP4_E2M1 / UFP4_E1M2 / UFP4_INT4 / UFP4_IF4          */
+    int32_t format;     /* UFP4_E2M1 / E1M2 / INT4 / IF4 / E2M1_MAX4 / MAX3 / MAX2 */
     int32_t scale;      /* UFP4_SCALE_*                                        */
     int32_t block;      /* 16 (FP32, E4M3) or 32 (E8M0)                        */
     int32_t rht;        /* UFP4_RHT_*                                          */

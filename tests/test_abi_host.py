@@ -59,6 +59,8 @@ def quant(cfg, rows, cols, ld, x=FAKE, codes=FAKE, scales=FAKE, ts=FAKE, amax=FA
     (U.Cfg("e2m1", "e8m0", 32, rounding="sr"), 16, 32, 32, -4),
     (U.Cfg("e2m1", "fp32", 32), 16, 32, 32, -4),           # FP32 scale uses 16-blocks
     (U.Cfg("e2m1", block=8), 16, 32, 32, -1),
+    (U.Cfg("e2m1_max2", rounding="sr"), 16, 32, 32, -4),   # capped E2M1: RTNE only
+    (U.Cfg("e2m1_max4", "e8m0", 32), 16, 32, 32, -4),      # capped E2M1: no E8M0
 ])
 def test_quantize_validation(cfg, rows, cols, ld, code):
     assert quant(cfg, rows, cols, ld) == code

@@ -25,6 +25,10 @@ def all_configs():
     for rht, axis in itertools.product(["none", "random", "det"], ["row", "col"]):
         out.append(dict(format="e2m1", scale="e8m0", block=32, rht=rht, rounding="rtne", axis=axis))
         out.append(dict(format="if4", scale="e4m3", block=16, rht=rht, rounding="rtne", axis=axis))
+    # range-capped E2M1
+    for fmt, scale, rht, axis in itertools.product(["e2m1_max4", "e2m1_max3", "e2m1_max2"], ["fp32", "e4m3"],
+                                                   ["none", "random"], ["row", "col"]):
+        out.append(dict(format=fmt, scale=scale, block=16, rht=rht, rounding="rtne", axis=axis))
     return out
 
 

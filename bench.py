@@ -221,13 +221,30 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
     ms_e1m2 = _time(lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws), torch, stream, reps)
     _, ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps, U)
     tf = flop / (ms * 1e-3) / 1e12
+    # IF4 against NVFP4 and MXFP4 on the MXFP4/IF4 workload's data: A, B are
+    # its two 8192-row halves (N(0,1) with uniform 1x32 blocks)
+    xh, _ = S.mx_if4(2 * M, K, seed=0)
+    xa = torch.from_numpy(xh[:M].view(np.int16)).view(torch.bfloat16).to(dev)
+    xb = torch.from_numpy(xh[M:].view(np.int16)).view(torch.bfloat16).to(dev)
+    zref = U.ufp4_gemm_bf16(xa, xb)
+    c4 = {}
+    for name, cfgf, mode in (("if4", U.Cfg("if4", "e4m3"), "bf16"), ("nvfp4", U.Cfg("e2m1", "e4m3"), "bf16"),
+                             ("mxfp4_h16", U.Cfg("e2m1", "e8m0", 32, rht="det"), "mxfp4")):
+        qa_, qb_ = U.ufp4_quantize(xa, cfgf), U.ufp4_quantize(xb, cfgf)
+        ws_ = torch.empty(U.ufp4_workspace_size(U.OP_QGEMM, M + N, K, cfgf), dtype=torch.uint8, device=dev) \
+            if mode == "bf16" else None
+        ms_ = _time(lambda: U.ufp4_qgemm(qa_, qb_, mode, c=c, ws=ws_), torch, stream, 3)
+        sm = U.ufp4_eta(c, zref).cpu().numpy()
+        c4[name] = {"ms": round(ms_, 4), "eta": round(float(sm[0] / sm[1]), 6),
+                    "sqnr_db": round(float(10 * np.log10(sm[1] / sm[2])), 3)}
     return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out", "ms": round(ms, 4),
             "ms_per_call_back_to_back": round(ms_call, 4),
             "tflops": round(tf, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tf / FP4_PEAK_TFLOPS, 4),
             "e1m2_dequant_bf16": {"ms": round(ms_e1m2, 4), "tflops": round(flop / (ms_e1m2 * 1e-3) / 1e12, 1),
                                   "note": "dequantize both operands to bf16 (workspace) + bf16 MFMA GEMM"},
             "bf16_reference": {"ms": round(ms_bf16, 4), "tflops": round(flop / (ms_bf16 * 1e-3) / 1e12, 1),
-                               "peak_tflops": 2500.0}}
+                               "peak_tflops": 2500.0},
+            "mxfp4_if4_data_8192^3": c4}
 
 
 def bench_linear(U, S, torch, dev, stream, reps=3):

@@ -360,7 +360,6 @@ int ufp4_qgemm(const ufp4_qtensor *a, const ufp4_qtensor *b, int mode, float *c,
                                           static_cast<const uint8_t *>(b->scales), M, N, K, c, ldc, st));
     }
     if (mode != UFP4_GEMM_DEQUANT_BF16) return UFP4_ERR_INVALID_ARG;
-    if (a->cfg.format == UFP4_IF4 || b->cfg.format == UFP4_IF4) return UFP4_ERR_UNSUPPORTED;
     const size_t need = (size_t)((M + N) * K * 2);
     if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
     if (!aligned16(ws)) return UFP4_ERR_ALIGN;

@@ -210,8 +210,11 @@ void ufp4_stats_finalize(const double *sums_host, ufp4_stats_report *report);
  * sign diagonal keeps A B^T).
  * mode UFP4_GEMM_NATIVE_MXFP4: E2M1/E8M0/32 operands on CDNA4's scaled MFMA
  *   ([UQ]; [MXFP4]); products exact, fp32 accumulation.
- * mode UFP4_GEMM_DEQUANT_BF16: any non-IF4 operands; x_hat rounded to bf16
- *   (nearest even), bf16 MFMA, fp32 accumulation ([UQ]: software E1M2/INT4).
+ * mode UFP4_GEMM_DEQUANT_BF16: any operands; x_hat rounded to bf16 (nearest
+ *   even), bf16 MFMA, fp32 accumulation ([UQ]: software E1M2/INT4).  IF4's
+ *   INT4 blocks dequantize with the 6/7 factor, so a product of two INT4
+ *   blocks carries 36/49 and a mixed one 6/7 ([IF4] 4.1, the MAC unit's
+ *   scaling by operand types).
  * Sizes: M, N multiples of 256; K multiple of 128; ldc multiple of 4, >= N.
  * ws: ufp4_workspace_size(UFP4_OP_QGEMM, ...) bytes (0 for NATIVE_MXFP4). */
 int ufp4_qgemm(const ufp4_qtensor *a, const ufp4_qtensor *b, int mode, float *c, int64_t ldc, void *ws,

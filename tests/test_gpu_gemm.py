@@ -45,13 +45,18 @@ def test_mxfp4_gemm_matches_oracle(M, N, K, rht):
     assert rel_fro(z, want) < 1e-5  # exact products, binary32 sums
 
 
-@pytest.mark.parametrize("fmt", ["e1m2", "int4", "e2m1"])
+@pytest.mark.parametrize("fmt", ["e1m2", "int4", "e2m1", "if4", "e2m1_max2"])
 def test_dequant_bf16_gemm_matches_oracle(fmt):
     U = lib()
     M, N, K = 256, 512, 256
-    a = S.normal(M, K, 1.0, 1, "gemm_a")
-    b = S.normal(N, K, 1.0, 1, "gemm_b")
-    cfg = U.Cfg(fmt, "fp32", rht="random", rht_seed=3)
+    if fmt == "if4":  # Gaussian rows with uniform blocks, so both block types occur
+        a, _ = S.mx_if4(M, K, seed=1, frac=0.3)
+        b, _ = S.mx_if4(N, K, seed=2, frac=0.3)
+        cfg = U.Cfg(fmt, "e4m3")
+    else:
+        a = S.normal(M, K, 1.0, 1, "gemm_a")
+        b = S.normal(N, K, 1.0, 1, "gemm_b")
+        cfg = U.Cfg(fmt, "fp32", rht="random", rht_seed=3)
     qa = U.ufp4_quantize(to_device_bf16(a), cfg)
     qb = U.ufp4_quantize(to_device_bf16(b), cfg)
     z = host(U.ufp4_qgemm(qa, qb, "bf16"))
@@ -80,3 +85,25 @@ def test_eta_sums():
     z64, q64 = z.astype(np.float64), zq.astype(np.float64)
     want = [np.sum(q64 * z64), np.sum(z64 * z64), np.sum((q64 - z64) ** 2)]
     np.testing.assert_allclose(sums, want, rtol=1e-12)
+
+
+def test_if4_gemm_block_type_factors():
+    """IF4 operands with both block types on both sides (uniform rows pick
+    INT4, Gaussian rows FP4): the GEMM equals the oracle's product of its own
+    dequantized bf16 operands, whose INT4 blocks carry the 6/7 factor, so
+    INT4 x INT4 block products carry 36/49 and mixed ones 6/7 ([IF4] 4.1)."""
+    U = lib()
+    rng = np.random.default_rng(7)
+    K = 128
+    a = np.where(np.arange(256)[:, None] % 2 == 0, rng.uniform(-1, 1, (256, K)), rng.standard_normal((256, K)))
+    b = np.where(np.arange(256)[:, None] % 3 == 0, rng.uniform(-1, 1, (256, K)), rng.standard_normal((256, K)))
+    a_bits, b_bits = S.f32_to_bf16_bits(a.astype(np.float32)), S.f32_to_bf16_bits(b.astype(np.float32))
+    cfg = U.Cfg("if4", "e4m3")
+    qa, qb = U.ufp4_quantize(to_device_bf16(a_bits), cfg), U.ufp4_quantize(to_device_bf16(b_bits), cfg)
+    fa = host(qa.scales) >> 7
+    fb = host(qb.scales) >> 7
+    assert fa.any() and (1 - fa).any() and fb.any() and (1 - fb).any()   # both types on both sides
+    z = host(U.ufp4_qgemm(qa, qb, "bf16")).astype(np.float64)
+    ocfg = oracle_cfg(cfg)
+    da, db = oracle_operand(a_bits, ocfg, bf16=True), oracle_operand(b_bits, ocfg, bf16=True)
+    assert rel_fro(z, O.gemm_nt(da, db)) < 1e-5

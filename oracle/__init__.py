@@ -97,6 +97,16 @@ def lib():
         L.orc_gridmax.restype = C.c_float
         L.orc_grid_value.argtypes = [i32, i32]
         L.orc_grid_value.restype = C.c_double
+        L.orc_fwht_f32.argtypes = [p, i32]
+        L.orc_mx_exponent.argtypes = [C.c_double, i32]
+        L.orc_mx_exponent.restype = i32
+        L.orc_e4m3_encode_d.argtypes = [C.c_double]
+        L.orc_e4m3_encode_d.restype = C.c_uint8
+        L.orc_q_quantize.argtypes = [p, i32, i32, p, p]
+        L.orc_k_quantize_row.argtypes = [p, i32, i32, p, p]
+        L.orc_kv_quantize_seq.argtypes = [p, p, i64, i64, i64, i32, i32, p, p, p, p]
+        L.orc_kv_decode_seq.argtypes = [p, i32, p, p, i64, i64, i32, C.c_float, i32, p, p]
+        L.orc_kv_decode_seq.restype = i32
         _lib = L
     return _lib
 
@@ -313,3 +323,70 @@ def finalize(s: np.ndarray) -> dict:
         "bucket_bias": np.divide(s[32:48], s[16:32], out=np.full(16, np.nan), where=s[16:32] > 0).reshape(2, 8),
     }
     return rep
+
+
+# ---- FP4 KV-cache decode attention (kvcache.c) ----------------------------
+
+def fwht(v) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform (binary32 butterflies)."""
+    a = np.array(v, dtype=np.float32).copy()
+    lib().orc_fwht_f32(_ptr(a), a.size)
+    return a
+
+
+def mx_exponent(amax: float, emax: int) -> int:
+    return int(lib().orc_mx_exponent(float(amax), emax))
+
+
+def e4m3_encode_d(a: float) -> int:
+    return int(lib().orc_e4m3_encode_d(float(a)))
+
+
+def q_quantize(q: np.ndarray, rotate: bool):
+    """MXFP8 of query rows q[..., D] (bf16 bits): (E4M3 bytes [..., D],
+    biased exponents [..., D/32])."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    D = q.shape[-1]
+    rows = q.reshape(-1, D)
+    codes = np.empty(rows.shape, dtype=np.uint8)
+    scales = np.empty((rows.shape[0], D // 32), dtype=np.uint8)
+    for i in range(rows.shape[0]):
+        r = np.ascontiguousarray(rows[i])
+        lib().orc_q_quantize(_ptr(r), D, int(rotate), _ptr(codes[i]), _ptr(scales[i]))
+    return codes.reshape(q.shape), scales.reshape(q.shape[:-1] + (D // 32,))
+
+
+def kv_quantize_seq(k: np.ndarray, v: np.ndarray, length: int, ntok: int, rotate: bool):
+    """The FP4 cache of one sequence, natural layout: k, v bf16 bits [T][D]
+    (T >= length).  Returns kcodes [ntok][D/2], kscales [ntok][D/32],
+    vcodes [D][ntok/2], vscales [D][ntok/32]."""
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    assert k.shape == v.shape and ntok % 32 == 0 and ntok >= length
+    D = k.shape[1]
+    kc = np.empty((ntok, D // 2), dtype=np.uint8)
+    ks = np.empty((ntok, D // 32), dtype=np.uint8)
+    vc = np.empty((D, ntok // 2), dtype=np.uint8)
+    vs = np.empty((D, ntok // 32), dtype=np.uint8)
+    lib().orc_kv_quantize_seq(_ptr(k), _ptr(v), D, int(length), int(ntok), D, int(rotate),
+                              _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs))
+    return kc, ks, vc, vs
+
+
+def kv_decode_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, length: int, sm_scale: float,
+                  rotate: bool) -> np.ndarray:
+    """Decode attention of one sequence: q bf16 bits [G][D], k, v [T][D]
+    (T >= length); binary64 output [G][D]."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    G, D = q.shape
+    ntok = (int(length) + 31) // 32 * 32
+    ws = np.empty(max(8, ntok * (8 + D // 2 + D // 32) + D * (ntok // 2 + ntok // 32)) // 8 + 1, dtype=np.float64)
+    out = np.empty((G, D), dtype=np.float64)
+    rc = lib().orc_kv_decode_seq(_ptr(q), G, _ptr(k), _ptr(v), D, int(length), D, float(sm_scale), int(rotate),
+                                 _ptr(ws), _ptr(out))
+    if rc:
+        raise ValueError("bad decode shape")
+    return out
+

@@ -1,4 +1,4 @@
-"""Build the CPU oracle (oracle.c -> liboracle.so) with gcc.
+"""Build the CPU oracle (oracle.c, kvcache.c -> liboracle.so) with gcc.
 
 Test infrastructure: the library is loaded only by the tests, the smoke check
 and the benchmark's cpu_baseline leg.  Binary32 arithmetic must be plain IEEE:
@@ -8,7 +8,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "oracle.c")
+SRCS = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "kvcache.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
@@ -16,7 +16,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC, "-lm"]
+    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", *SRCS, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

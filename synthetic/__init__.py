@@ -16,7 +16,13 @@ Recipe (all tensors row-major):
   * ``llama_dy``        16384x14336 N(0, 1e-3);
   * ``mx_if4``          16384x8192 N(0,1) with round(0.005 n / 32) aligned
                         1x32 row blocks replaced by U(-1,1);
-  * ``gemm_a``/``gemm_b`` 8192x8192 N(0,1), independent streams.
+  * ``gemm_a``/``gemm_b`` 8192x8192 N(0,1), independent streams;
+  * ``kv_decode``       one decode step of attention: q [B][Hq][D] N(0,1);
+                        k, v [B][Hkv][L][D], one stream per (batch entry,
+                        KV head); k N(0,1) with 4 seeded channels per KV head
+                        scaled by 10 (the channel outliers of keys), v N(0,1);
+  * ``kv_lens``         per-sequence lengths: all L, or ragged, uniform in
+                        [1, L] with the first entry L.
 Every generator takes ``rows``/``cols`` so tests can draw smaller tensors of
 the same distribution.
 """
@@ -30,13 +36,14 @@ CHUNK = 1 << 20
 
 # tensor ids keep the streams of different tensors independent
 TID = {"quantize_x": 1, "activations_t3": 2, "llama_x": 3, "llama_w": 4, "llama_dy": 5,
-       "mx_if4": 6, "gemm_a": 7, "gemm_b": 8, "uniform": 9, "edge": 10}
+       "mx_if4": 6, "gemm_a": 7, "gemm_b": 8, "uniform": 9, "edge": 10, "kv_q": 11, "kv_k": 12,
+       "kv_v": 13, "kv_lens": 14}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16   # no overflow for finite values
     return r.astype(np.uint16)
 
 
@@ -116,6 +123,45 @@ def gemm_a(rows=8192, cols=8192, seed=0):
 
 def gemm_b(rows=8192, cols=8192, seed=0):
     return normal(rows, cols, 1.0, seed, "gemm_b")
+
+
+def kv_seq(b, h, L, D=128, seed=0):
+    """k, v [L][D] of batch entry b, KV head h (bf16 bits)."""
+    rk = np.random.default_rng([seed, TID["kv_k"], b, h])
+    k = rk.standard_normal((L, D))
+    k[:, np.sort(rk.choice(D, 4, replace=False))] *= 10.0
+    rv = np.random.default_rng([seed, TID["kv_v"], b, h])
+    v = rv.standard_normal((L, D))
+    return f32_to_bf16_bits(k.astype(np.float32)), f32_to_bf16_bits(v.astype(np.float32))
+
+
+def kv_q(B, Hq, D=128, seed=0):
+    rng = np.random.default_rng([seed, TID["kv_q"]])
+    return f32_to_bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32))
+
+
+def kv_decode(B=32, Hq=32, Hkv=8, L=16384, D=128, seed=0):
+    """q [B][Hq][D], k, v [B][Hkv][L][D] (bf16 bits)."""
+    from concurrent.futures import ThreadPoolExecutor
+    k = np.empty((B, Hkv, L, D), dtype=np.uint16)
+    v = np.empty((B, Hkv, L, D), dtype=np.uint16)
+
+    def fill(i):
+        b, h = divmod(i, Hkv)
+        k[b, h], v[b, h] = kv_seq(b, h, L, D, seed)
+
+    with ThreadPoolExecutor(min(8, B * Hkv)) as ex:
+        list(ex.map(fill, range(B * Hkv)))
+    return kv_q(B, Hq, D, seed), k, v
+
+
+def kv_lens(B, L, seed=0, ragged=False):
+    if not ragged:
+        return np.full(B, L, dtype=np.int32)
+    rng = np.random.default_rng([seed, TID["kv_lens"]])
+    n = rng.integers(1, L + 1, B).astype(np.int32)
+    n[0] = L
+    return n
 
 
 def edge_cases(rows=64, cols=256, seed=0):

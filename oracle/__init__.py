@@ -107,6 +107,8 @@ def lib():
         L.orc_kv_quantize_seq.argtypes = [p, p, i64, i64, i64, i32, i32, p, p, p, p]
         L.orc_kv_decode_seq.argtypes = [p, i32, p, p, i64, i64, i32, C.c_float, i32, p, p]
         L.orc_kv_decode_seq.restype = i32
+        L.orc_kv_decode_bounds.argtypes = [p, i32, p, p, i64, i64, i32, C.c_float, i32, C.c_double, p, p, p, p]
+        L.orc_kv_decode_bounds.restype = i32
         _lib = L
     return _lib
 
@@ -389,4 +391,24 @@ def kv_decode_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, length: int, sm_s
     if rc:
         raise ValueError("bad decode shape")
     return out
+
+
+def kv_decode_bounds(q: np.ndarray, k: np.ndarray, v: np.ndarray, length: int, sm_scale: float, rotate: bool,
+                     eps_s: float = 2.0 ** -15):
+    """(mass [G][D], ambiguity bound [G][D], number of fragile tokens) for
+    comparing a binary32 decode with kv_decode_seq."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    G, D = q.shape
+    ntok = (int(length) + 31) // 32 * 32
+    ws = np.empty(max(8, ntok * (8 + D // 2 + D // 32) + D * (ntok // 2 + ntok // 32)) // 8 + 1, dtype=np.float64)
+    mass = np.empty((G, D), dtype=np.float64)
+    amb = np.empty((G, D), dtype=np.float64)
+    frag = C.c_int64(0)
+    rc = lib().orc_kv_decode_bounds(_ptr(q), G, _ptr(k), _ptr(v), D, int(length), D, float(sm_scale), int(rotate),
+                                    float(eps_s), _ptr(ws), _ptr(mass), _ptr(amb), C.byref(frag))
+    if rc:
+        raise ValueError("bad decode shape")
+    return mass, amb, int(frag.value)
 

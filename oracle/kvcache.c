@@ -253,3 +253,108 @@ int orc_kv_decode_seq(const uint16_t *q, int G, const uint16_t *k, const uint16_
     }
     return 0;
 }
+
+/* Comparison bound for a decode computed in binary32 (test infrastructure).
+ * An implementation that forms the scores with binary32 accumulation and
+ * 2^x with a few-ulp exponential takes the E4M3 decisions of P from values
+ * within a small relative distance of these binary64 ones, so a probability
+ * (or a block exponent) lying that close to a rounding boundary may go
+ * either way; both results are correct.  For each output element this
+ * writes
+ *   mass[r][d] = sum_t p'_t |V'_t[d]| / sum_t p_t   (the scale of the sum),
+ *   amb[r][d]  = sum over such tokens of |largest possible change of p'_t|
+ *                |V'_t[d]| / sum_t p_t, plus mass[r][d] times the largest
+ *                relative change of the normaliser, sum_t eps_t p_t / sum p,
+ * with the relative perturbation of p_t taken as
+ *   eps_t = c eps_s sum_d |Q'_d K'_td| + 2^-20 (|x_t| + 1)
+ * (eps_s: accumulation error of a score relative to the sum of the
+ * magnitudes of its products).  Scratch as for orc_kv_decode_seq. */
+static double deq_p(double p, int e)
+{
+    return ldexp((double)orc_e4m3_decode(orc_e4m3_encode_d(ldexp(p, -e))), e);
+}
+
+int orc_kv_decode_bounds(const uint16_t *q, int G, const uint16_t *k, const uint16_t *v, int64_t tok_stride,
+                         int64_t len, int D, float sm_scale, int rotate, double eps_s, uint8_t *ws, double *mass,
+                         double *amb, int64_t *fragile)
+{
+    if (D % 32 || D > 512 || G < 1) return -1;
+    memset(mass, 0, sizeof(double) * (size_t)G * (size_t)D);
+    memset(amb, 0, sizeof(double) * (size_t)G * (size_t)D);
+    *fragile = 0;
+    if (len <= 0) return 0;
+    const int64_t ntok = (len + 31) / 32 * 32;
+    double *x = (double *)(void *)ws;
+    uint8_t *kc = ws + ntok * 8;
+    uint8_t *ks = kc + ntok * (D / 2);
+    uint8_t *vc = ks + ntok * (D / 32);
+    uint8_t *vs = vc + (int64_t)D * (ntok / 2);
+    orc_kv_quantize_seq(k, v, tok_stride, len, ntok, D, rotate, kc, ks, vc, vs);
+    const double c = (double)sm_scale / log(2.0);
+    for (int r = 0; r < G; ++r) {
+        uint8_t qc[512], qs[16];
+        orc_q_quantize(q + (int64_t)r * D, D, rotate, qc, qs);
+        double qh[512];
+        for (int d = 0; d < D; ++d) qh[d] = ldexp(e4m3_value(qc[d]), (int)qs[d / 32] - 127);
+        /* x[t] holds the score, the perturbation goes to a second pass */
+        double xmax = -INFINITY;
+        for (int64_t t = 0; t < len; ++t) {
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) {
+                uint8_t byte = kc[t * (D / 2) + d / 2];
+                s += qh[d] * ldexp(e2m1_value((uint8_t)((d & 1) ? byte >> 4 : byte & 15)),
+                                   (int)ks[t * (D / 32) + d / 32] - 127);
+            }
+            x[t] = s * c;
+            xmax = fmax(xmax, x[t]);
+        }
+        const double m = ceil(xmax);
+        double l = 0.0, wsum = 0.0;
+        for (int64_t t = 0; t < len; ++t) l += exp2(x[t] - m);
+        for (int64_t g = 0; g < ntok / 32; ++g) {
+            double p[32], eps[32], a = 0.0, emax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                int64_t t = 32 * g + i;
+                p[i] = 0.0;
+                eps[i] = 0.0;
+                if (t >= len) continue;
+                double sabs = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    uint8_t byte = kc[t * (D / 2) + d / 2];
+                    sabs += fabs(qh[d] * ldexp(e2m1_value((uint8_t)((d & 1) ? byte >> 4 : byte & 15)),
+                                               (int)ks[t * (D / 32) + d / 32] - 127));
+                }
+                p[i] = exp2(x[t] - m);
+                eps[i] = c * eps_s * sabs + ldexp(fabs(x[t]) + 1.0, -20);
+                a = fmax(a, p[i]);
+                emax = fmax(emax, eps[i]);
+            }
+            const int e = orc_mx_exponent(a, 7);
+            const int e_lo = orc_mx_exponent(a * (1.0 - emax), 7), e_hi = orc_mx_exponent(a * (1.0 + emax), 7);
+            for (int i = 0; i < 32; ++i) {
+                int64_t t = 32 * g + i;
+                if (t >= len) continue;
+                const double ph = deq_p(p[i], e);
+                double worst = 0.0;
+                for (int ee = e_lo; ee <= e_hi; ++ee) {
+                    worst = fmax(worst, fabs(deq_p(p[i] * (1.0 - eps[i]), ee) - ph));
+                    worst = fmax(worst, fabs(deq_p(p[i] * (1.0 + eps[i]), ee) - ph));
+                    worst = fmax(worst, fabs(deq_p(p[i], ee) - ph));
+                }
+                /* a change within the perturbation itself is not a flip */
+                if (worst <= 2.0 * eps[i] * p[i]) worst = 0.0;
+                wsum += eps[i] * p[i];
+                if (worst > 0.0) ++*fragile;
+                for (int d = 0; d < D; ++d) {
+                    uint8_t byte = vc[(int64_t)d * (ntok / 2) + t / 2];
+                    double vh = fabs(ldexp(e2m1_value((uint8_t)((t & 1) ? byte >> 4 : byte & 15)),
+                                           (int)vs[(int64_t)d * (ntok / 32) + g] - 127));
+                    mass[(int64_t)r * D + d] += ph * vh / l;
+                    amb[(int64_t)r * D + d] += worst * vh / l;
+                }
+            }
+        }
+        for (int d = 0; d < D; ++d) amb[(int64_t)r * D + d] += mass[(int64_t)r * D + d] * wsum / l;
+    }
+    return 0;
+}

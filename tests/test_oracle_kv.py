@@ -296,3 +296,35 @@ def test_rotation_helps_keys_with_outlier_channels():
     e_rot = np.linalg.norm(O.kv_decode_seq(q, k, v, L, sm, True) - exact)
     e_raw = np.linalg.norm(O.kv_decode_seq(q, k, v, L, sm, False) - exact)
     assert e_rot < e_raw
+
+
+def test_comparison_bound_covers_perturbed_scores():
+    """kv_decode_bounds: a decode whose scores are perturbed anywhere inside
+    the allowed error (here in numpy, probabilities rounded by torch's E4M3
+    cast) stays within 2e-4 mass + amb of the oracle, and the bound is zero
+    where no code can move."""
+    G, D, L, length, sm = 4, 128, 1024, 1000, 1 / math.sqrt(128)
+    q = S.kv_q(1, G, D, seed=12)[0]
+    k, v = S.kv_seq(0, 0, L, D, seed=12)
+    want = O.kv_decode_seq(q, k, v, length, sm, True)
+    mass, amb, nfrag = O.kv_decode_bounds(q, k, v, length, sm, True, eps_s=2.0 ** -15)
+    assert (amb >= 0).all() and (mass > 0).all() and nfrag > 0
+    qh, kh, vh = dequant_seq(q, k, v, length, True)
+    s = qh @ kh.T
+    sabs = np.abs(qh) @ np.abs(kh).T
+    c = sm / math.log(2)
+    rng = np.random.default_rng(13)
+    ntok = (length + 31) // 32 * 32
+    for _ in range(6):
+        x = (s + rng.uniform(-1, 1, s.shape) * 2.0 ** -15 * sabs) * c
+        p = np.exp2(x - np.ceil(x.max(axis=1, keepdims=True)))
+        pp = np.zeros((G, ntok))
+        pp[:, :length] = p
+        E = np.floor(np.log2(pp.reshape(G, -1, 32).max(axis=2))) - 7
+        scale = np.repeat(2.0 ** E, 32, axis=1)
+        ph = e4m3_values(e4m3_torch((pp / scale).astype(np.float32))).reshape(G, ntok) * scale
+        out = ph[:, :length] @ vh / p.sum(axis=1, keepdims=True)
+        assert (np.abs(out - want) <= 2e-4 * mass + amb).all()
+    # with no score error only the exponential's 2^-20 allowance remains
+    _, amb0, nf0 = O.kv_decode_bounds(q, k, v, length, sm, True, eps_s=0.0)
+    assert nf0 < nfrag and amb0.max() < amb.max()

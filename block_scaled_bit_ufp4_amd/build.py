@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libufp4.so")
-SOURCES = ["api.hip", "quantize.hip", "dequant_stats.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "dequant_stats.hip", "gemm.hip", "kvdecode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -386,4 +386,106 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
     return hip_fail(launch_eta(zq, z, M, N, ld, static_cast<double *>(ws), sums, (hipStream_t)stream));
 }
 
+// ---- FP4 KV cache ------------------------------------------------------
+
+static constexpr int64_t KV_PAGE_TOKENS = 128;
+static constexpr int64_t KV_PAGE_BYTES = 17408;
+
+// Pages per split of a decode: requested, or about 2048 workgroups in all
+// with at least one page per wave.
+static int64_t kv_pages_per_split(int64_t B, int64_t Hkv, int64_t npages, int64_t req)
+{
+    if (req > 0) return req < npages ? req : npages;
+    const int64_t total = B * Hkv * npages;
+    int64_t pps = (total + 2047) / 2048;
+    pps = (pps + 3) / 4 * 4;
+    if (pps < 4) pps = 4;
+    return pps;
+}
+
+static int kv_check_heads(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_cap)
+{
+    if (B < 0 || Hkv < 1 || Hq < 1 || L_cap < 1) return UFP4_ERR_SHAPE;
+    if (D != 128) return UFP4_ERR_UNSUPPORTED;
+    if (Hq % Hkv) return UFP4_ERR_SHAPE;
+    if (Hq / Hkv > 16) return UFP4_ERR_UNSUPPORTED;
+    if (L_cap % KV_PAGE_TOKENS) return UFP4_ERR_SHAPE;
+    return UFP4_OK;
+}
+
+size_t ufp4_kv_cache_bytes(int64_t B, int64_t Hkv, int64_t L_cap, int64_t D)
+{
+    if (B < 0 || Hkv < 1 || D != 128 || L_cap < 1 || L_cap % KV_PAGE_TOKENS) return 0;
+    return (size_t)(B * Hkv * (L_cap / KV_PAGE_TOKENS) * KV_PAGE_BYTES);
+}
+
+int ufp4_kv_cache_quantize(const void *k, const void *v, int64_t B, int64_t Hkv, int64_t L_cap, int64_t D,
+                           int64_t stride_b, int64_t stride_h, int64_t stride_t, const int32_t *lens, int rotate_k,
+                           uint8_t *cache, void *stream)
+{
+    int rc = kv_check_heads(B, Hkv, Hkv, D, L_cap);
+    if (rc) return rc;
+    if (rotate_k != 0 && rotate_k != 1) return UFP4_ERR_INVALID_ARG;
+    if (B == 0) return UFP4_OK;
+    if (!k || !v || !lens || !cache) return UFP4_ERR_INVALID_ARG;
+    if (stride_t < D || stride_b < 0 || stride_h < 0 || B > 65535 || Hkv > 65535) return UFP4_ERR_SHAPE;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(cache) || stride_b % 8 || stride_h % 8 || stride_t % 8)
+        return UFP4_ERR_ALIGN;
+    return hip_fail(launch_kv_quantize(static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), B, Hkv, L_cap,
+                                       stride_b, stride_h, stride_t, lens, rotate_k, cache, (hipStream_t)stream));
+}
+
+int ufp4_kv_q_quantize(const void *q, int64_t rows, int64_t D, int rotate, uint8_t *codes, uint8_t *scales,
+                       void *stream)
+{
+    if (rows < 0) return UFP4_ERR_SHAPE;
+    if (D != 128) return UFP4_ERR_UNSUPPORTED;
+    if (rotate != 0 && rotate != 1) return UFP4_ERR_INVALID_ARG;
+    if (rows == 0) return UFP4_OK;
+    if (!q || !codes || !scales) return UFP4_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(codes)) return UFP4_ERR_ALIGN;
+    return hip_fail(launch_q_quantize(static_cast<const uint16_t *>(q), rows, rotate, codes, scales,
+                                      (hipStream_t)stream));
+}
+
+size_t ufp4_kv_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_cap,
+                                     int64_t pages_per_split)
+{
+    if (kv_check_heads(B, Hq, Hkv, D, L_cap)) return 0;
+    const int64_t npages = L_cap / KV_PAGE_TOKENS;
+    const int64_t pps = kv_pages_per_split(B, Hkv, npages, pages_per_split);
+    const int64_t nsplit = (npages + pps - 1) / pps;
+    if (nsplit <= 1) return 0;
+    return (size_t)(B * Hq * nsplit * (D + 2) * (int64_t)sizeof(float));
+}
+
+int ufp4_kv_decode(const void *q, const uint8_t *cache, const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t D, int64_t L_cap, float sm_scale, int rotate, int64_t pages_per_split, float *out, void *ws,
+                   size_t ws_bytes, void *stream)
+{
+    int rc = kv_check_heads(B, Hq, Hkv, D, L_cap);
+    if (rc) return rc;
+    if (rotate != 0 && rotate != 1) return UFP4_ERR_INVALID_ARG;
+    if (!(fabsf(sm_scale) <= 3.0e38f) || pages_per_split < 0) return UFP4_ERR_INVALID_ARG;
+    if (B == 0) return UFP4_OK;
+    if (!q || !cache || !lens || !out) return UFP4_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(cache) || !aligned16(out)) return UFP4_ERR_ALIGN;
+    const int64_t npages = L_cap / KV_PAGE_TOKENS;
+    const int64_t pps = kv_pages_per_split(B, Hkv, npages, pages_per_split);
+    const int64_t nsplit = (npages + pps - 1) / pps;
+    if (nsplit > 65535 || B > 65535 || Hkv > 65535) return UFP4_ERR_SHAPE;
+    float *ws_o = nullptr, *ws_ml = nullptr;
+    if (nsplit > 1) {
+        const size_t need = ufp4_kv_decode_workspace_size(B, Hq, Hkv, D, L_cap, pages_per_split);
+        if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
+        if (!aligned16(ws)) return UFP4_ERR_ALIGN;
+        ws_o = static_cast<float *>(ws);
+        ws_ml = ws_o + B * Hq * nsplit * D;
+    }
+    // log2(e) folded into the score scale, rounded once to binary32
+    const float c = (float)((double)sm_scale * 1.4426950408889634074);
+    return hip_fail(launch_kv_decode(static_cast<const uint16_t *>(q), cache, lens, B, Hkv, (int)(Hq / Hkv), L_cap, c,
+                                     rotate, (int)pps, (int)nsplit, out, ws_o, ws_ml, (hipStream_t)stream));
+}
+
 }  // extern "C"

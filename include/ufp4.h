@@ -21,7 +21,9 @@
  *             the two-level scale alpha = max|X|/(6x448),
  *             Delta = max|X_block|/(alpha x 6) (3.2), stochastic rounding (6.1).
  *   [UQ]      "FP4 训练 vs FP4 推理" (reports.10n1j.top): FP4 tensors with UE8M0
- *             group scales on CDNA4's native scaled-MFMA path (UltraQuant).
+ *             group scales on CDNA4's native scaled-MFMA path; UltraQuant's
+ *             FP8-query x FP4-KV decode attention (asymmetric K/V,
+ *             Walsh-Hadamard rotation).
  *
  * Conventions shared by every call
  *   - Device pointers are HIP device memory owned by the caller; the library
@@ -232,6 +234,82 @@ int ufp4_gemm_bf16(const void *a, const void *b, int64_t M, int64_t N, int64_t K
  * ws: ufp4_workspace_size(UFP4_OP_ETA, ...) bytes. */
 int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, double *sums, void *ws,
              size_t ws_bytes, void *stream);
+
+/* ---- FP4 KV cache and decode attention ([UQ], UltraQuant) ---------------
+ * [UQ] describes decode attention with an FP8 query against a 4-bit KV cache
+ * with UE8M0 group scales on CDNA4's native scaled MFMA, K and V treated
+ * asymmetrically and K Walsh-Hadamard rotated; it gives no formulas.  These
+ * calls compute (head dim D = 128, groups of 32, binary32 unless stated):
+ *   MX rule: a group's exponent is E = floor(log2 amax) - emax, clamped to
+ *     [-127, 127] (amax = 0 gives -127), stored biased (E + 127); elements
+ *     are rounded to nearest-even after scaling by 2^-E and saturate at the
+ *     format's maximum (E2M1: emax 2, max 6; E4M3FN: emax 8, max 448).
+ *   Rotation: H_128, the Walsh-Hadamard matrix of order 128 (entries
+ *     (-1)^popcount(i & j)), applied by butterflies with spans 1, 2, ..., 64
+ *     in that order, each (a, b) -> (a + b, a - b).
+ *   K (per token): MXFP4 of H k (rotate) or of k, groups along the head dim.
+ *   V (per channel): MXFP4 over 32 consecutive tokens, no rotation.
+ *   Q (per query row): MXFP8 (E4M3) of (H q) / 128 (rotate) or of q, groups
+ *     along the head dim; (H q / 128) . (H k) = q . k.
+ *   Scores s_t = <Q', K'_t> of the dequantized operands (fp32 accumulation),
+ *     x_t = s_t c with c = sm_scale log2(e) rounded to binary32, tokens
+ *     t < len.  p_t = 2^(x_t - m) for an integer m >= max x_t.
+ *   P: per 32-token block, E = floor(log2 max p) - 7 (one above the MX rule,
+ *     so the block maximum is never clamped), p' = E4M3(p 2^-E) 2^E.
+ *   out = sum_t p'_t V'_t / sum_t p_t (fp32 accumulation); len = 0 gives 0.
+ *     Any integer m gives the same result (the block exponents absorb 2^m),
+ *     so the splits of a long cache combine by exact power-of-two rescaling.
+ *
+ * Cache layout: [B][Hkv][L_cap/128] pages of 17408 bytes, one per 128 tokens.
+ * A page holds the operands of v_mfma_scale_f32_16x16x128_f8f6f4 in register
+ * order (lane l, rho = l % 16, g = l / 16):
+ *   [0, 8192)      K codes: 16 bytes at j*1024 + l*16 (j = 0..7) = channels
+ *                  32g .. 32g+31 (low nibble first) of token
+ *                  64(j/4) + 16(rho/4) + 4(j%4) + rho%4 of the page;
+ *   [8192, 8704)   K exponents: byte j at l*8 + j, for the same token and
+ *                  channel group;
+ *   [8704, 16896)  V codes: 16 bytes at n*1024 + l*16 (n = 0..7) = tokens
+ *                  32g .. 32g+31 (low nibble first) of channel 8 rho + n;
+ *   [16896, 17408) V exponents: byte n at l*8 + n, same channel and tokens.
+ * Tokens len .. (end of the last page) are stored as zeros; pages past the
+ * last one holding a token are not written.
+ */
+
+/* Bytes of a cache for B sequences, Hkv KV heads, capacity L_cap tokens
+ * (a multiple of 128), head dim D (128).  0 for unsupported sizes. */
+size_t ufp4_kv_cache_bytes(int64_t B, int64_t Hkv, int64_t L_cap, int64_t D);
+
+/* Quantize K and V (bf16, device) into the cache.  Element (b, h, t, d) is at
+ * k[b*stride_b + h*stride_h + t*stride_t + d] (strides in elements, multiples
+ * of 8; k, v, cache 16-byte aligned).  lens: device int32[B], tokens per
+ * sequence (clamped to [0, L_cap]).  rotate_k: 1 applies H_128 to K (the
+ * decode must be called with the same value).  Errors: SHAPE (L_cap not a
+ * multiple of 128, Hkv < 1, stride_t < D), UNSUPPORTED (D != 128), ALIGN,
+ * INVALID_ARG (null pointer, rotate_k not 0/1). */
+int ufp4_kv_cache_quantize(const void *k, const void *v, int64_t B, int64_t Hkv, int64_t L_cap, int64_t D,
+                           int64_t stride_b, int64_t stride_h, int64_t stride_t, const int32_t *lens, int rotate_k,
+                           uint8_t *cache, void *stream);
+
+/* The query quantization of the decode on its own: rows x 128 bf16 (device,
+ * contiguous) -> codes uint8[rows][128] (E4M3FN, sign in bit 7) and scales
+ * uint8[rows][4] (biased exponents). */
+int ufp4_kv_q_quantize(const void *q, int64_t rows, int64_t D, int rotate, uint8_t *codes, uint8_t *scales,
+                       void *stream);
+
+/* Workspace bytes of ufp4_kv_decode (0 when the cache is not split). */
+size_t ufp4_kv_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_cap,
+                                     int64_t pages_per_split);
+
+/* One decode step: q bf16 [B][Hq][128] (query heads h*G .. h*G+G-1 read KV
+ * head h, G = Hq/Hkv <= 16), the cache and lens as written by
+ * ufp4_kv_cache_quantize, out fp32 [B][Hq][128].  pages_per_split: pages of
+ * one workgroup (0 = chosen from the sizes); with more than one split a
+ * second kernel combines them and ws must hold
+ * ufp4_kv_decode_workspace_size(...) bytes.  Errors as above, plus
+ * WORKSPACE, INVALID_ARG for a non-finite sm_scale. */
+int ufp4_kv_decode(const void *q, const uint8_t *cache, const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t D, int64_t L_cap, float sm_scale, int rotate, int64_t pages_per_split, float *out, void *ws,
+                   size_t ws_bytes, void *stream);
 
 /* Workspace bytes for op (UFP4_OP_*) on a rows x cols source (QGEMM: rows = M+N,
  * cols = K; ETA: rows = M, cols = N).  cfg may be NULL except for QGEMM and

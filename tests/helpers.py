@@ -48,3 +48,39 @@ def sample_rows(V: int, n: int, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(V, size=min(n, V), replace=False).tolist()) | {0, V - 1}
     return np.array(sorted(pick))
+
+
+KV_PAGE_BYTES = 17408
+
+
+def kv_unshuffle(cache: np.ndarray, B: int, Hkv: int, L_cap: int, b: int, h: int, npages: int):
+    """One sequence's pages of the FP4 KV cache in natural layout: K codes
+    [T][64], K exponents [T][4], V codes [128][T/2], V exponents [128][T/32]
+    for T = 128 npages.  Index logic only, from the documented page layout
+    (lane l, rho = l % 16, g = l / 16; K instruction j holds channel group g
+    of token 64(j/4) + 16(rho/4) + 4(j%4) + rho%4; V instruction n holds
+    tokens 32g..32g+31 of channel 8 rho + n)."""
+    pages = cache.reshape(B, Hkv, L_cap // 128, KV_PAGE_BYTES)[b, h, :npages]
+    T = 128 * npages
+    kc = np.empty((T, 64), np.uint8)
+    ks = np.empty((T, 4), np.uint8)
+    vc = np.empty((128, T // 2), np.uint8)
+    vs = np.empty((128, T // 32), np.uint8)
+    lane = np.arange(64)
+    rho, g = lane % 16, lane // 16
+    cols16 = 16 * g[:, None] + np.arange(16)
+    for p in range(npages):
+        pg = pages[p]
+        kcodes = pg[:8192].reshape(8, 64, 16)
+        kscl = pg[8192:8704].reshape(64, 8)
+        vcodes = pg[8704:16896].reshape(8, 64, 16)
+        vscl = pg[16896:].reshape(64, 8)
+        for j in range(8):
+            tok = 128 * p + 64 * (j // 4) + 16 * (rho // 4) + 4 * (j % 4) + rho % 4
+            kc[tok[:, None], cols16] = kcodes[j]
+            ks[tok, g] = kscl[:, j]
+        for n in range(8):
+            ch = 8 * rho + n
+            vc[ch[:, None], (64 * p + 16 * g)[:, None] + np.arange(16)] = vcodes[n]
+            vs[ch, 4 * p + g] = vscl[:, n]
+    return kc, ks, vc, vs

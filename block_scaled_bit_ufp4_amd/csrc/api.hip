@@ -391,13 +391,14 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
 static constexpr int64_t KV_PAGE_TOKENS = 128;
 static constexpr int64_t KV_PAGE_BYTES = 17408;
 
-// Pages per split of a decode: requested, or about 2048 workgroups in all
-// with at least one page per wave.
+// Pages per split of a decode: requested, or about 512 workgroups in all
+// (two per compute unit, all resident at once) with at least one page per
+// wave.
 static int64_t kv_pages_per_split(int64_t B, int64_t Hkv, int64_t npages, int64_t req)
 {
     if (req > 0) return req < npages ? req : npages;
     const int64_t total = B * Hkv * npages;
-    int64_t pps = (total + 2047) / 2048;
+    int64_t pps = (total + 511) / 512;
     pps = (pps + 3) / 4 * 4;
     if (pps < 4) pps = 4;
     return pps;
@@ -410,6 +411,8 @@ static int kv_check_heads(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t
     if (Hq % Hkv) return UFP4_ERR_SHAPE;
     if (Hq / Hkv > 16) return UFP4_ERR_UNSUPPORTED;
     if (L_cap % KV_PAGE_TOKENS) return UFP4_ERR_SHAPE;
+    // one sequence's pages are addressed with 32-bit buffer offsets
+    if ((L_cap / KV_PAGE_TOKENS + 4) * KV_PAGE_BYTES > INT32_MAX) return UFP4_ERR_SHAPE;
     return UFP4_OK;
 }
 

@@ -276,7 +276,8 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
  */
 
 /* Bytes of a cache for B sequences, Hkv KV heads, capacity L_cap tokens
- * (a multiple of 128), head dim D (128).  0 for unsupported sizes. */
+ * (a multiple of 128, below 15.7 million: one sequence's pages stay under
+ * 2 GiB), head dim D (128).  0 for unsupported sizes. */
 size_t ufp4_kv_cache_bytes(int64_t B, int64_t Hkv, int64_t L_cap, int64_t D);
 
 /* Quantize K and V (bf16, device) into the cache.  Element (b, h, t, d) is at

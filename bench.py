@@ -21,6 +21,7 @@ MXFP4 block-scaled GEMM at 8192^3 (A, B: N(0,1) bf16 -> RHT -> MXFP4).
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -50,6 +51,7 @@ def parse():
     p.add_argument("--no-gemm", action="store_true", help="skip the qgemm leg")
     p.add_argument("--no-configs", action="store_true", help="skip the per-workload kernel timings")
     p.add_argument("--no-linear", action="store_true", help="skip the 4-bit linear-layer GEMMs")
+    p.add_argument("--no-kv", action="store_true", help="skip the FP4 KV-cache decode attention")
     p.add_argument("--cpu-rows", type=int, default=ROWS)
     p.add_argument("--cpu-reps", type=int, default=2)
     return p.parse_args()
@@ -173,6 +175,8 @@ def main():
         out["configs"] = bench_configs(U, S, torch, dev, stream)
     if not args.no_linear:
         out["linear"] = bench_linear(U, S, torch, dev, stream)
+    if not args.no_kv:
+        out["kv_decode"] = bench_kv(U, S, torch, dev, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x_bits, args.cpu_rows, args.cpu_reps)
     print(json.dumps(out), flush=True)
@@ -286,6 +290,59 @@ def bench_linear(U, S, torch, dev, stream, reps=3):
                       "eta": round(float(sm[0] / sm[1]), 6),
                       "sqnr_db": round(float(10 * np.log10(sm[1] / sm[2])), 3)}
         out[name] = res
+    return out
+
+
+def bench_kv(U, S, torch, dev, stream, reps=20):
+    """One decode step of attention against the FP4 KV cache at the Llama-3-8B
+    attention shape (32 query heads, 8 KV heads, head dim 128) for 32
+    sequences of 16384 tokens: MXFP8 query x MXFP4 keys (Walsh-Hadamard
+    rotated, or not) and values on the scaled MFMA.  Reports the step (decode
+    kernel + split combine), the decode kernel alone, its HBM rate against the
+    algorithmic bytes (cache + query + output), the cache quantization, and the
+    output error against exact attention (fp32 softmax over the unquantized
+    bf16 keys and values)."""
+    B, Hq, Hkv, L, D = 32, 32, 8, 16384, 128
+    G = Hq // Hkv
+    q, k, v = S.kv_decode(B, Hq, Hkv, L, D, seed=0)
+
+    def dev_bf16(h):
+        return torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    del k, v
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    exact = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    for b in range(B):  # fp32 reference, one sequence at a time
+        qf = qd[b].float().view(Hkv, G, D)
+        kt = kd[b].float().transpose(1, 2).contiguous()
+        p = torch.softmax(torch.matmul(qf, kt) * sm, dim=-1)
+        exact[b] = torch.matmul(p, vd[b].float()).view(Hq, D)
+    cache_bytes = U.ufp4_kv_cache_bytes(B, Hkv, L, D)
+    alg_bytes = cache_bytes + B * Hq * D * 2 + B * Hq * D * 4
+    out = {"workload": "decode step, 32 sequences x 16384 tokens, 32 query / 8 KV heads, head dim 128; FP4 cache "
+                       "(E2M1 + UE8M0/32: keys per token over the head dim, values per channel over 32 tokens)",
+           "cache_bytes": cache_bytes, "bytes_per_token_per_kv_head": 136, "bf16_bytes_per_token_per_kv_head": 512,
+           "algorithmic_bytes_per_step": alg_bytes}
+    for name, rot in (("rotated_keys", True), ("no_rotation", False)):
+        cache = U.ufp4_kv_cache_quantize(kd, vd, lens, rot)
+        o = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        need = U.ufp4_kv_decode_workspace_size(B, Hq, Hkv, L)
+        ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+        ms_step, ms_kernel = _time(lambda: U.ufp4_kv_decode(qd, cache, lens, Hkv, L, sm, rot, out=o, ws=ws),
+                                   torch, stream, reps, U)
+        ms_quant = _time(lambda: U.ufp4_kv_cache_quantize(kd, vd, lens, rot, cache), torch, stream, 3)
+        err = float(torch.linalg.norm(o - exact) / torch.linalg.norm(exact))
+        gbs = alg_bytes / (ms_kernel * 1e-3) / 1e9
+        out[name] = {"step_us": round(ms_step * 1e3, 2), "decode_kernel_us": round(ms_kernel * 1e3, 2),
+                     "decode_kernel_GBps": round(gbs, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                     "step_GBps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "cache_quantize_us": round(ms_quant * 1e3, 2),
+                     "rel_err_vs_exact_attention": round(err, 5)}
+        del cache
     return out
 
 

@@ -391,16 +391,17 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
 static constexpr int64_t KV_PAGE_TOKENS = 128;
 static constexpr int64_t KV_PAGE_BYTES = 17408;
 
-// Pages per split of a decode: requested, or about 512 workgroups in all
-// (two per compute unit, all resident at once) with at least one page per
-// wave.
+// Pages per split of a decode: requested, or about 256 workgroups in all
+// (one 8-wave workgroup per compute unit, all resident at once) with at least
+// one page per wave.  With B * Hkv >= 256 every sequence is one split and no
+// combine pass runs.
 static int64_t kv_pages_per_split(int64_t B, int64_t Hkv, int64_t npages, int64_t req)
 {
     if (req > 0) return req < npages ? req : npages;
     const int64_t total = B * Hkv * npages;
-    int64_t pps = (total + 511) / 512;
-    pps = (pps + 3) / 4 * 4;
-    if (pps < 4) pps = 4;
+    int64_t pps = (total + 255) / 256;
+    pps = (pps + 7) / 8 * 8;
+    if (pps < 8) pps = 8;
     return pps;
 }
 

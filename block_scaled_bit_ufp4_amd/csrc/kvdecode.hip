@@ -51,7 +51,8 @@ constexpr int KV_K_SCALES = 8192;
 constexpr int KV_V_CODES = 8704;
 constexpr int KV_V_SCALES = 16896;
 constexpr int KV_PAGE_BYTES = 17408;
-constexpr int KV_NT = 2;  // cache-policy bits of a buffer load: non-temporal
+constexpr int KV_NT = 2;     // cache-policy bits of a buffer load: non-temporal
+constexpr int KV_WAVES = 8;  // waves of a decode workgroup (pages are dealt out round-robin)
 
 // Token of score MFMA j, A row rho, inside a page.
 __device__ __forceinline__ int page_token(int j, int rho)
@@ -392,11 +393,11 @@ __device__ __forceinline__ void process_page(const PageRegs &P, const v8i &qb, i
         st.O[n] = mfma_fp4_fp8(P.vc[n], pb, st.O[n], n & 3, (int)(n < 4 ? P.vs.x : P.vs.y), ps);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kv_decode_kernel(KvDecodeArgs a)
+__global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void kv_decode_kernel(KvDecodeArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t q_lds[16 * KV_D + 64];
-    __shared__ float o_lds[4][16][KV_D];
-    __shared__ float ml_lds[4][16][2];
+    __shared__ float o_lds[KV_WAVES][16][KV_D];
+    __shared__ float ml_lds[KV_WAVES][16][2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -449,15 +450,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // current page is processed, and no copy between the sets waits on them.
     PageRegs nxt;
     while (p < p1) {
-        load_page(rs, p + 4, v16, v8, nxt);
+        load_page(rs, p + KV_WAVES, v16, v8, nxt);
         __builtin_amdgcn_sched_barrier(0);
         process_page(cur, qb, qs, p, len, a.c, g, st);
-        p += 4;
+        p += KV_WAVES;
         if (p >= p1) break;
-        load_page(rs, p + 4, v16, v8, cur);
+        load_page(rs, p + KV_WAVES, v16, v8, cur);
         __builtin_amdgcn_sched_barrier(0);
         process_page(nxt, qb, qs, p, len, a.c, g, st);
-        p += 4;
+        p += KV_WAVES;
     }
     const float m_run = st.m_run, l_lane = st.l_lane;
     v4f O[8];
@@ -479,33 +480,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     __syncthreads();
 
-    // merge the four waves: thread t -> row t/16, channels 8 (t%16) .. +7
-    const int t = threadIdx.x, row = t >> 4, d0 = (t & 15) * 8;
+    // merge the waves: thread t -> row t/32, channels 4 (t%32) .. +3
+    const int t = threadIdx.x, row = t >> 5, d0 = (t & 31) * 4;
     if (row >= a.G) return;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][row][0]);
-    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0}, lsum = 0.0f;
+    for (int w = 0; w < KV_WAVES; ++w) M = fmaxf(M, ml_lds[w][row][0]);
+    float o[4] = {0, 0, 0, 0}, lsum = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < KV_WAVES; ++w) {
             const float f = ldexpf(1.0f, (int)fmaxf(ml_lds[w][row][0] - M, -1000.0f));
             lsum += ml_lds[w][row][1] * f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) o[k] += o_lds[w][row][d0 + k] * f;
+            for (int k = 0; k < 4; ++k) o[k] += o_lds[w][row][d0 + k] * f;
         }
     }
     if (a.nsplit == 1) {
         const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-        float4 *dst = reinterpret_cast<float4 *>(a.out + ((b * Hq + h * a.G + row) * KV_D + d0));
-        dst[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-        dst[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+        *reinterpret_cast<float4 *>(a.out + ((b * Hq + h * a.G + row) * KV_D + d0)) =
+            make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
     } else {
         const int64_t slot = ((b * a.Hkv + h) * a.nsplit + split) * a.G + row;
-        float4 *dst = reinterpret_cast<float4 *>(a.ws_o + slot * KV_D + d0);
-        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-        if ((t & 15) == 0) {
+        *reinterpret_cast<float4 *>(a.ws_o + slot * KV_D + d0) = make_float4(o[0], o[1], o[2], o[3]);
+        if ((t & 31) == 0) {
             a.ws_ml[slot * 2 + 0] = M;
             a.ws_ml[slot * 2 + 1] = lsum;
         }
@@ -557,7 +555,7 @@ hipError_t launch_kv_decode(const uint16_t *q, const uint8_t *cache, const int32
                             float *ws_ml, hipStream_t s)
 {
     KvDecodeArgs a{q, cache, lens, Hkv, L_cap, L_cap / KV_PAGE, G, pps, nsplit, rotate, c, out, ws_o, ws_ml};
-    launch_kernel(kv_decode_kernel, dim3((unsigned)nsplit, (unsigned)Hkv, (unsigned)B), dim3(256), s, a);
+    launch_kernel(kv_decode_kernel, dim3((unsigned)nsplit, (unsigned)Hkv, (unsigned)B), dim3(64 * KV_WAVES), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     launch_kernel(kv_combine_kernel, dim3((unsigned)(B * Hkv * G)), dim3(128), s, a);

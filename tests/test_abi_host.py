@@ -178,5 +178,7 @@ def test_kv_decode_workspace_sizes():
     # one split: no workspace; four splits of 2 pages: B * Hq * 4 * (128 + 2) floats
     assert U.ufp4_kv_decode_workspace_size(1, 4, 1, 256) == 0
     assert U.ufp4_kv_decode_workspace_size(1, 4, 1, 1024, pages_per_split=2) == 1 * 4 * 4 * 130 * 4
-    # automatic split: about 512 workgroups, at least 4 pages each (64 pages: 2 splits)
-    assert U.ufp4_kv_decode_workspace_size(32, 32, 8, 16384) == 32 * 32 * 2 * 130 * 4
+    # automatic split: about 256 workgroups of at least 8 pages; 256 sequences
+    # of 128 pages need no split, 4 sequences are cut into 16 splits of 8 pages
+    assert U.ufp4_kv_decode_workspace_size(32, 32, 8, 16384) == 0
+    assert U.ufp4_kv_decode_workspace_size(1, 16, 4, 16384) == 1 * 16 * 16 * 130 * 4

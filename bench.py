@@ -39,6 +39,8 @@ QUANT_BYTES = N_ELEM * 2 + N_ELEM // 2 + N_ELEM // 16  # bf16 in + codes + E4M3 
 AMAX_BYTES = N_ELEM * 2
 PMC_FILE = os.path.join(ROOT, "profiles", "quantize_row_e2m1_e4m3_rht_8192x8192_pmc.json")
 KERNEL_SRC = os.path.join(ROOT, "block_scaled_bit_ufp4_amd", "csrc", "quantize.hip")
+KV_PMC_FILE = os.path.join(ROOT, "profiles", "kv_decode_32x16384_pmc.json")
+KV_KERNEL_SRC = os.path.join(ROOT, "block_scaled_bit_ufp4_amd", "csrc", "kvdecode.hip")
 
 
 def parse():
@@ -61,14 +63,15 @@ def src_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the quantize kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+def traffic_from_profile(pmc_file=None, kernel_src=None):
+    """HBM bytes per launch of a kernel (by default the quantize kernel) from
+    the committed rocprofv3 counter summary, if it was taken on the current
+    kernel source."""
     try:
-        d = json.load(open(PMC_FILE))
+        d = json.load(open(pmc_file or PMC_FILE))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_sha256_16") != src_hash(KERNEL_SRC):
+    if d.get("kernel_source_sha256_16") != src_hash(kernel_src or KERNEL_SRC):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -320,6 +323,7 @@ def bench_kv(U, S, torch, dev, stream, reps=20):
         p = torch.softmax(torch.matmul(qf, kt) * sm, dim=-1)
         exact[b] = torch.matmul(p, vd[b].float()).view(Hq, D)
     cache_bytes = U.ufp4_kv_cache_bytes(B, Hkv, L, D)
+    traffic = traffic_from_profile(KV_PMC_FILE, KV_KERNEL_SRC)
     alg_bytes = cache_bytes + B * Hq * D * 2 + B * Hq * D * 4
     out = {"workload": "decode step, 32 sequences x 16384 tokens, 32 query / 8 KV heads, head dim 128; FP4 cache "
                        "(E2M1 + UE8M0/32: keys per token over the head dim, values per channel over 32 tokens)",
@@ -338,7 +342,8 @@ def bench_kv(U, S, torch, dev, stream, reps=20):
         out[name] = {"step_us": round(ms_step * 1e3, 2), "decode_kernel_us": round(ms_kernel * 1e3, 2),
                      "decode_kernel_GBps": round(gbs, 1),
                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                                  "kernel": "kv_decode_kernel", "bytes_per_launch": alg_bytes},
                      "step_GBps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "cache_quantize_us": round(ms_quant * 1e3, 2),
                      "rel_err_vs_exact_attention": round(err, 5)}

@@ -12,11 +12,11 @@
 // pipeline stage (128 E2M1 codes or 32 bf16 values), and one 32x32 MFMA step
 // consumes 32 bytes of each of 32 rows, lane l holding row l mod 32 and the
 // 16-byte half l / 32 (32 FP4 codes of one 32-element scale block, or 8 bf16).
-// Workgroup tile 256 x 256: eight waves (two per SIMD, so one wave's MFMAs
-// cover the other's LDS and barrier waits) of 128 x 64 (4 x 2 MFMA tiles of
-// 32 x 32, 128 fp32 accumulators per lane) over a ring of four LDS stages
-// (256 rows x 64 bytes per operand plus scales), filled by asynchronous
-// global -> LDS copies three stages ahead of the multiplications.  The
+// Workgroup tile 256 x 256: four waves (one per SIMD) of 128 x 128 (4 x 4
+// MFMA tiles of 32 x 32, 256 fp32 accumulators per lane) over a ring of four
+// LDS stages (256 rows x 64 bytes per operand plus scales), filled by
+// asynchronous global -> LDS copies three stages ahead of the
+// multiplications.  The
 // 16-byte chunks of each row are XOR-swizzled so the 16-byte fragment reads
 // are free of bank conflicts.  Workgroups are ordered so that
 // the eight XCDs each work on a compact band of output tiles.

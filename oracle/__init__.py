@@ -103,11 +103,11 @@ def lib():
         L.orc_e4m3_encode_d.argtypes = [C.c_double]
         L.orc_e4m3_encode_d.restype = C.c_uint8
         L.orc_q_quantize.argtypes = [p, i32, i32, p, p]
-        L.orc_k_quantize_row.argtypes = [p, i32, i32, p, p]
-        L.orc_kv_quantize_seq.argtypes = [p, p, i64, i64, i64, i32, i32, p, p, p, p]
-        L.orc_kv_decode_seq.argtypes = [p, i32, p, p, i64, i64, i32, C.c_float, i32, p, p]
+        L.orc_k_quantize_row.argtypes = [p, i32, i32, i32, p, p]
+        L.orc_kv_quantize_seq.argtypes = [p, p, i64, i64, i64, i32, i32, i32, p, p, p, p]
+        L.orc_kv_decode_seq.argtypes = [p, i32, p, p, i64, i64, i32, C.c_float, i32, i32, p]
         L.orc_kv_decode_seq.restype = i32
-        L.orc_kv_decode_bounds.argtypes = [p, i32, p, p, i64, i64, i32, C.c_float, i32, C.c_double, p, p, p, p]
+        L.orc_kv_decode_bounds.argtypes = [p, i32, p, p, i64, i64, i32, C.c_float, i32, i32, C.c_double, p, p, p]
         L.orc_kv_decode_bounds.restype = i32
         _lib = L
     return _lib
@@ -358,57 +358,57 @@ def q_quantize(q: np.ndarray, rotate: bool):
     return codes.reshape(q.shape), scales.reshape(q.shape[:-1] + (D // 32,))
 
 
-def kv_quantize_seq(k: np.ndarray, v: np.ndarray, length: int, ntok: int, rotate: bool):
-    """The FP4 cache of one sequence, natural layout: k, v bf16 bits [T][D]
-    (T >= length).  Returns kcodes [ntok][D/2], kscales [ntok][D/32],
-    vcodes [D][ntok/2], vscales [D][ntok/32]."""
+KV_FORMATS = {"fp4": 0, "fp8": 1}
+
+
+def kv_quantize_seq(k: np.ndarray, v: np.ndarray, length: int, ntok: int, rotate: bool, fmt: str = "fp4"):
+    """The KV cache of one sequence, natural layout: k, v bf16 bits [T][D]
+    (T >= length).  Returns kcodes [ntok][D cb], kscales [ntok][D/32],
+    vcodes [D][ntok cb], vscales [D][ntok/32] with cb = 1/2 (fp4) or 1 (fp8)."""
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
     assert k.shape == v.shape and ntok % 32 == 0 and ntok >= length
     D = k.shape[1]
-    kc = np.empty((ntok, D // 2), dtype=np.uint8)
+    fp8 = KV_FORMATS[fmt]
+    cb = 1 if fp8 else 2
+    kc = np.empty((ntok, D // cb), dtype=np.uint8)
     ks = np.empty((ntok, D // 32), dtype=np.uint8)
-    vc = np.empty((D, ntok // 2), dtype=np.uint8)
+    vc = np.empty((D, ntok // cb), dtype=np.uint8)
     vs = np.empty((D, ntok // 32), dtype=np.uint8)
-    lib().orc_kv_quantize_seq(_ptr(k), _ptr(v), D, int(length), int(ntok), D, int(rotate),
+    lib().orc_kv_quantize_seq(_ptr(k), _ptr(v), D, int(length), int(ntok), D, int(rotate), fp8,
                               _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs))
     return kc, ks, vc, vs
 
 
 def kv_decode_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, length: int, sm_scale: float,
-                  rotate: bool) -> np.ndarray:
+                  rotate: bool, fmt: str = "fp4") -> np.ndarray:
     """Decode attention of one sequence: q bf16 bits [G][D], k, v [T][D]
     (T >= length); binary64 output [G][D]."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
     G, D = q.shape
-    ntok = (int(length) + 31) // 32 * 32
-    ws = np.empty(max(8, ntok * (8 + D // 2 + D // 32) + D * (ntok // 2 + ntok // 32)) // 8 + 1, dtype=np.float64)
     out = np.empty((G, D), dtype=np.float64)
     rc = lib().orc_kv_decode_seq(_ptr(q), G, _ptr(k), _ptr(v), D, int(length), D, float(sm_scale), int(rotate),
-                                 _ptr(ws), _ptr(out))
+                                 KV_FORMATS[fmt], _ptr(out))
     if rc:
-        raise ValueError("bad decode shape")
+        raise ValueError("bad decode shape" if rc == -1 else "out of memory")
     return out
 
 
 def kv_decode_bounds(q: np.ndarray, k: np.ndarray, v: np.ndarray, length: int, sm_scale: float, rotate: bool,
-                     eps_s: float = 2.0 ** -15):
+                     eps_s: float = 2.0 ** -15, fmt: str = "fp4"):
     """(mass [G][D], ambiguity bound [G][D], number of fragile tokens) for
     comparing a binary32 decode with kv_decode_seq."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
     G, D = q.shape
-    ntok = (int(length) + 31) // 32 * 32
-    ws = np.empty(max(8, ntok * (8 + D // 2 + D // 32) + D * (ntok // 2 + ntok // 32)) // 8 + 1, dtype=np.float64)
     mass = np.empty((G, D), dtype=np.float64)
     amb = np.empty((G, D), dtype=np.float64)
     frag = C.c_int64(0)
     rc = lib().orc_kv_decode_bounds(_ptr(q), G, _ptr(k), _ptr(v), D, int(length), D, float(sm_scale), int(rotate),
-                                    float(eps_s), _ptr(ws), _ptr(mass), _ptr(amb), C.byref(frag))
+                                    KV_FORMATS[fmt], float(eps_s), _ptr(mass), _ptr(amb), C.byref(frag))
     if rc:
-        raise ValueError("bad decode shape")
+        raise ValueError("bad decode shape" if rc == -1 else "out of memory")
     return mass, amb, int(frag.value)
-

@@ -20,6 +20,8 @@
  *     P V), no rotation -- the asymmetric treatment;
  *   - Q: E4M3 groups of 32 channels after the same transform scaled by 1/D,
  *     so that the rotation cancels in Q K^T;
+ *   - the FP8 KV baseline the page measures against is read as the same cache
+ *     in MXFP8 (E4M3 codes, the same groups and rotation);
  *   - the softmax probabilities P are the second FP8 operand: quantized to
  *     E4M3 per 32 consecutive tokens with the exponent floor(log2 amax) - 7,
  *     one above the MX rule, so the group maximum is never clamped; the
@@ -30,6 +32,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* From oracle.c (same library). */
@@ -129,104 +132,151 @@ void orc_q_quantize(const uint16_t *q, int D, int rotate, uint8_t *codes, uint8_
     }
 }
 
-/* MXFP4 (E2M1, UE8M0 per 32 channels) of one key row of D channels after the
- * optional unnormalised transform H_D k in binary32.  codes[D/2]: byte j holds
- * channels 2j (low nibble) and 2j+1; scales[D/32]: biased exponents. */
-void orc_k_quantize_row(const uint16_t *k, int D, int rotate, uint8_t *codes, uint8_t *scales)
+/* One MX group of 32 values: the exponent E = floor(log2 amax) - emax
+ * (emax 2 for E2M1, 8 for E4M3), then each value scaled by 2^-E (exact) and
+ * rounded to nearest-even, saturating at the format maximum.  E2M1 codes are
+ * packed two per byte (element 2j in the low nibble of byte j), E4M3FN codes
+ * one per byte with the sign in bit 7.  Returns the biased exponent. */
+static uint8_t mx_group(const float *y, int fp8, uint8_t *codes)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)y[i]));
+    const int e = orc_mx_exponent(amax, fp8 ? 8 : 2);
+    if (fp8) {
+        for (int i = 0; i < 32; ++i)
+            codes[i] = (uint8_t)((signbit(y[i]) ? 0x80 : 0) | orc_e4m3_encode_d(ldexp(fabs((double)y[i]), -e)));
+    } else {
+        for (int i = 0; i < 32; i += 2) {
+            int c0 = orc_round_rtne((float)ldexp((double)y[i], -e), ORC_E2M1_FMT);
+            int c1 = orc_round_rtne((float)ldexp((double)y[i + 1], -e), ORC_E2M1_FMT);
+            codes[i / 2] = (uint8_t)(c0 | (c1 << 4));
+        }
+    }
+    return (uint8_t)(e + 127);
+}
+
+/* Value (without the group scale) of element i of a code array. */
+static double code_value(const uint8_t *codes, int64_t i, int fp8)
+{
+    if (fp8) return e4m3_value(codes[i]);
+    const uint8_t b = codes[i / 2];
+    return e2m1_value((uint8_t)((i & 1) ? b >> 4 : b & 15));
+}
+
+/* One key row of D channels after the optional unnormalised transform H_D k
+ * in binary32, in MX groups of 32 channels: E2M1 (fp8 = 0, codes[D/2]) or
+ * E4M3 (fp8 = 1, codes[D]); scales[D/32] biased exponents. */
+void orc_k_quantize_row(const uint16_t *k, int D, int rotate, int fp8, uint8_t *codes, uint8_t *scales)
 {
     float y[512];
     for (int d = 0; d < D; ++d) y[d] = orc_bf16_to_f32(k[d]);
     if (rotate) orc_fwht_f32(y, D);
-    for (int g = 0; g < D / 32; ++g) {
-        double amax = 0.0;
-        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)y[32 * g + i]));
-        int e = orc_mx_exponent(amax, 2);
-        scales[g] = (uint8_t)(e + 127);
-        for (int i = 0; i < 32; i += 2) {
-            int c0 = orc_round_rtne((float)ldexp((double)y[32 * g + i], -e), ORC_E2M1_FMT);
-            int c1 = orc_round_rtne((float)ldexp((double)y[32 * g + i + 1], -e), ORC_E2M1_FMT);
-            codes[(32 * g + i) / 2] = (uint8_t)(c0 | (c1 << 4));
-        }
-    }
+    for (int g = 0; g < D / 32; ++g) scales[g] = mx_group(y + 32 * g, fp8, codes + g * (fp8 ? 32 : 16));
 }
 
-/* The FP4 cache of one sequence (one batch entry, one KV head), natural layout.
+/* The KV cache of one sequence (one batch entry, one KV head), natural layout,
+ * FP4 (E2M1, fp8 = 0) or the FP8 baseline (E4M3, fp8 = 1); cb = bytes per code
+ * (1/2 or 1).
  *   k, v: bf16 [token][tok_stride], channels contiguous; tokens [0, len) hold
  *         data, tokens [len, ntok) count as zeros (ntok a multiple of 32).
- *   kcodes [ntok][D/2], kscales [ntok][D/32]: K along the head dim.
- *   vcodes [D][ntok/2], vscales [D][ntok/32]: V along tokens, one group per
- *         channel and 32 tokens; byte j of a channel holds tokens 2j, 2j+1. */
+ *   kcodes [ntok][D cb], kscales [ntok][D/32]: K along the head dim.
+ *   vcodes [D][ntok cb], vscales [D][ntok/32]: V along tokens, one group per
+ *         channel and 32 tokens. */
 void orc_kv_quantize_seq(const uint16_t *k, const uint16_t *v, int64_t tok_stride, int64_t len, int64_t ntok, int D,
-                         int rotate, uint8_t *kcodes, uint8_t *kscales, uint8_t *vcodes, uint8_t *vscales)
+                         int rotate, int fp8, uint8_t *kcodes, uint8_t *kscales, uint8_t *vcodes, uint8_t *vscales)
 {
     uint16_t zero[512];
     memset(zero, 0, sizeof(zero));
+    const int64_t krow = fp8 ? D : D / 2, vrow = fp8 ? ntok : ntok / 2;
     for (int64_t t = 0; t < ntok; ++t)
-        orc_k_quantize_row(t < len ? k + t * tok_stride : zero, D, 0 != rotate, kcodes + t * (D / 2),
+        orc_k_quantize_row(t < len ? k + t * tok_stride : zero, D, 0 != rotate, fp8, kcodes + t * krow,
                            kscales + t * (D / 32));
     for (int d = 0; d < D; ++d)
         for (int64_t g = 0; g < ntok / 32; ++g) {
             float y[32];
-            double amax = 0.0;
             for (int i = 0; i < 32; ++i) {
                 int64_t t = 32 * g + i;
                 y[i] = t < len ? orc_bf16_to_f32(v[t * tok_stride + d]) : 0.0f;
-                amax = fmax(amax, fabs((double)y[i]));
             }
-            int e = orc_mx_exponent(amax, 2);
-            vscales[(int64_t)d * (ntok / 32) + g] = (uint8_t)(e + 127);
-            for (int i = 0; i < 32; i += 2) {
-                int c0 = orc_round_rtne((float)ldexp((double)y[i], -e), ORC_E2M1_FMT);
-                int c1 = orc_round_rtne((float)ldexp((double)y[i + 1], -e), ORC_E2M1_FMT);
-                vcodes[(int64_t)d * (ntok / 2) + (32 * g + i) / 2] = (uint8_t)(c0 | (c1 << 4));
-            }
+            vscales[(int64_t)d * (ntok / 32) + g] = mx_group(y, fp8, vcodes + (int64_t)d * vrow + g * (fp8 ? 32 : 16));
         }
 }
 
-/* Decode attention of one sequence: G query rows against its FP4 cache.
+/* Dequantized cache of one sequence: kh [len][D], vh [len][D] (binary64,
+ * exact), from the quantization above.  Returns 0, or -2 if out of memory. */
+static int dequantized_seq(const uint16_t *k, const uint16_t *v, int64_t tok_stride, int64_t len, int D, int rotate,
+                           int fp8, double *kh, double *vh)
+{
+    const int64_t ntok = (len + 31) / 32 * 32;
+    const int64_t krow = fp8 ? D : D / 2, vrow = fp8 ? ntok : ntok / 2;
+    uint8_t *kc = malloc((size_t)(ntok * krow)), *ks = malloc((size_t)(ntok * (D / 32)));
+    uint8_t *vc = malloc((size_t)(D * vrow)), *vs = malloc((size_t)(D * (ntok / 32)));
+    if (!kc || !ks || !vc || !vs) {
+        free(kc), free(ks), free(vc), free(vs);
+        return -2;
+    }
+    orc_kv_quantize_seq(k, v, tok_stride, len, ntok, D, rotate, fp8, kc, ks, vc, vs);
+    for (int64_t t = 0; t < len; ++t)
+        for (int d = 0; d < D; ++d) {
+            kh[t * D + d] = ldexp(code_value(kc + t * krow, d, fp8), (int)ks[t * (D / 32) + d / 32] - 127);
+            vh[t * D + d] = ldexp(code_value(vc + (int64_t)d * vrow, t, fp8), (int)vs[(int64_t)d * (ntok / 32) + t / 32] - 127);
+        }
+    free(kc), free(ks), free(vc), free(vs);
+    return 0;
+}
+
+/* Dequantized MXFP8 query row. */
+static void query_row(const uint16_t *q, int D, int rotate, double *qh)
+{
+    uint8_t qc[512], qs[16];
+    orc_q_quantize(q, D, rotate, qc, qs);
+    for (int d = 0; d < D; ++d) qh[d] = ldexp(e4m3_value(qc[d]), (int)qs[d / 32] - 127);
+}
+
+/* E4M3 value of p in a block with exponent e: E4M3(p 2^-e) 2^e. */
+static double deq_p(double p, int e)
+{
+    return ldexp((double)orc_e4m3_decode(orc_e4m3_encode_d(ldexp(p, -e))), e);
+}
+
+/* Decode attention of one sequence: G query rows against its KV cache (FP4,
+ * or the FP8 baseline with fp8 = 1).
  *   q [G][D] bf16; k, v as for orc_kv_quantize_seq; out [G][D] binary64.
- *   Q' = MXFP8(q), K' = MXFP4(k), V' = MXFP4(v) as above (dequantized exactly);
+ *   Q' = MXFP8(q), K', V' the dequantized cache (exact);
  *   s_t = <Q'_r, K'_t>, x_t = s_t sm_scale log2(e) for t < len;
  *   p_t = 2^(x_t - m) with m = ceil(max_t x_t) (any integer m gives the same
  *   output: the group scales below absorb the power of two);
  *   per 32-token group a = max p, E = floor(log2 a) - 7 (>= -127; a = 0 gives
  *   -127), p'_t = E4M3(p_t 2^-E) 2^E;
  *   out_r = sum_t p'_t V'_t / sum_t p_t.   len = 0 gives zeros.
- * Scratch comes from the caller, 8-byte aligned, for ntok = len rounded up
- * to 32 tokens: ntok * (8 + D/2 + D/32) + D * (ntok/2 + ntok/32) bytes. */
+ * Returns 0, -1 for a bad shape, -2 if out of memory. */
 int orc_kv_decode_seq(const uint16_t *q, int G, const uint16_t *k, const uint16_t *v, int64_t tok_stride, int64_t len,
-                      int D, float sm_scale, int rotate, uint8_t *ws, double *out)
+                      int D, float sm_scale, int rotate, int fp8, double *out)
 {
     if (D % 32 || D > 512 || G < 1) return -1;
     memset(out, 0, sizeof(double) * (size_t)G * (size_t)D);
     if (len <= 0) return 0;
     const int64_t ntok = (len + 31) / 32 * 32;
-    double *x = (double *)(void *)ws;
-    uint8_t *kc = ws + ntok * 8;
-    uint8_t *ks = kc + ntok * (D / 2);
-    uint8_t *vc = ks + ntok * (D / 32);
-    uint8_t *vs = vc + (int64_t)D * (ntok / 2);
-    orc_kv_quantize_seq(k, v, tok_stride, len, ntok, D, rotate, kc, ks, vc, vs);
+    double *kh = malloc(sizeof(double) * (size_t)(len * D)), *vh = malloc(sizeof(double) * (size_t)(len * D));
+    double *x = malloc(sizeof(double) * (size_t)len);
+    if (!kh || !vh || !x || dequantized_seq(k, v, tok_stride, len, D, rotate, fp8, kh, vh)) {
+        free(kh), free(vh), free(x);
+        return -2;
+    }
     const double c = (double)sm_scale / log(2.0);
     for (int r = 0; r < G; ++r) {
-        uint8_t qc[512], qs[16];
-        orc_q_quantize(q + (int64_t)r * D, D, rotate, qc, qs);
         double qh[512];
-        for (int d = 0; d < D; ++d) qh[d] = ldexp(e4m3_value(qc[d]), (int)qs[d / 32] - 127);
+        query_row(q + (int64_t)r * D, D, rotate, qh);
         double xmax = -INFINITY;
         for (int64_t t = 0; t < len; ++t) {
             double s = 0.0;
-            for (int d = 0; d < D; ++d) {
-                uint8_t byte = kc[t * (D / 2) + d / 2];
-                double kh = ldexp(e2m1_value((uint8_t)((d & 1) ? byte >> 4 : byte & 15)),
-                                  (int)ks[t * (D / 32) + d / 32] - 127);
-                s += qh[d] * kh;
-            }
+            for (int d = 0; d < D; ++d) s += qh[d] * kh[t * D + d];
             x[t] = s * c;
             xmax = fmax(xmax, x[t]);
         }
         const double m = ceil(xmax);
         double l = 0.0;
+        double *o = out + (int64_t)r * D;
         for (int64_t g = 0; g < ntok / 32; ++g) {
             double p[32], a = 0.0;
             for (int i = 0; i < 32; ++i) {
@@ -235,22 +285,18 @@ int orc_kv_decode_seq(const uint16_t *q, int G, const uint16_t *k, const uint16_
                 a = fmax(a, p[i]);
                 l += p[i];
             }
-            int e = orc_mx_exponent(a, 7);
+            const int e = orc_mx_exponent(a, 7);
             for (int i = 0; i < 32; ++i) {
                 int64_t t = 32 * g + i;
                 if (t >= len) continue;
-                double ph = ldexp((double)orc_e4m3_decode(orc_e4m3_encode_d(ldexp(p[i], -e))), e);
+                const double ph = deq_p(p[i], e);
                 if (ph == 0.0) continue;
-                for (int d = 0; d < D; ++d) {
-                    uint8_t byte = vc[(int64_t)d * (ntok / 2) + t / 2];
-                    double vh = ldexp(e2m1_value((uint8_t)((t & 1) ? byte >> 4 : byte & 15)),
-                                      (int)vs[(int64_t)d * (ntok / 32) + g] - 127);
-                    out[(int64_t)r * D + d] += ph * vh;
-                }
+                for (int d = 0; d < D; ++d) o[d] += ph * vh[t * D + d];
             }
         }
-        for (int d = 0; d < D; ++d) out[(int64_t)r * D + d] /= l;
+        for (int d = 0; d < D; ++d) o[d] /= l;
     }
+    free(kh), free(vh), free(x);
     return 0;
 }
 
@@ -268,14 +314,9 @@ int orc_kv_decode_seq(const uint16_t *q, int G, const uint16_t *k, const uint16_
  * with the relative perturbation of p_t taken as
  *   eps_t = c eps_s sum_d |Q'_d K'_td| + 2^-20 (|x_t| + 1)
  * (eps_s: accumulation error of a score relative to the sum of the
- * magnitudes of its products).  Scratch as for orc_kv_decode_seq. */
-static double deq_p(double p, int e)
-{
-    return ldexp((double)orc_e4m3_decode(orc_e4m3_encode_d(ldexp(p, -e))), e);
-}
-
+ * magnitudes of its products). */
 int orc_kv_decode_bounds(const uint16_t *q, int G, const uint16_t *k, const uint16_t *v, int64_t tok_stride,
-                         int64_t len, int D, float sm_scale, int rotate, double eps_s, uint8_t *ws, double *mass,
+                         int64_t len, int D, float sm_scale, int rotate, int fp8, double eps_s, double *mass,
                          double *amb, int64_t *fragile)
 {
     if (D % 32 || D > 512 || G < 1) return -1;
@@ -284,33 +325,31 @@ int orc_kv_decode_bounds(const uint16_t *q, int G, const uint16_t *k, const uint
     *fragile = 0;
     if (len <= 0) return 0;
     const int64_t ntok = (len + 31) / 32 * 32;
-    double *x = (double *)(void *)ws;
-    uint8_t *kc = ws + ntok * 8;
-    uint8_t *ks = kc + ntok * (D / 2);
-    uint8_t *vc = ks + ntok * (D / 32);
-    uint8_t *vs = vc + (int64_t)D * (ntok / 2);
-    orc_kv_quantize_seq(k, v, tok_stride, len, ntok, D, rotate, kc, ks, vc, vs);
+    double *kh = malloc(sizeof(double) * (size_t)(len * D)), *vh = malloc(sizeof(double) * (size_t)(len * D));
+    double *x = malloc(sizeof(double) * (size_t)len), *sabs = malloc(sizeof(double) * (size_t)len);
+    if (!kh || !vh || !x || !sabs || dequantized_seq(k, v, tok_stride, len, D, rotate, fp8, kh, vh)) {
+        free(kh), free(vh), free(x), free(sabs);
+        return -2;
+    }
     const double c = (double)sm_scale / log(2.0);
     for (int r = 0; r < G; ++r) {
-        uint8_t qc[512], qs[16];
-        orc_q_quantize(q + (int64_t)r * D, D, rotate, qc, qs);
         double qh[512];
-        for (int d = 0; d < D; ++d) qh[d] = ldexp(e4m3_value(qc[d]), (int)qs[d / 32] - 127);
-        /* x[t] holds the score, the perturbation goes to a second pass */
+        query_row(q + (int64_t)r * D, D, rotate, qh);
         double xmax = -INFINITY;
         for (int64_t t = 0; t < len; ++t) {
-            double s = 0.0;
+            double s = 0.0, sa = 0.0;
             for (int d = 0; d < D; ++d) {
-                uint8_t byte = kc[t * (D / 2) + d / 2];
-                s += qh[d] * ldexp(e2m1_value((uint8_t)((d & 1) ? byte >> 4 : byte & 15)),
-                                   (int)ks[t * (D / 32) + d / 32] - 127);
+                s += qh[d] * kh[t * D + d];
+                sa += fabs(qh[d] * kh[t * D + d]);
             }
             x[t] = s * c;
+            sabs[t] = sa;
             xmax = fmax(xmax, x[t]);
         }
         const double m = ceil(xmax);
         double l = 0.0, wsum = 0.0;
         for (int64_t t = 0; t < len; ++t) l += exp2(x[t] - m);
+        double *ms = mass + (int64_t)r * D, *am = amb + (int64_t)r * D;
         for (int64_t g = 0; g < ntok / 32; ++g) {
             double p[32], eps[32], a = 0.0, emax = 0.0;
             for (int i = 0; i < 32; ++i) {
@@ -318,14 +357,8 @@ int orc_kv_decode_bounds(const uint16_t *q, int G, const uint16_t *k, const uint
                 p[i] = 0.0;
                 eps[i] = 0.0;
                 if (t >= len) continue;
-                double sabs = 0.0;
-                for (int d = 0; d < D; ++d) {
-                    uint8_t byte = kc[t * (D / 2) + d / 2];
-                    sabs += fabs(qh[d] * ldexp(e2m1_value((uint8_t)((d & 1) ? byte >> 4 : byte & 15)),
-                                               (int)ks[t * (D / 32) + d / 32] - 127));
-                }
                 p[i] = exp2(x[t] - m);
-                eps[i] = c * eps_s * sabs + ldexp(fabs(x[t]) + 1.0, -20);
+                eps[i] = c * eps_s * sabs[t] + ldexp(fabs(x[t]) + 1.0, -20);
                 a = fmax(a, p[i]);
                 emax = fmax(emax, eps[i]);
             }
@@ -343,18 +376,17 @@ int orc_kv_decode_bounds(const uint16_t *q, int G, const uint16_t *k, const uint
                 }
                 /* a change within the perturbation itself is not a flip */
                 if (worst <= 2.0 * eps[i] * p[i]) worst = 0.0;
-                wsum += eps[i] * p[i];
                 if (worst > 0.0) ++*fragile;
+                wsum += eps[i] * p[i];
                 for (int d = 0; d < D; ++d) {
-                    uint8_t byte = vc[(int64_t)d * (ntok / 2) + t / 2];
-                    double vh = fabs(ldexp(e2m1_value((uint8_t)((t & 1) ? byte >> 4 : byte & 15)),
-                                           (int)vs[(int64_t)d * (ntok / 32) + g] - 127));
-                    mass[(int64_t)r * D + d] += ph * vh / l;
-                    amb[(int64_t)r * D + d] += worst * vh / l;
+                    const double va = fabs(vh[t * D + d]);
+                    ms[d] += ph * va / l;
+                    am[d] += worst * va / l;
                 }
             }
         }
-        for (int d = 0; d < D; ++d) amb[(int64_t)r * D + d] += mass[(int64_t)r * D + d] * wsum / l;
+        for (int d = 0; d < D; ++d) am[d] += ms[d] * wsum / l;
     }
+    free(kh), free(vh), free(x), free(sabs);
     return 0;
 }

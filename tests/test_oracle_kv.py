@@ -185,14 +185,16 @@ def test_k_quantize_rotated_integer_inputs():
 
 # ---- decode attention --------------------------------------------------------
 
-def dequant_seq(q, k, v, length, rotate):
+def dequant_seq(q, k, v, length, rotate, fmt="fp4"):
     """Dequantized operands from the (brute-force pinned) quantizers."""
     D = q.shape[1]
     ntok = (length + 31) // 32 * 32
     qc, qs = O.q_quantize(q, rotate)
     qh = e4m3_values(qc) * 2.0 ** (qs.astype(np.int64) - 127).repeat(32, axis=1)
-    kc, ks, vc, vs = O.kv_quantize_seq(k, v, length, ntok, rotate)
+    kc, ks, vc, vs = O.kv_quantize_seq(k, v, length, ntok, rotate, fmt)
     def nib(codes):
+        if fmt == "fp8":
+            return e4m3_values(codes)
         n = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
         return np.where(n & 8, -1.0, 1.0) * E2M1[n & 7]
     kh = nib(kc) * 2.0 ** (ks.astype(np.int64) - 127).repeat(32, axis=1)
@@ -232,8 +234,9 @@ def test_decode_dominant_key_returns_its_value():
     assert abs(ratio - 1) <= 2.0 ** -4
 
 
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
 @pytest.mark.parametrize("rotate", [False, True])
-def test_decode_within_fp8_probability_bound(rotate):
+def test_decode_within_fp8_probability_bound(rotate, fmt):
     """The output differs from a plain numpy softmax over the dequantized
     operands only by the E4M3 rounding of the probabilities: per token at
     most 2^-4 p (normal range) or 2^(E-10) (subnormal range, E the group's
@@ -241,8 +244,8 @@ def test_decode_within_fp8_probability_bound(rotate):
     G, D, L, length, sm = 8, 128, 1000, 931, 1 / math.sqrt(128)
     q = S.kv_q(1, G, D, seed=8)[0]
     k, v = S.kv_seq(0, 0, L, D, seed=8)
-    out = O.kv_decode_seq(q, k, v, length, sm, rotate)
-    qh, kh, vh = dequant_seq(q, k, v, length, rotate)
+    out = O.kv_decode_seq(q, k, v, length, sm, rotate, fmt)
+    qh, kh, vh = dequant_seq(q, k, v, length, rotate, fmt)
     s = qh @ kh.T * sm
     p = np.exp(s - s.max(axis=1, keepdims=True))
     ref = p @ vh / p.sum(axis=1, keepdims=True)
@@ -298,7 +301,8 @@ def test_rotation_helps_keys_with_outlier_channels():
     assert e_rot < e_raw
 
 
-def test_comparison_bound_covers_perturbed_scores():
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_comparison_bound_covers_perturbed_scores(fmt):
     """kv_decode_bounds: a decode whose scores are perturbed anywhere inside
     the allowed error (here in numpy, probabilities rounded by torch's E4M3
     cast) stays within 2e-4 mass + amb of the oracle, and the bound is zero
@@ -306,10 +310,10 @@ def test_comparison_bound_covers_perturbed_scores():
     G, D, L, length, sm = 4, 128, 1024, 1000, 1 / math.sqrt(128)
     q = S.kv_q(1, G, D, seed=12)[0]
     k, v = S.kv_seq(0, 0, L, D, seed=12)
-    want = O.kv_decode_seq(q, k, v, length, sm, True)
-    mass, amb, nfrag = O.kv_decode_bounds(q, k, v, length, sm, True, eps_s=2.0 ** -15)
+    want = O.kv_decode_seq(q, k, v, length, sm, True, fmt)
+    mass, amb, nfrag = O.kv_decode_bounds(q, k, v, length, sm, True, eps_s=2.0 ** -15, fmt=fmt)
     assert (amb >= 0).all() and (mass > 0).all() and nfrag > 0
-    qh, kh, vh = dequant_seq(q, k, v, length, True)
+    qh, kh, vh = dequant_seq(q, k, v, length, True, fmt)
     s = qh @ kh.T
     sabs = np.abs(qh) @ np.abs(kh).T
     c = sm / math.log(2)
@@ -326,5 +330,58 @@ def test_comparison_bound_covers_perturbed_scores():
         out = ph[:, :length] @ vh / p.sum(axis=1, keepdims=True)
         assert (np.abs(out - want) <= 2e-4 * mass + amb).all()
     # with no score error only the exponential's 2^-20 allowance remains
-    _, amb0, nf0 = O.kv_decode_bounds(q, k, v, length, sm, True, eps_s=0.0)
+    _, amb0, nf0 = O.kv_decode_bounds(q, k, v, length, sm, True, eps_s=0.0, fmt=fmt)
     assert nf0 < nfrag and amb0.max() < amb.max()
+
+
+# ---- the FP8 (MXFP8) cache baseline -------------------------------------------
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_fp8_cache_brute_force(rotate):
+    rng = np.random.default_rng(14)
+    L, D, length, ntok = 70, 128, 65, 96
+    k = rng.integers(-5, 6, (L, D)).astype(np.float32) if rotate else \
+        rng.standard_normal((L, D)) * 2.0 ** rng.integers(-8, 8, (L, 1))
+    v = rng.standard_normal((L, D)) * 2.0 ** rng.integers(-8, 8, (1, D))
+    v[3, :] = 1.9 * 2.0 ** 6            # group maxima in [448, 512) after scaling: saturation
+    kb, vb = bf16(k), bf16(v)
+    kc, ks, vc, vs = O.kv_quantize_seq(kb, vb, length, ntok, rotate, "fp8")
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    for t in range(ntok):
+        y = (S.bf16_bits_to_f32(kb[t]) if t < length else np.zeros(D, np.float32)).astype(np.float64)
+        c, sc = mxfp8_brute((H @ y if rotate else y).astype(np.float32))
+        np.testing.assert_array_equal(kc[t], c)
+        np.testing.assert_array_equal(ks[t], sc)
+    vf = np.zeros((ntok, D), np.float32)
+    vf[:length] = S.bf16_bits_to_f32(vb[:length])
+    for d in range(D):
+        c, sc = mxfp8_brute(vf[:, d])
+        np.testing.assert_array_equal(vc[d], c)
+        np.testing.assert_array_equal(vs[d], sc)
+    assert (vc[:, 3] & 0x7F == 0x7E).any()       # some saturated code
+
+
+def test_fp8_decode_zero_query_averages_v():
+    """Integers in [-8, 8] with an 8 in every 32-token group are exact in
+    MXFP8 (exponent -5, codes up to 256), so a zero query returns their mean."""
+    rng = np.random.default_rng(15)
+    G, D, L, length = 2, 128, 64, 61
+    v = rng.integers(-8, 9, (L, D)).astype(np.float64)
+    v[0::32, :] = 8.0
+    k = rng.standard_normal((L, D))
+    out = O.kv_decode_seq(np.zeros((G, D), np.uint16), bf16(k), bf16(v), length, 0.1, True, "fp8")
+    np.testing.assert_allclose(out, np.tile(v[:length].mean(axis=0), (G, 1)), rtol=0, atol=1e-15)
+
+
+def test_fp8_cache_is_closer_to_exact_attention():
+    G, D, L, sm = 8, 128, 2048, 1 / math.sqrt(128)
+    q = S.kv_q(1, G, D, seed=16)[0]
+    k, v = S.kv_seq(0, 0, L, D, seed=16)
+    qf, kf, vf = (S.bf16_bits_to_f32(t).astype(np.float64) for t in (q, k, v))
+    s = qf @ kf.T * sm
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    exact = p @ vf / p.sum(axis=1, keepdims=True)
+    e4 = np.linalg.norm(O.kv_decode_seq(q, k, v, L, sm, True, "fp4") - exact)
+    e8 = np.linalg.norm(O.kv_decode_seq(q, k, v, L, sm, True, "fp8") - exact)
+    assert e8 < e4 / 3
+

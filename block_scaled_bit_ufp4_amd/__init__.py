@@ -74,13 +74,14 @@ _lib.ufp4_strerror.restype = C.c_char_p
 _lib.ufp4_last_hip_error.restype = _i32
 _lib.ufp4_version.restype = _i32
 _lib.ufp4_time_next_launch.argtypes = [_p, _p]
-_lib.ufp4_kv_cache_bytes.argtypes = [_i64, _i64, _i64, _i64]
+_lib.ufp4_kv_cache_bytes.argtypes = [_i64, _i64, _i64, _i64, _i32]
 _lib.ufp4_kv_cache_bytes.restype = _sz
-_lib.ufp4_kv_cache_quantize.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _i32, _p, _p]
+_lib.ufp4_kv_cache_quantize.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _i64, _i64, _p, _i32, _p, _p]
 _lib.ufp4_kv_q_quantize.argtypes = [_p, _i64, _i64, _i32, _p, _p, _p]
 _lib.ufp4_kv_decode_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64]
 _lib.ufp4_kv_decode_workspace_size.restype = _sz
-_lib.ufp4_kv_decode.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, C.c_float, _i32, _i64, _p, _p, _sz, _p]
+_lib.ufp4_kv_decode.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, C.c_float, _i32, _i64, _p, _p, _sz,
+                                _p]
 
 EXPORTS = ["ufp4_rht", "ufp4_amax", "ufp4_quantize", "ufp4_dequantize", "ufp4_stats", "ufp4_stats_finalize",
            "ufp4_qgemm", "ufp4_gemm_bf16", "ufp4_eta", "ufp4_workspace_size", "ufp4_strerror",
@@ -333,25 +334,27 @@ def ufp4_time_next_launch(start=None, stop=None) -> None:
 # ---- FP4 KV cache and decode attention -------------------------------------
 
 KV_PAGE_TOKENS = 128
-KV_PAGE_BYTES = 17408
+KV_FORMATS = {"fp4": 0, "fp8": 1}
+KV_PAGE_BYTES = {"fp4": 17408, "fp8": 33792}
 
 
-def ufp4_kv_cache_bytes(B: int, Hkv: int, L_cap: int, D: int = 128) -> int:
-    return int(_lib.ufp4_kv_cache_bytes(B, Hkv, L_cap, D))
+def ufp4_kv_cache_bytes(B: int, Hkv: int, L_cap: int, D: int = 128, fmt: str = "fp4") -> int:
+    return int(_lib.ufp4_kv_cache_bytes(B, Hkv, L_cap, D, KV_FORMATS[fmt]))
 
 
 def ufp4_kv_cache_quantize(k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor, rotate: bool = True,
-                           cache: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                           cache: Optional[torch.Tensor] = None, stream=None, fmt: str = "fp4") -> torch.Tensor:
     """k, v: bf16 [B][Hkv][L_cap][128] views with unit channel stride (any
-    batch/head/token strides); lens: int32 [B] on the device.  Returns the
-    uint8 cache (ufp4_kv_cache_bytes)."""
+    batch/head/token strides); lens: int32 [B] on the device; fmt "fp4" or
+    the "fp8" baseline.  Returns the uint8 cache (ufp4_kv_cache_bytes)."""
     B, Hkv, L_cap, D = k.shape
     if v.shape != k.shape or v.stride() != k.stride() or k.stride(3) != 1:
         raise ValueError("k and v must have the same shape and strides, channels contiguous")
     if cache is None:
-        cache = torch.empty(max(1, ufp4_kv_cache_bytes(B, Hkv, L_cap, D)), dtype=torch.uint8, device=k.device)
-    rc = _lib.ufp4_kv_cache_quantize(k.data_ptr(), v.data_ptr(), B, Hkv, L_cap, D, k.stride(0), k.stride(1),
-                                     k.stride(2), lens.data_ptr(), int(rotate), cache.data_ptr(), _stream(stream))
+        cache = torch.empty(max(1, ufp4_kv_cache_bytes(B, Hkv, L_cap, D, fmt)), dtype=torch.uint8, device=k.device)
+    rc = _lib.ufp4_kv_cache_quantize(k.data_ptr(), v.data_ptr(), B, Hkv, L_cap, D, KV_FORMATS[fmt], k.stride(0),
+                                     k.stride(1), k.stride(2), lens.data_ptr(), int(rotate), cache.data_ptr(),
+                                     _stream(stream))
     _check(rc, "ufp4_kv_cache_quantize")
     return cache
 
@@ -375,17 +378,20 @@ def ufp4_kv_decode_workspace_size(B: int, Hq: int, Hkv: int, L_cap: int, pages_p
 
 def ufp4_kv_decode(q: torch.Tensor, cache: torch.Tensor, lens: torch.Tensor, Hkv: int, L_cap: int,
                    sm_scale: float, rotate: bool = True, pages_per_split: int = 0,
-                   out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One decode step: q bf16 [B][Hq][128] contiguous -> fp32 [B][Hq][128]."""
+                   out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None,
+                   fmt: str = "fp4") -> torch.Tensor:
+    """One decode step: q bf16 [B][Hq][128] contiguous -> fp32 [B][Hq][128],
+    against a cache of format fmt ("fp4", or the "fp8" baseline)."""
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     need = ufp4_kv_decode_workspace_size(B, Hq, Hkv, L_cap, pages_per_split, D)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    rc = _lib.ufp4_kv_decode(q.data_ptr(), cache.data_ptr(), lens.data_ptr(), B, Hq, Hkv, D, L_cap, float(sm_scale),
-                             int(rotate), pages_per_split, out.data_ptr(), ws.data_ptr() if ws is not None else None,
-                             ws.numel() if ws is not None else 0, _stream(stream))
+    rc = _lib.ufp4_kv_decode(q.data_ptr(), cache.data_ptr(), lens.data_ptr(), B, Hq, Hkv, D, KV_FORMATS[fmt], L_cap,
+                             float(sm_scale), int(rotate), pages_per_split, out.data_ptr(),
+                             ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                             _stream(stream))
     _check(rc, "ufp4_kv_decode")
     return out
 

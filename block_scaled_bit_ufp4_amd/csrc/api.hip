@@ -389,7 +389,13 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
 // ---- FP4 KV cache ------------------------------------------------------
 
 static constexpr int64_t KV_PAGE_TOKENS = 128;
-static constexpr int64_t KV_PAGE_BYTES = 17408;
+static constexpr int64_t KV_WAVES_PER_WG = 8;  // a decode wave prefetches one page past its last
+
+// Bytes of a 128-token page: FP4 or the FP8 baseline (0 for an unknown format).
+static int64_t kv_page_bytes(int kv_format)
+{
+    return kv_format == UFP4_KV_FP4 ? 17408 : kv_format == UFP4_KV_FP8 ? 33792 : 0;
+}
 
 // Pages per split of a decode: requested, or about 256 workgroups in all
 // (one 8-wave workgroup per compute unit, all resident at once) with at least
@@ -412,31 +418,33 @@ static int kv_check_heads(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t
     if (Hq % Hkv) return UFP4_ERR_SHAPE;
     if (Hq / Hkv > 16) return UFP4_ERR_UNSUPPORTED;
     if (L_cap % KV_PAGE_TOKENS) return UFP4_ERR_SHAPE;
-    // one sequence's pages are addressed with 32-bit buffer offsets
-    if ((L_cap / KV_PAGE_TOKENS + 4) * KV_PAGE_BYTES > INT32_MAX) return UFP4_ERR_SHAPE;
+    // one sequence's pages (of either format) are addressed with 32-bit
+    // buffer offsets
+    if ((L_cap / KV_PAGE_TOKENS + KV_WAVES_PER_WG) * kv_page_bytes(UFP4_KV_FP8) > INT32_MAX) return UFP4_ERR_SHAPE;
     return UFP4_OK;
 }
 
-size_t ufp4_kv_cache_bytes(int64_t B, int64_t Hkv, int64_t L_cap, int64_t D)
+size_t ufp4_kv_cache_bytes(int64_t B, int64_t Hkv, int64_t L_cap, int64_t D, int kv_format)
 {
-    if (B < 0 || Hkv < 1 || D != 128 || L_cap < 1 || L_cap % KV_PAGE_TOKENS) return 0;
-    return (size_t)(B * Hkv * (L_cap / KV_PAGE_TOKENS) * KV_PAGE_BYTES);
+    if (kv_check_heads(B, Hkv, Hkv, D, L_cap) || !kv_page_bytes(kv_format)) return 0;
+    return (size_t)(B * Hkv * (L_cap / KV_PAGE_TOKENS) * kv_page_bytes(kv_format));
 }
 
 int ufp4_kv_cache_quantize(const void *k, const void *v, int64_t B, int64_t Hkv, int64_t L_cap, int64_t D,
-                           int64_t stride_b, int64_t stride_h, int64_t stride_t, const int32_t *lens, int rotate_k,
-                           uint8_t *cache, void *stream)
+                           int kv_format, int64_t stride_b, int64_t stride_h, int64_t stride_t, const int32_t *lens,
+                           int rotate_k, uint8_t *cache, void *stream)
 {
     int rc = kv_check_heads(B, Hkv, Hkv, D, L_cap);
     if (rc) return rc;
-    if (rotate_k != 0 && rotate_k != 1) return UFP4_ERR_INVALID_ARG;
+    if ((rotate_k != 0 && rotate_k != 1) || !kv_page_bytes(kv_format)) return UFP4_ERR_INVALID_ARG;
     if (B == 0) return UFP4_OK;
     if (!k || !v || !lens || !cache) return UFP4_ERR_INVALID_ARG;
     if (stride_t < D || stride_b < 0 || stride_h < 0 || B > 65535 || Hkv > 65535) return UFP4_ERR_SHAPE;
     if (!aligned16(k) || !aligned16(v) || !aligned16(cache) || stride_b % 8 || stride_h % 8 || stride_t % 8)
         return UFP4_ERR_ALIGN;
     return hip_fail(launch_kv_quantize(static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), B, Hkv, L_cap,
-                                       stride_b, stride_h, stride_t, lens, rotate_k, cache, (hipStream_t)stream));
+                                       kv_format == UFP4_KV_FP8, stride_b, stride_h, stride_t, lens, rotate_k, cache,
+                                       (hipStream_t)stream));
 }
 
 int ufp4_kv_q_quantize(const void *q, int64_t rows, int64_t D, int rotate, uint8_t *codes, uint8_t *scales,
@@ -464,12 +472,12 @@ size_t ufp4_kv_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t
 }
 
 int ufp4_kv_decode(const void *q, const uint8_t *cache, const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
-                   int64_t D, int64_t L_cap, float sm_scale, int rotate, int64_t pages_per_split, float *out, void *ws,
-                   size_t ws_bytes, void *stream)
+                   int64_t D, int kv_format, int64_t L_cap, float sm_scale, int rotate, int64_t pages_per_split,
+                   float *out, void *ws, size_t ws_bytes, void *stream)
 {
     int rc = kv_check_heads(B, Hq, Hkv, D, L_cap);
     if (rc) return rc;
-    if (rotate != 0 && rotate != 1) return UFP4_ERR_INVALID_ARG;
+    if ((rotate != 0 && rotate != 1) || !kv_page_bytes(kv_format)) return UFP4_ERR_INVALID_ARG;
     if (!(fabsf(sm_scale) <= 3.0e38f) || pages_per_split < 0) return UFP4_ERR_INVALID_ARG;
     if (B == 0) return UFP4_OK;
     if (!q || !cache || !lens || !out) return UFP4_ERR_INVALID_ARG;
@@ -488,8 +496,9 @@ int ufp4_kv_decode(const void *q, const uint8_t *cache, const int32_t *lens, int
     }
     // log2(e) folded into the score scale, rounded once to binary32
     const float c = (float)((double)sm_scale * 1.4426950408889634074);
-    return hip_fail(launch_kv_decode(static_cast<const uint16_t *>(q), cache, lens, B, Hkv, (int)(Hq / Hkv), L_cap, c,
-                                     rotate, (int)pps, (int)nsplit, out, ws_o, ws_ml, (hipStream_t)stream));
+    return hip_fail(launch_kv_decode(static_cast<const uint16_t *>(q), cache, lens, B, Hkv, (int)(Hq / Hkv),
+                                     kv_format == UFP4_KV_FP8, L_cap, c, rotate, (int)pps, (int)nsplit, out, ws_o,
+                                     ws_ml, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -116,13 +116,14 @@ hipError_t launch_eta(const float *zq, const float *z, int64_t M, int64_t N, int
 // GEMMs: C[M][ldc] = A B^T.
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t M, int64_t N, int64_t K, int64_t lda,
                             int64_t ldb, float *c, int64_t ldc, hipStream_t st);
-// FP4 KV cache and decode attention (head dim 128).
-hipError_t launch_kv_quantize(const uint16_t *k, const uint16_t *v, int64_t B, int64_t Hkv, int64_t L_cap, int64_t sb,
-                              int64_t sh, int64_t st, const int32_t *lens, int rotate, uint8_t *cache, hipStream_t s);
+// FP4 KV cache (or the FP8 baseline, fp8 = 1) and decode attention (head dim 128).
+hipError_t launch_kv_quantize(const uint16_t *k, const uint16_t *v, int64_t B, int64_t Hkv, int64_t L_cap, int fp8,
+                              int64_t sb, int64_t sh, int64_t st, const int32_t *lens, int rotate, uint8_t *cache,
+                              hipStream_t s);
 hipError_t launch_q_quantize(const uint16_t *q, int64_t rows, int rotate, uint8_t *codes, uint8_t *scales,
                              hipStream_t s);
 hipError_t launch_kv_decode(const uint16_t *q, const uint8_t *cache, const int32_t *lens, int64_t B, int64_t Hkv, int G,
-                            int64_t L_cap, float c, int rotate, int pps, int nsplit, float *out, float *ws_o,
+                            int fp8, int64_t L_cap, float c, int rotate, int pps, int nsplit, float *out, float *ws_o,
                             float *ws_ml, hipStream_t s);
 
 hipError_t launch_gemm_mxfp4(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb, int64_t M,

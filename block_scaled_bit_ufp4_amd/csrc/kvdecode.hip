@@ -51,6 +51,12 @@ constexpr int KV_K_SCALES = 8192;
 constexpr int KV_V_CODES = 8704;
 constexpr int KV_V_SCALES = 16896;
 constexpr int KV_PAGE_BYTES = 17408;
+// FP8 (MXFP8) baseline page: the same operands with 32-byte E4M3 lanes.
+constexpr int KV8_K_CODES = 0;
+constexpr int KV8_K_SCALES = 16384;
+constexpr int KV8_V_CODES = 16896;
+constexpr int KV8_V_SCALES = 33280;
+constexpr int KV8_PAGE_BYTES = 33792;
 constexpr int KV_NT = 2;     // cache-policy bits of a buffer load: non-temporal
 constexpr int KV_WAVES = 8;  // waves of a decode workgroup (pages are dealt out round-robin)
 
@@ -171,6 +177,23 @@ __device__ __forceinline__ void q_chunk(const uint16_t *q_rows, int G, int rotat
     }
 }
 
+// FP8 A-operand order: lane (rho, g) holds K positions 16g .. 16g+15 and
+// 64 + 16g .. 64 + 16g + 15.  cw holds this lane's 32 codes in contiguous
+// order (positions 32c .. 32c+31 for c = lane / 16); the result gathers the
+// two 16-byte halves from lanes (rho, g / 2) and (rho, 2 + g / 2).
+__device__ __forceinline__ void fp8_operand_order(const uint32_t *cw, int lane, uint32_t *out)
+{
+    const int g = lane >> 4, h = g & 1;
+    const int src1 = (lane & 15) + 16 * (g >> 1), src2 = src1 + 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a0 = (uint32_t)__shfl((int)cw[i], src1), a1 = (uint32_t)__shfl((int)cw[4 + i], src1);
+        const uint32_t b0 = (uint32_t)__shfl((int)cw[i], src2), b1 = (uint32_t)__shfl((int)cw[4 + i], src2);
+        out[i] = h ? a1 : a0;
+        out[4 + i] = h ? b1 : b0;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Cache quantizer: one wave per 128-token page.
 // ---------------------------------------------------------------------------
@@ -183,14 +206,16 @@ struct KvQuantArgs {
     uint8_t *cache;
 };
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
 {
+    constexpr int PB = FP8 ? KV8_PAGE_BYTES : KV_PAGE_BYTES;
     const int lane = threadIdx.x & 63;
     const int64_t page = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t h = blockIdx.y, b = blockIdx.z;
     const int64_t len = min((int64_t)max(a.lens[b], 0), a.L_cap);
     if (page >= a.npages || page * KV_PAGE >= len) return;
-    uint8_t *out = a.cache + ((b * a.Hkv + h) * a.npages + page) * KV_PAGE_BYTES;
+    uint8_t *out = a.cache + ((b * a.Hkv + h) * a.npages + page) * PB;
     const int64_t t0 = page * KV_PAGE;
 
     // K: score-MFMA order, one 32-channel group per lane and instruction.
@@ -209,14 +234,25 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
                 for (int i = 0; i < 32; ++i) y[i] = 0.0f;
             }
             if (a.rotate) wht128(y, lane);
-            const int e = mx_exp(absmax32(y), 2);
-            const float inv = pow2_neg(e);
+            uint32_t eb;
+            if constexpr (FP8) {
+                uint32_t cw[8], ow[8];
+                eb = q_codes32(y, cw);
+                fp8_operand_order(cw, lane, ow);
+                uint4 *dst = reinterpret_cast<uint4 *>(out + KV8_K_CODES + j * 2048 + lane * 32);
+                dst[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                dst[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+            } else {
+                const int e = mx_exp(absmax32(y), 2);
+                const float inv = pow2_neg(e);
 #pragma unroll
-            for (int i = 0; i < 32; ++i) y[i] = y[i] * inv;
-            *reinterpret_cast<uint4 *>(out + KV_K_CODES + j * 1024 + lane * 16) = pack32_e2m1(y);
-            sc[j >> 2] |= (uint32_t)(e + 127) << (8 * (j & 3));
+                for (int i = 0; i < 32; ++i) y[i] = y[i] * inv;
+                *reinterpret_cast<uint4 *>(out + KV_K_CODES + j * 1024 + lane * 16) = pack32_e2m1(y);
+                eb = (uint32_t)(e + 127);
+            }
+            sc[j >> 2] |= eb << (8 * (j & 3));
         }
-        *reinterpret_cast<uint2 *>(out + KV_K_SCALES + lane * 8) = make_uint2(sc[0], sc[1]);
+        *reinterpret_cast<uint2 *>(out + (FP8 ? KV8_K_SCALES : KV_K_SCALES) + lane * 8) = make_uint2(sc[0], sc[1]);
     }
     // V: lane (rho, g) holds channels 8 rho .. 8 rho + 7 of tokens 32g .. 32g+31.
     {
@@ -237,14 +273,25 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
                 const uint32_t w = n < 2 ? raw[u].x : n < 4 ? raw[u].y : n < 6 ? raw[u].z : raw[u].w;
                 y[u] = (n & 1) ? bf16hi(w) : bf16lo(w);
             }
-            const int e = mx_exp(absmax32(y), 2);
-            const float inv = pow2_neg(e);
+            uint32_t eb;
+            if constexpr (FP8) {
+                uint32_t cw[8], ow[8];
+                eb = q_codes32(y, cw);
+                fp8_operand_order(cw, lane, ow);
+                uint4 *dst = reinterpret_cast<uint4 *>(out + KV8_V_CODES + n * 2048 + lane * 32);
+                dst[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                dst[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+            } else {
+                const int e = mx_exp(absmax32(y), 2);
+                const float inv = pow2_neg(e);
 #pragma unroll
-            for (int u = 0; u < 32; ++u) y[u] = y[u] * inv;
-            *reinterpret_cast<uint4 *>(out + KV_V_CODES + n * 1024 + lane * 16) = pack32_e2m1(y);
-            sc[n >> 2] |= (uint32_t)(e + 127) << (8 * (n & 3));
+                for (int u = 0; u < 32; ++u) y[u] = y[u] * inv;
+                *reinterpret_cast<uint4 *>(out + KV_V_CODES + n * 1024 + lane * 16) = pack32_e2m1(y);
+                eb = (uint32_t)(e + 127);
+            }
+            sc[n >> 2] |= eb << (8 * (n & 3));
         }
-        *reinterpret_cast<uint2 *>(out + KV_V_SCALES + lane * 8) = make_uint2(sc[0], sc[1]);
+        *reinterpret_cast<uint2 *>(out + (FP8 ? KV8_V_SCALES : KV_V_SCALES) + lane * 8) = make_uint2(sc[0], sc[1]);
     }
 }
 
@@ -285,7 +332,19 @@ struct KvDecodeArgs {
     float *ws_ml;           // [B][Hkv][nsplit][G][2]  (integer max m, sum l)
 };
 
-__device__ __forceinline__ v4f mfma_fp4_fp8(v4u a, const v8i &b, v4f acc, int sel_a, int scale_a, int scale_b)
+// Scaled MFMA with an FP4 (16-byte) or FP8 (32-byte) A operand and an FP8 B
+// operand; sel_a picks the byte of scale_a.
+__device__ __forceinline__ v4f mfma_kv(const v8i &a, const v8i &b, v4f acc, int sel_a, int scale_a, int scale_b)
+{
+    switch (sel_a) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, scale_a, 0, scale_b);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 1, scale_a, 0, scale_b);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 2, scale_a, 0, scale_b);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 3, scale_a, 0, scale_b);
+    }
+}
+
+__device__ __forceinline__ v4f mfma_kv(v4u a, const v8i &b, v4f acc, int sel_a, int scale_a, int scale_b)
 {
     const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
     switch (sel_a) {
@@ -321,6 +380,35 @@ __device__ __forceinline__ void load_page(__amdgpu_buffer_rsrc_t rs, int64_t p, 
     P.vs = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + KV_V_SCALES, KV_NT);
 }
 
+// One FP8 page: the K operands, then the V operands, each loaded in one go.
+struct PageRegs8 {
+    v8i kc[8], vc[8];
+    v2u ks, vs;
+};
+
+__device__ __forceinline__ v8i load32(__amdgpu_buffer_rsrc_t rs, uint32_t v, int s)
+{
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(rs, v, s, KV_NT);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rs, v + 16, s, KV_NT);
+    return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ void load_k8(__amdgpu_buffer_rsrc_t rs, int64_t p, uint32_t v32, uint32_t v8, PageRegs8 &P)
+{
+    const int sp = __builtin_amdgcn_readfirstlane((int)(p * KV8_PAGE_BYTES));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) P.kc[j] = load32(rs, v32 + (j & 1) * 2048, sp + KV8_K_CODES + (j >> 1) * 4096);
+    P.ks = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + KV8_K_SCALES, KV_NT);
+}
+
+__device__ __forceinline__ void load_v8(__amdgpu_buffer_rsrc_t rs, int64_t p, uint32_t v32, uint32_t v8, PageRegs8 &P)
+{
+    const int sp = __builtin_amdgcn_readfirstlane((int)(p * KV8_PAGE_BYTES));
+#pragma unroll
+    for (int n = 0; n < 8; ++n) P.vc[n] = load32(rs, v32 + (n & 1) * 2048, sp + KV8_V_CODES + (n >> 1) * 4096);
+    P.vs = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + KV8_V_SCALES, KV_NT);
+}
+
 // Running softmax state of one wave: integer running maximum, the lane's
 // share of the normaliser, and the output accumulators (lane (r, g): O[n][i]
 // is channel 32g + 8i + n of query row r).
@@ -329,18 +417,17 @@ struct DecodeState {
     v4f O[8];
 };
 
-// One page: scores on the MFMA, softmax update, E4M3 probabilities, P V.
-__device__ __forceinline__ void process_page(const PageRegs &P, const v8i &qb, int qs, int64_t p, int64_t len,
-                                             float c, int g, DecodeState &st)
+// Scores of a page, x[j][i] for token page_token(j, 4g + i) (masked past the
+// length), and their maximum in this lane.
+template <typename KOp>
+__device__ __forceinline__ float page_scores(const KOp *kc, v2u ks, const v8i &qb, int qs, int64_t p, int64_t len,
+                                             float c, int g, float (&x)[8][4])
 {
-    // scores of the page: x[j][i] for token page_token(j, 4g + i)
-    float x[8][4];
     float mloc = -INFINITY;
     const int64_t tbase = p * KV_PAGE + 16 * g;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const v4f s =
-            mfma_fp4_fp8(P.kc[j], qb, (v4f){0.0f, 0.0f, 0.0f, 0.0f}, j & 3, (int)(j < 4 ? P.ks.x : P.ks.y), qs);
+        const v4f s = mfma_kv(kc[j], qb, (v4f){0.0f, 0.0f, 0.0f, 0.0f}, j & 3, (int)(j < 4 ? ks.x : ks.y), qs);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t t = tbase + 64 * (j >> 2) + 4 * (j & 3) + i;
@@ -348,6 +435,13 @@ __device__ __forceinline__ void process_page(const PageRegs &P, const v8i &qb, i
             mloc = fmaxf(mloc, x[j][i]);
         }
     }
+    return mloc;
+}
+
+// Softmax update of one page and its E4M3 probabilities: the operand pb and
+// the biased exponent ps this lane supplies.
+__device__ __forceinline__ void page_softmax(float (&x)[8][4], float mloc, int g, DecodeState &st, v8i &pb, int &ps)
+{
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float m_new = fmaxf(st.m_run, ceilf(mloc));
@@ -376,7 +470,6 @@ __device__ __forceinline__ void process_page(const PageRegs &P, const v8i &qb, i
     a2 = fmaxf(a2, __shfl_xor(a2, 16));
     const int e1 = mx_exp(a1, 7), e2 = mx_exp(a2, 7);
     const float inv1 = pow2_neg(e1), inv2 = pow2_neg(e2);
-    v8i pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float inv = j < 4 ? inv1 : inv2;
@@ -387,14 +480,33 @@ __device__ __forceinline__ void process_page(const PageRegs &P, const v8i &qb, i
     const int recv = __shfl_xor(g >= 2 ? e1 : e2, 32);
     const int keep = g == 0 ? e1 : e2;
     const int swap = -(int)((unsigned)(g - 1) < 2u);
-    const int ps = ((recv & swap) | (keep & ~swap)) + 127;
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-        st.O[n] = mfma_fp4_fp8(P.vc[n], pb, st.O[n], n & 3, (int)(n < 4 ? P.vs.x : P.vs.y), ps);
+    ps = ((recv & swap) | (keep & ~swap)) + 127;
 }
 
+// O += V^T P^T for one page.
+template <typename VOp>
+__device__ __forceinline__ void page_pv(const VOp *vc, v2u vs, const v8i &pb, int ps, DecodeState &st)
+{
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.O[n] = mfma_kv(vc[n], pb, st.O[n], n & 3, (int)(n < 4 ? vs.x : vs.y), ps);
+}
+
+// One FP4 page: scores on the MFMA, softmax update, E4M3 probabilities, P V.
+__device__ __forceinline__ void process_page(const PageRegs &P, const v8i &qb, int qs, int64_t p, int64_t len,
+                                             float c, int g, DecodeState &st)
+{
+    float x[8][4];
+    const float mloc = page_scores(P.kc, P.ks, qb, qs, p, len, c, g, x);
+    v8i pb;
+    int ps;
+    page_softmax(x, mloc, g, st, pb, ps);
+    page_pv(P.vc, P.vs, pb, ps, st);
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void kv_decode_kernel(KvDecodeArgs a)
 {
+    constexpr int PB = FP8 ? KV8_PAGE_BYTES : KV_PAGE_BYTES;
     __shared__ __attribute__((aligned(16))) uint8_t q_lds[16 * KV_D + 64];
     __shared__ float o_lds[KV_WAVES][16][KV_D];
     __shared__ float ml_lds[KV_WAVES][16][2];
@@ -410,14 +522,24 @@ __global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2
     const int64_t npg = (len + KV_PAGE - 1) / KV_PAGE;
     const int64_t p0 = (int64_t)split * a.pps;
     const int64_t p1 = max(p0, min(p0 + a.pps, npg));
-    const uint8_t *seq = a.cache + (b * a.Hkv + h) * a.npages * KV_PAGE_BYTES;
+    const uint8_t *seq = a.cache + (b * a.Hkv + h) * a.npages * PB;
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(seq), (short)0, (int)(p1 * KV_PAGE_BYTES), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(seq), (short)0, (int)(p1 * PB), 0x00020000);
 
     int64_t p = p0 + wave;
+    const uint32_t v16 = (uint32_t)lane * 16u, v8 = (uint32_t)lane * 8u, v32 = (uint32_t)lane * 32u;
     PageRegs cur;
-    const uint32_t v16 = (uint32_t)lane * 16u, v8 = (uint32_t)lane * 8u;
-    load_page(rs, p, v16, v8, cur);
+    PageRegs8 cur8;
+    if constexpr (FP8) {
+        // same order as in the loop (keys with their scales, then values), so
+        // the loop's waits count the same outstanding loads on every entry
+        load_k8(rs, p, v32, v8, cur8);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v8(rs, p, v32, v8, cur8);
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        load_page(rs, p, v16, v8, cur);
+    }
 
     // Query operand: wave 0 quantizes (contiguous chunks), all waves read it
     // back in the B-operand order.
@@ -446,19 +568,40 @@ __global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.O[n] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Two register sets in turn: the next page's loads are issued before the
-    // current page is processed, and no copy between the sets waits on them.
-    PageRegs nxt;
-    while (p < p1) {
-        load_page(rs, p + KV_WAVES, v16, v8, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        process_page(cur, qb, qs, p, len, a.c, g, st);
-        p += KV_WAVES;
-        if (p >= p1) break;
-        load_page(rs, p + KV_WAVES, v16, v8, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        process_page(nxt, qb, qs, p, len, a.c, g, st);
-        p += KV_WAVES;
+    if constexpr (FP8) {
+        // One register set: the next page's keys load once the score MFMAs
+        // have read the current ones, its values once P V has.
+        while (p < p1) {
+            float x[8][4];
+            const float mloc = page_scores(cur8.kc, cur8.ks, qb, qs, p, len, a.c, g, x);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k8(rs, p + KV_WAVES, v32, v8, cur8);
+            __builtin_amdgcn_sched_barrier(0);
+            v8i pb;
+            int ps;
+            page_softmax(x, mloc, g, st, pb, ps);
+            page_pv(cur8.vc, cur8.vs, pb, ps, st);
+            __builtin_amdgcn_sched_barrier(0);
+            load_v8(rs, p + KV_WAVES, v32, v8, cur8);
+            __builtin_amdgcn_sched_barrier(0);
+            p += KV_WAVES;
+        }
+    } else {
+        // Two register sets in turn: the next page's loads are issued before
+        // the current page is processed, and no copy between the sets waits
+        // on them.
+        PageRegs nxt;
+        while (p < p1) {
+            load_page(rs, p + KV_WAVES, v16, v8, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            process_page(cur, qb, qs, p, len, a.c, g, st);
+            p += KV_WAVES;
+            if (p >= p1) break;
+            load_page(rs, p + KV_WAVES, v16, v8, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            process_page(nxt, qb, qs, p, len, a.c, g, st);
+            p += KV_WAVES;
+        }
     }
     const float m_run = st.m_run, l_lane = st.l_lane;
     v4f O[8];
@@ -535,12 +678,16 @@ __global__ __launch_bounds__(128) void kv_combine_kernel(KvDecodeArgs a)
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_kv_quantize(const uint16_t *k, const uint16_t *v, int64_t B, int64_t Hkv, int64_t L_cap, int64_t sb,
-                              int64_t sh, int64_t st, const int32_t *lens, int rotate, uint8_t *cache, hipStream_t s)
+hipError_t launch_kv_quantize(const uint16_t *k, const uint16_t *v, int64_t B, int64_t Hkv, int64_t L_cap, int fp8,
+                              int64_t sb, int64_t sh, int64_t st, const int32_t *lens, int rotate, uint8_t *cache,
+                              hipStream_t s)
 {
     KvQuantArgs a{k, v, sb, sh, st, lens, Hkv, L_cap, L_cap / KV_PAGE, rotate, cache};
     const dim3 grid((unsigned)((a.npages + 3) / 4), (unsigned)Hkv, (unsigned)B);
-    launch_kernel(kv_quantize_kernel, grid, dim3(256), s, a);
+    if (fp8)
+        launch_kernel(kv_quantize_kernel<true>, grid, dim3(256), s, a);
+    else
+        launch_kernel(kv_quantize_kernel<false>, grid, dim3(256), s, a);
     return hipGetLastError();
 }
 
@@ -551,11 +698,15 @@ hipError_t launch_q_quantize(const uint16_t *q, int64_t rows, int rotate, uint8_
 }
 
 hipError_t launch_kv_decode(const uint16_t *q, const uint8_t *cache, const int32_t *lens, int64_t B, int64_t Hkv, int G,
-                            int64_t L_cap, float c, int rotate, int pps, int nsplit, float *out, float *ws_o,
+                            int fp8, int64_t L_cap, float c, int rotate, int pps, int nsplit, float *out, float *ws_o,
                             float *ws_ml, hipStream_t s)
 {
     KvDecodeArgs a{q, cache, lens, Hkv, L_cap, L_cap / KV_PAGE, G, pps, nsplit, rotate, c, out, ws_o, ws_ml};
-    launch_kernel(kv_decode_kernel, dim3((unsigned)nsplit, (unsigned)Hkv, (unsigned)B), dim3(64 * KV_WAVES), s, a);
+    const dim3 grid((unsigned)nsplit, (unsigned)Hkv, (unsigned)B);
+    if (fp8)
+        launch_kernel(kv_decode_kernel<true>, grid, dim3(64 * KV_WAVES), s, a);
+    else
+        launch_kernel(kv_decode_kernel<false>, grid, dim3(64 * KV_WAVES), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     launch_kernel(kv_combine_kernel, dim3((unsigned)(B * Hkv * G)), dim3(128), s, a);

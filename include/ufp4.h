@@ -109,6 +109,7 @@ enum { UFP4_ROW = 0, UFP4_COL = 1 };
 enum { UFP4_BF16 = 0, UFP4_F32 = 1 };
 enum { UFP4_GEMM_NATIVE_MXFP4 = 0, UFP4_GEMM_DEQUANT_BF16 = 1 };
 enum { UFP4_OP_STATS = 0, UFP4_OP_QGEMM = 1, UFP4_OP_ETA = 2, UFP4_OP_AMAX = 3 };
+enum { UFP4_KV_FP4 = 0, UFP4_KV_FP8 = 1 }; /* KV-cache element format (see the KV section) */
 
 /* Supported combinations (anything else returns UFP4_ERR_UNSUPPORTED):
  *   E2M1 with FP32/16, E4M3/16 or E8M0/32; E1M2 and INT4 with FP32/16 or E4M3/16;
@@ -259,6 +260,9 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
  *   out = sum_t p'_t V'_t / sum_t p_t (fp32 accumulation); len = 0 gives 0.
  *     Any integer m gives the same result (the block exponents absorb 2^m),
  *     so the splits of a long cache combine by exact power-of-two rescaling.
+ *   UFP4_KV_FP8: the FP8 KV cache [UQ] measures against, read as the same
+ *     cache in MXFP8 (E4M3 elements with the MX rule above, same groups,
+ *     rotation and probabilities).
  *
  * Cache layout: [B][Hkv][L_cap/128] pages of 17408 bytes, one per 128 tokens.
  * A page holds the operands of v_mfma_scale_f32_16x16x128_f8f6f4 in register
@@ -273,23 +277,30 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
  *   [16896, 17408) V exponents: byte n at l*8 + n, same channel and tokens.
  * Tokens len .. (end of the last page) are stored as zeros; pages past the
  * last one holding a token are not written.
+ * UFP4_KV_FP8 pages hold 33792 bytes: K codes 32 bytes at j*2048 + l*32 (E4M3,
+ * K positions 16g .. 16g+15 then 64+16g .. 64+16g+15 of the same token's
+ * channels), K exponents at 16384 + l*8 (byte j: the token's channel group g),
+ * V codes at 16896 + n*2048 + l*32 (tokens 16g .. 16g+15 then 64+16g .. +15 of
+ * channel 8 rho + n), V exponents at 33280 + l*8 (byte n: tokens 32g .. 32g+31).
  */
 
 /* Bytes of a cache for B sequences, Hkv KV heads, capacity L_cap tokens
- * (a multiple of 128, below 15.7 million: one sequence's pages stay under
- * 2 GiB), head dim D (128).  0 for unsupported sizes. */
-size_t ufp4_kv_cache_bytes(int64_t B, int64_t Hkv, int64_t L_cap, int64_t D);
+ * (a multiple of 128, below 8.1 million: one sequence's pages stay under
+ * 2 GiB), head dim D (128), format UFP4_KV_FP4 or UFP4_KV_FP8.  0 for
+ * unsupported sizes or formats. */
+size_t ufp4_kv_cache_bytes(int64_t B, int64_t Hkv, int64_t L_cap, int64_t D, int kv_format);
 
 /* Quantize K and V (bf16, device) into the cache.  Element (b, h, t, d) is at
  * k[b*stride_b + h*stride_h + t*stride_t + d] (strides in elements, multiples
  * of 8; k, v, cache 16-byte aligned).  lens: device int32[B], tokens per
  * sequence (clamped to [0, L_cap]).  rotate_k: 1 applies H_128 to K (the
- * decode must be called with the same value).  Errors: SHAPE (L_cap not a
- * multiple of 128, Hkv < 1, stride_t < D), UNSUPPORTED (D != 128), ALIGN,
- * INVALID_ARG (null pointer, rotate_k not 0/1). */
+ * decode must be called with the same value and format).  Errors: SHAPE
+ * (L_cap not a multiple of 128, Hkv < 1, stride_t < D), UNSUPPORTED
+ * (D != 128), ALIGN, INVALID_ARG (null pointer, rotate_k not 0/1, unknown
+ * format). */
 int ufp4_kv_cache_quantize(const void *k, const void *v, int64_t B, int64_t Hkv, int64_t L_cap, int64_t D,
-                           int64_t stride_b, int64_t stride_h, int64_t stride_t, const int32_t *lens, int rotate_k,
-                           uint8_t *cache, void *stream);
+                           int kv_format, int64_t stride_b, int64_t stride_h, int64_t stride_t, const int32_t *lens,
+                           int rotate_k, uint8_t *cache, void *stream);
 
 /* The query quantization of the decode on its own: rows x 128 bf16 (device,
  * contiguous) -> codes uint8[rows][128] (E4M3FN, sign in bit 7) and scales
@@ -309,8 +320,8 @@ size_t ufp4_kv_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t
  * ufp4_kv_decode_workspace_size(...) bytes.  Errors as above, plus
  * WORKSPACE, INVALID_ARG for a non-finite sm_scale. */
 int ufp4_kv_decode(const void *q, const uint8_t *cache, const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
-                   int64_t D, int64_t L_cap, float sm_scale, int rotate, int64_t pages_per_split, float *out, void *ws,
-                   size_t ws_bytes, void *stream);
+                   int64_t D, int kv_format, int64_t L_cap, float sm_scale, int rotate, int64_t pages_per_split,
+                   float *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes for op (UFP4_OP_*) on a rows x cols source (QGEMM: rows = M+N,
  * cols = K; ETA: rows = M, cols = N).  cfg may be NULL except for QGEMM and

@@ -50,37 +50,48 @@ def sample_rows(V: int, n: int, seed: int = 0) -> np.ndarray:
     return np.array(sorted(pick))
 
 
-KV_PAGE_BYTES = 17408
+KV_PAGE_BYTES = {"fp4": 17408, "fp8": 33792}
 
 
-def kv_unshuffle(cache: np.ndarray, B: int, Hkv: int, L_cap: int, b: int, h: int, npages: int):
-    """One sequence's pages of the FP4 KV cache in natural layout: K codes
-    [T][64], K exponents [T][4], V codes [128][T/2], V exponents [128][T/32]
-    for T = 128 npages.  Index logic only, from the documented page layout
-    (lane l, rho = l % 16, g = l / 16; K instruction j holds channel group g
-    of token 64(j/4) + 16(rho/4) + 4(j%4) + rho%4; V instruction n holds
-    tokens 32g..32g+31 of channel 8 rho + n)."""
-    pages = cache.reshape(B, Hkv, L_cap // 128, KV_PAGE_BYTES)[b, h, :npages]
+def kv_unshuffle(cache: np.ndarray, B: int, Hkv: int, L_cap: int, b: int, h: int, npages: int, fmt: str = "fp4"):
+    """One sequence's pages of the KV cache in natural layout: K codes
+    [T][D cb], K exponents [T][4], V codes [128][T cb], V exponents
+    [128][T/32] for T = 128 npages and cb = 1/2 (fp4) or 1 (fp8).  Index
+    logic only, from the documented page layout (lane l, rho = l % 16,
+    g = l / 16; K instruction j holds token 64(j/4) + 16(rho/4) + 4(j%4) +
+    rho%4; V instruction n holds channel 8 rho + n).  FP4 lanes hold the 32
+    consecutive positions 32g .. 32g+31 (channels of K, tokens of V); FP8 lanes
+    hold positions 16g .. 16g+15 and 64+16g .. 64+16g+15; the exponent a lane
+    stores is that of positions 32g .. 32g+31 in both."""
+    fp8 = fmt == "fp8"
+    PB = KV_PAGE_BYTES[fmt]
+    pages = cache.reshape(B, Hkv, L_cap // 128, PB)[b, h, :npages]
     T = 128 * npages
-    kc = np.empty((T, 64), np.uint8)
+    cb = 1 if fp8 else 2          # positions per byte
+    lb = 32 if fp8 else 16        # bytes per lane and instruction
+    kc = np.empty((T, 128 // cb), np.uint8)
     ks = np.empty((T, 4), np.uint8)
-    vc = np.empty((128, T // 2), np.uint8)
+    vc = np.empty((128, T // cb), np.uint8)
     vs = np.empty((128, T // 32), np.uint8)
     lane = np.arange(64)
     rho, g = lane % 16, lane // 16
-    cols16 = 16 * g[:, None] + np.arange(16)
+    if fp8:   # byte i of lane g -> position
+        pos = np.where(np.arange(32) < 16, 16 * g[:, None] + np.arange(32), 64 + 16 * g[:, None] + np.arange(32) - 16)
+    else:     # byte i of lane g -> byte of the natural row (two positions per byte)
+        pos = 16 * g[:, None] + np.arange(16)
+    ko, kso, vo, vso = (0, 16384, 16896, 33280) if fp8 else (0, 8192, 8704, 16896)
     for p in range(npages):
         pg = pages[p]
-        kcodes = pg[:8192].reshape(8, 64, 16)
-        kscl = pg[8192:8704].reshape(64, 8)
-        vcodes = pg[8704:16896].reshape(8, 64, 16)
-        vscl = pg[16896:].reshape(64, 8)
+        kcodes = pg[ko:ko + 8 * 64 * lb].reshape(8, 64, lb)
+        kscl = pg[kso:kso + 512].reshape(64, 8)
+        vcodes = pg[vo:vo + 8 * 64 * lb].reshape(8, 64, lb)
+        vscl = pg[vso:vso + 512].reshape(64, 8)
         for j in range(8):
             tok = 128 * p + 64 * (j // 4) + 16 * (rho // 4) + 4 * (j % 4) + rho % 4
-            kc[tok[:, None], cols16] = kcodes[j]
+            kc[tok[:, None], pos] = kcodes[j]
             ks[tok, g] = kscl[:, j]
         for n in range(8):
             ch = 8 * rho + n
-            vc[ch[:, None], (64 * p + 16 * g)[:, None] + np.arange(16)] = vcodes[n]
+            vc[ch[:, None], (128 // cb) * p + pos] = vcodes[n]
             vs[ch, 4 * p + g] = vscl[:, n]
     return kc, ks, vc, vs

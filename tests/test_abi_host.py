@@ -153,25 +153,30 @@ def test_time_next_launch_needs_both_events_or_none():
 def test_kv_calls_validate():
     L = U.lib()
     assert U.ufp4_kv_cache_bytes(2, 2, 256) == 2 * 2 * 2 * 17408
+    assert U.ufp4_kv_cache_bytes(2, 2, 256, fmt="fp8") == 2 * 2 * 2 * 33792
     assert U.ufp4_kv_cache_bytes(2, 2, 100) == 0                       # capacity not a multiple of 128
     assert U.ufp4_kv_cache_bytes(2, 2, 256, 64) == 0                   # head dim 128 only
+    assert L.ufp4_kv_cache_bytes(2, 2, 256, 128, 2) == 0               # unknown format
+    assert U.ufp4_kv_cache_bytes(1, 1, 128 * 70000) == 0               # one sequence's pages over 2 GiB
     q = L.ufp4_kv_cache_quantize
-    assert q(FAKE, FAKE, 1, 1, 100, 128, 0, 0, 128, FAKE, 1, FAKE, None) == -2
-    assert q(FAKE, FAKE, 1, 1, 128, 64, 0, 0, 128, FAKE, 1, FAKE, None) == -4
-    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 120, FAKE, 1, FAKE, None) == -2   # token stride < D
-    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 130, FAKE, 1, FAKE, None) == -3   # stride not a multiple of 8
-    assert q(FAKE + 2, FAKE, 1, 1, 128, 128, 0, 0, 128, FAKE, 1, FAKE, None) == -3
-    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 128, None, 1, FAKE, None) == -1
-    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 128, FAKE, 2, FAKE, None) == -1
-    assert q(None, None, 0, 1, 128, 128, 0, 0, 128, None, 1, None, None) == 0    # empty batch
+    assert q(FAKE, FAKE, 1, 1, 100, 128, 0, 0, 0, 128, FAKE, 1, FAKE, None) == -2
+    assert q(FAKE, FAKE, 1, 1, 128, 64, 0, 0, 0, 128, FAKE, 1, FAKE, None) == -4
+    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 0, 120, FAKE, 1, FAKE, None) == -2   # token stride < D
+    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 0, 130, FAKE, 1, FAKE, None) == -3   # stride not a multiple of 8
+    assert q(FAKE + 2, FAKE, 1, 1, 128, 128, 0, 0, 0, 128, FAKE, 1, FAKE, None) == -3
+    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 0, 128, None, 1, FAKE, None) == -1
+    assert q(FAKE, FAKE, 1, 1, 128, 128, 0, 0, 0, 128, FAKE, 2, FAKE, None) == -1
+    assert q(FAKE, FAKE, 1, 1, 128, 128, 5, 0, 0, 128, FAKE, 1, FAKE, None) == -1   # unknown format
+    assert q(None, None, 0, 1, 128, 128, 0, 0, 0, 128, None, 1, None, None) == 0    # empty batch
     assert L.ufp4_kv_q_quantize(FAKE, 4, 64, 1, FAKE, FAKE, None) == -4
     assert L.ufp4_kv_q_quantize(FAKE, 4, 128, 1, FAKE + 4, FAKE, None) == -3
     d = L.ufp4_kv_decode
-    assert d(FAKE, FAKE, FAKE, 1, 6, 4, 128, 128, 0.1, 1, 0, FAKE, None, 0, None) == -2    # Hq % Hkv
-    assert d(FAKE, FAKE, FAKE, 1, 32, 1, 128, 128, 0.1, 1, 0, FAKE, None, 0, None) == -4   # 32 query rows per KV head
-    assert d(FAKE, FAKE, FAKE, 1, 4, 1, 128, 128, float("inf"), 1, 0, FAKE, None, 0, None) == -1
-    assert d(FAKE, FAKE, FAKE, 1, 4, 1, 128, 128, 0.1, 1, -1, FAKE, None, 0, None) == -1
-    assert d(FAKE, FAKE, FAKE, 1, 4, 1, 128, 1024, 0.1, 1, 2, FAKE, None, 0, None) == -5   # 4 splits need a workspace
+    assert d(FAKE, FAKE, FAKE, 1, 6, 4, 128, 0, 128, 0.1, 1, 0, FAKE, None, 0, None) == -2    # Hq % Hkv
+    assert d(FAKE, FAKE, FAKE, 1, 32, 1, 128, 0, 128, 0.1, 1, 0, FAKE, None, 0, None) == -4   # 32 query rows per KV head
+    assert d(FAKE, FAKE, FAKE, 1, 4, 1, 128, 0, 128, float("inf"), 1, 0, FAKE, None, 0, None) == -1
+    assert d(FAKE, FAKE, FAKE, 1, 4, 1, 128, 0, 128, 0.1, 1, -1, FAKE, None, 0, None) == -1
+    assert d(FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 128, 0.1, 1, 0, FAKE, None, 0, None) == -1    # unknown format
+    assert d(FAKE, FAKE, FAKE, 1, 4, 1, 128, 0, 1024, 0.1, 1, 2, FAKE, None, 0, None) == -5   # 4 splits need a workspace
 
 
 def test_kv_decode_workspace_sizes():

@@ -300,11 +300,12 @@ def bench_kv(U, S, torch, dev, stream, reps=20):
     """One decode step of attention against the FP4 KV cache at the Llama-3-8B
     attention shape (32 query heads, 8 KV heads, head dim 128) for 32
     sequences of 16384 tokens: MXFP8 query x MXFP4 keys (Walsh-Hadamard
-    rotated, or not) and values on the scaled MFMA.  Reports the step (decode
-    kernel + split combine), the decode kernel alone, its HBM rate against the
-    algorithmic bytes (cache + query + output), the cache quantization, and the
+    rotated, or not) and values on the scaled MFMA, and the FP8 (MXFP8) cache
+    the UltraQuant section measures against.  Reports the step (decode kernel
+    + split combine), the decode kernel alone, its HBM rate against the
+    algorithmic bytes (cache + query + output), the cache quantization, the
     output error against exact attention (fp32 softmax over the unquantized
-    bf16 keys and values)."""
+    bf16 keys and values), and the FP4 over FP8 decode speedup."""
     B, Hq, Hkv, L, D = 32, 32, 8, 16384, 128
     G = Hq // Hkv
     q, k, v = S.kv_decode(B, Hq, Hkv, L, D, seed=0)
@@ -329,25 +330,32 @@ def bench_kv(U, S, torch, dev, stream, reps=20):
                        "(E2M1 + UE8M0/32: keys per token over the head dim, values per channel over 32 tokens)",
            "cache_bytes": cache_bytes, "bytes_per_token_per_kv_head": 136, "bf16_bytes_per_token_per_kv_head": 512,
            "algorithmic_bytes_per_step": alg_bytes}
-    for name, rot in (("rotated_keys", True), ("no_rotation", False)):
-        cache = U.ufp4_kv_cache_quantize(kd, vd, lens, rot)
+    for name, rot, fmt in (("rotated_keys", True, "fp4"), ("no_rotation", False, "fp4"),
+                           ("fp8_baseline_rotated_keys", True, "fp8")):
+        cache = U.ufp4_kv_cache_quantize(kd, vd, lens, rot, fmt=fmt)
         o = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         need = U.ufp4_kv_decode_workspace_size(B, Hq, Hkv, L)
         ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
-        ms_step, ms_kernel = _time(lambda: U.ufp4_kv_decode(qd, cache, lens, Hkv, L, sm, rot, out=o, ws=ws),
+        ms_step, ms_kernel = _time(lambda: U.ufp4_kv_decode(qd, cache, lens, Hkv, L, sm, rot, out=o, ws=ws, fmt=fmt),
                                    torch, stream, reps, U)
-        ms_quant = _time(lambda: U.ufp4_kv_cache_quantize(kd, vd, lens, rot, cache), torch, stream, 3)
+        ms_quant = _time(lambda: U.ufp4_kv_cache_quantize(kd, vd, lens, rot, cache, fmt=fmt), torch, stream, 3)
         err = float(torch.linalg.norm(o - exact) / torch.linalg.norm(exact))
-        gbs = alg_bytes / (ms_kernel * 1e-3) / 1e9
-        out[name] = {"step_us": round(ms_step * 1e3, 2), "decode_kernel_us": round(ms_kernel * 1e3, 2),
+        nbytes = U.ufp4_kv_cache_bytes(B, Hkv, L, D, fmt) + B * Hq * D * 6
+        gbs = nbytes / (ms_kernel * 1e-3) / 1e9
+        out[name] = {"cache_format": fmt, "step_us": round(ms_step * 1e3, 2),
+                     "decode_kernel_us": round(ms_kernel * 1e3, 2),
                      "decode_kernel_GBps": round(gbs, 1),
                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                                  "kernel": "kv_decode_kernel", "bytes_per_launch": alg_bytes},
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": traffic if fmt == "fp4" else None,
+                                  "kernel": f"kv_decode_kernel<{fmt == 'fp8'}>".lower(),
+                                  "bytes_per_launch": nbytes},
                      "step_GBps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "cache_quantize_us": round(ms_quant * 1e3, 2),
                      "rel_err_vs_exact_attention": round(err, 5)}
         del cache
+    out["fp4_over_fp8_decode_speedup"] = round(out["fp8_baseline_rotated_keys"]["decode_kernel_us"] /
+                                               out["rotated_keys"]["decode_kernel_us"], 3)
     return out
 
 

@@ -34,6 +34,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -239,9 +241,9 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
                 uint32_t cw[8], ow[8];
                 eb = q_codes32(y, cw);
                 fp8_operand_order(cw, lane, ow);
-                uint4 *dst = reinterpret_cast<uint4 *>(out + KV8_K_CODES + j * 2048 + lane * 32);
-                dst[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-                dst[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+                uint8_t *dst = out + KV8_K_CODES + j * 2048 + lane * 16;
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                *reinterpret_cast<uint4 *>(dst + 1024) = make_uint4(ow[4], ow[5], ow[6], ow[7]);
             } else {
                 const int e = mx_exp(absmax32(y), 2);
                 const float inv = pow2_neg(e);
@@ -278,9 +280,9 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
                 uint32_t cw[8], ow[8];
                 eb = q_codes32(y, cw);
                 fp8_operand_order(cw, lane, ow);
-                uint4 *dst = reinterpret_cast<uint4 *>(out + KV8_V_CODES + n * 2048 + lane * 32);
-                dst[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-                dst[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+                uint8_t *dst = out + KV8_V_CODES + n * 2048 + lane * 16;
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                *reinterpret_cast<uint4 *>(dst + 1024) = make_uint4(ow[4], ow[5], ow[6], ow[7]);
             } else {
                 const int e = mx_exp(absmax32(y), 2);
                 const float inv = pow2_neg(e);
@@ -355,58 +357,63 @@ __device__ __forceinline__ v4f mfma_kv(v4u a, const v8i &b, v4f acc, int sel_a, 
     }
 }
 
-// One page's operands in registers.
-struct PageRegs {
-    v4u kc[8], vc[8];
+// One page's operands in registers: FP4 lanes hold 16 bytes per MFMA (v4u),
+// FP8 lanes 32 bytes (v8i).
+template <bool FP8>
+struct Page {
+    using Op = typename std::conditional<FP8, v8i, v4u>::type;
+    Op kc[8], vc[8];
     v2u ks, vs;
 };
 
-// Loads a page through a buffer resource whose range ends at the split's last
-// page: a page past it reads as zeros without touching memory, so the
-// prefetch of the next page needs no branch.  The page offset is wave-uniform
-// and goes in the scalar offset; the per-lane offsets stay fixed.  The cache
-// is read once per step, so the loads are non-temporal (measured: 12 % faster
-// on a cache larger than the last-level cache).
-__device__ __forceinline__ void load_page(__amdgpu_buffer_rsrc_t rs, int64_t p, uint32_t v16, uint32_t v8, PageRegs &P)
-{
-    const int sp = __builtin_amdgcn_readfirstlane((int)(p * KV_PAGE_BYTES));
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        P.kc[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, v16 + (j & 3) * 1024, sp + KV_K_CODES + (j >> 2) * 4096, KV_NT);
-    P.ks = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + KV_K_SCALES, KV_NT);
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-        P.vc[n] = __builtin_amdgcn_raw_buffer_load_b128(rs, v16 + (n & 3) * 1024, sp + KV_V_CODES + (n >> 2) * 4096, KV_NT);
-    P.vs = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + KV_V_SCALES, KV_NT);
-}
-
-// One FP8 page: the K operands, then the V operands, each loaded in one go.
-struct PageRegs8 {
-    v8i kc[8], vc[8];
-    v2u ks, vs;
-};
-
-__device__ __forceinline__ v8i load32(__amdgpu_buffer_rsrc_t rs, uint32_t v, int s)
+// A lane's A operand for one MFMA.  FP4: 16 bytes at lane*16.  FP8: the
+// instruction's 2 KiB hold the first 16 bytes of every lane, then the second
+// 16 bytes, so each of the two loads reads 1 KiB of whole lines.
+template <bool FP8>
+__device__ __forceinline__ typename Page<FP8>::Op load_op(__amdgpu_buffer_rsrc_t rs, uint32_t v, int s)
 {
     const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(rs, v, s, KV_NT);
-    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rs, v + 16, s, KV_NT);
-    return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    if constexpr (FP8) {
+        const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rs, v + 1024, s, KV_NT);
+        return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+        return lo;
+    }
 }
 
-__device__ __forceinline__ void load_k8(__amdgpu_buffer_rsrc_t rs, int64_t p, uint32_t v32, uint32_t v8, PageRegs8 &P)
+// Loads of a page's keys (with their exponents) or values go through a buffer
+// resource whose range ends at the split's last page: a page past it reads as
+// zeros without touching memory, so the prefetch of the next page needs no
+// branch.  The page offset is wave-uniform and goes in the scalar offset; the
+// per-lane offsets stay fixed.  The cache is read once per step, so the loads
+// are non-temporal (measured: 12 % faster on a cache larger than the
+// last-level cache).
+template <bool FP8>
+__device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t rs, int64_t p, uint32_t v16, uint32_t v8,
+                                          Page<FP8> &P)
 {
-    const int sp = __builtin_amdgcn_readfirstlane((int)(p * KV8_PAGE_BYTES));
+    constexpr int PB = FP8 ? KV8_PAGE_BYTES : KV_PAGE_BYTES, STRIDE = FP8 ? 2048 : 1024;
+    constexpr int CODES = FP8 ? KV8_K_CODES : KV_K_CODES, SCALES = FP8 ? KV8_K_SCALES : KV_K_SCALES;
+    constexpr int PER4K = 4096 / STRIDE;  // instructions per 4 KiB of scalar offset
+    const int sp = __builtin_amdgcn_readfirstlane((int)(p * PB));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) P.kc[j] = load32(rs, v32 + (j & 1) * 2048, sp + KV8_K_CODES + (j >> 1) * 4096);
-    P.ks = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + KV8_K_SCALES, KV_NT);
+    for (int j = 0; j < 8; ++j)
+        P.kc[j] = load_op<FP8>(rs, v16 + (j % PER4K) * STRIDE, sp + CODES + (j / PER4K) * 4096);
+    P.ks = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + SCALES, KV_NT);
 }
 
-__device__ __forceinline__ void load_v8(__amdgpu_buffer_rsrc_t rs, int64_t p, uint32_t v32, uint32_t v8, PageRegs8 &P)
+template <bool FP8>
+__device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t rs, int64_t p, uint32_t v16, uint32_t v8,
+                                            Page<FP8> &P)
 {
-    const int sp = __builtin_amdgcn_readfirstlane((int)(p * KV8_PAGE_BYTES));
+    constexpr int PB = FP8 ? KV8_PAGE_BYTES : KV_PAGE_BYTES, STRIDE = FP8 ? 2048 : 1024;
+    constexpr int CODES = FP8 ? KV8_V_CODES : KV_V_CODES, SCALES = FP8 ? KV8_V_SCALES : KV_V_SCALES;
+    constexpr int PER4K = 4096 / STRIDE;
+    const int sp = __builtin_amdgcn_readfirstlane((int)(p * PB));
 #pragma unroll
-    for (int n = 0; n < 8; ++n) P.vc[n] = load32(rs, v32 + (n & 1) * 2048, sp + KV8_V_CODES + (n >> 1) * 4096);
-    P.vs = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + KV8_V_SCALES, KV_NT);
+    for (int n = 0; n < 8; ++n)
+        P.vc[n] = load_op<FP8>(rs, v16 + (n % PER4K) * STRIDE, sp + CODES + (n / PER4K) * 4096);
+    P.vs = __builtin_amdgcn_raw_buffer_load_b64(rs, v8, sp + SCALES, KV_NT);
 }
 
 // Running softmax state of one wave: integer running maximum, the lane's
@@ -491,18 +498,6 @@ __device__ __forceinline__ void page_pv(const VOp *vc, v2u vs, const v8i &pb, in
     for (int n = 0; n < 8; ++n) st.O[n] = mfma_kv(vc[n], pb, st.O[n], n & 3, (int)(n < 4 ? vs.x : vs.y), ps);
 }
 
-// One FP4 page: scores on the MFMA, softmax update, E4M3 probabilities, P V.
-__device__ __forceinline__ void process_page(const PageRegs &P, const v8i &qb, int qs, int64_t p, int64_t len,
-                                             float c, int g, DecodeState &st)
-{
-    float x[8][4];
-    const float mloc = page_scores(P.kc, P.ks, qb, qs, p, len, c, g, x);
-    v8i pb;
-    int ps;
-    page_softmax(x, mloc, g, st, pb, ps);
-    page_pv(P.vc, P.vs, pb, ps, st);
-}
-
 template <bool FP8>
 __global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void kv_decode_kernel(KvDecodeArgs a)
 {
@@ -527,19 +522,15 @@ __global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(seq), (short)0, (int)(p1 * PB), 0x00020000);
 
     int64_t p = p0 + wave;
-    const uint32_t v16 = (uint32_t)lane * 16u, v8 = (uint32_t)lane * 8u, v32 = (uint32_t)lane * 32u;
-    PageRegs cur;
-    PageRegs8 cur8;
-    if constexpr (FP8) {
-        // same order as in the loop (keys with their scales, then values), so
-        // the loop's waits count the same outstanding loads on every entry
-        load_k8(rs, p, v32, v8, cur8);
-        __builtin_amdgcn_sched_barrier(0);
-        load_v8(rs, p, v32, v8, cur8);
-        __builtin_amdgcn_sched_barrier(0);
-    } else {
-        load_page(rs, p, v16, v8, cur);
-    }
+    const uint32_t v16 = (uint32_t)lane * 16u, v8 = (uint32_t)lane * 8u;
+    // the first page, in the loop's order (keys with their scales, then
+    // values), so the loop's waits count the same outstanding loads on every
+    // entry
+    Page<FP8> cur;
+    load_keys(rs, p, v16, v8, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    load_values(rs, p, v16, v8, cur);
+    __builtin_amdgcn_sched_barrier(0);
 
     // Query operand: wave 0 quantizes (contiguous chunks), all waves read it
     // back in the B-operand order.
@@ -568,40 +559,23 @@ __global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.O[n] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-    if constexpr (FP8) {
-        // One register set: the next page's keys load once the score MFMAs
-        // have read the current ones, its values once P V has.
-        while (p < p1) {
-            float x[8][4];
-            const float mloc = page_scores(cur8.kc, cur8.ks, qb, qs, p, len, a.c, g, x);
-            __builtin_amdgcn_sched_barrier(0);
-            load_k8(rs, p + KV_WAVES, v32, v8, cur8);
-            __builtin_amdgcn_sched_barrier(0);
-            v8i pb;
-            int ps;
-            page_softmax(x, mloc, g, st, pb, ps);
-            page_pv(cur8.vc, cur8.vs, pb, ps, st);
-            __builtin_amdgcn_sched_barrier(0);
-            load_v8(rs, p + KV_WAVES, v32, v8, cur8);
-            __builtin_amdgcn_sched_barrier(0);
-            p += KV_WAVES;
-        }
-    } else {
-        // Two register sets in turn: the next page's loads are issued before
-        // the current page is processed, and no copy between the sets waits
-        // on them.
-        PageRegs nxt;
-        while (p < p1) {
-            load_page(rs, p + KV_WAVES, v16, v8, nxt);
-            __builtin_amdgcn_sched_barrier(0);
-            process_page(cur, qb, qs, p, len, a.c, g, st);
-            p += KV_WAVES;
-            if (p >= p1) break;
-            load_page(rs, p + KV_WAVES, v16, v8, cur);
-            __builtin_amdgcn_sched_barrier(0);
-            process_page(nxt, qb, qs, p, len, a.c, g, st);
-            p += KV_WAVES;
-        }
+    // One register set: the next page's keys load once the score MFMAs have
+    // read the current ones, its values once P V has, so about one page per
+    // wave is in flight at all times.
+    while (p < p1) {
+        float x[8][4];
+        const float mloc = page_scores(cur.kc, cur.ks, qb, qs, p, len, a.c, g, x);
+        __builtin_amdgcn_sched_barrier(0);
+        load_keys(rs, p + KV_WAVES, v16, v8, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        v8i pb;
+        int ps;
+        page_softmax(x, mloc, g, st, pb, ps);
+        page_pv(cur.vc, cur.vs, pb, ps, st);
+        __builtin_amdgcn_sched_barrier(0);
+        load_values(rs, p + KV_WAVES, v16, v8, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        p += KV_WAVES;
     }
     const float m_run = st.m_run, l_lane = st.l_lane;
     v4f O[8];

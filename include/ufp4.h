@@ -277,11 +277,13 @@ int ufp4_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, 
  *   [16896, 17408) V exponents: byte n at l*8 + n, same channel and tokens.
  * Tokens len .. (end of the last page) are stored as zeros; pages past the
  * last one holding a token are not written.
- * UFP4_KV_FP8 pages hold 33792 bytes: K codes 32 bytes at j*2048 + l*32 (E4M3,
- * K positions 16g .. 16g+15 then 64+16g .. 64+16g+15 of the same token's
- * channels), K exponents at 16384 + l*8 (byte j: the token's channel group g),
- * V codes at 16896 + n*2048 + l*32 (tokens 16g .. 16g+15 then 64+16g .. +15 of
- * channel 8 rho + n), V exponents at 33280 + l*8 (byte n: tokens 32g .. 32g+31).
+ * UFP4_KV_FP8 pages hold 33792 bytes.  K codes (E4M3): 16 bytes at
+ * j*2048 + l*16 for the token's channels 16g .. 16g+15 and 16 bytes at
+ * j*2048 + 1024 + l*16 for channels 64+16g .. 64+16g+15; K exponents at
+ * 16384 + l*8 (byte j: the token's channel group g).  V codes at
+ * 16896 + n*2048 + l*16 (tokens 16g .. 16g+15 of channel 8 rho + n) and
+ * 16896 + n*2048 + 1024 + l*16 (tokens 64+16g .. +15); V exponents at
+ * 33280 + l*8 (byte n: tokens 32g .. 32g+31).
  */
 
 /* Bytes of a cache for B sequences, Hkv KV heads, capacity L_cap tokens

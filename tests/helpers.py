@@ -61,8 +61,9 @@ def kv_unshuffle(cache: np.ndarray, B: int, Hkv: int, L_cap: int, b: int, h: int
     g = l / 16; K instruction j holds token 64(j/4) + 16(rho/4) + 4(j%4) +
     rho%4; V instruction n holds channel 8 rho + n).  FP4 lanes hold the 32
     consecutive positions 32g .. 32g+31 (channels of K, tokens of V); FP8 lanes
-    hold positions 16g .. 16g+15 and 64+16g .. 64+16g+15; the exponent a lane
-    stores is that of positions 32g .. 32g+31 in both."""
+    hold positions 16g .. 16g+15 and 64+16g .. 64+16g+15, stored as the first
+    halves of all 64 lanes, then the second halves; the exponent a lane stores
+    is that of positions 32g .. 32g+31 in both."""
     fp8 = fmt == "fp8"
     PB = KV_PAGE_BYTES[fmt]
     pages = cache.reshape(B, Hkv, L_cap // 128, PB)[b, h, :npages]
@@ -82,9 +83,13 @@ def kv_unshuffle(cache: np.ndarray, B: int, Hkv: int, L_cap: int, b: int, h: int
     ko, kso, vo, vso = (0, 16384, 16896, 33280) if fp8 else (0, 8192, 8704, 16896)
     for p in range(npages):
         pg = pages[p]
-        kcodes = pg[ko:ko + 8 * 64 * lb].reshape(8, 64, lb)
+        if fp8:  # [instruction][half][lane][16 B] -> [instruction][lane][32 B]
+            kcodes = pg[ko:ko + 16384].reshape(8, 2, 64, 16).transpose(0, 2, 1, 3).reshape(8, 64, 32)
+            vcodes = pg[vo:vo + 16384].reshape(8, 2, 64, 16).transpose(0, 2, 1, 3).reshape(8, 64, 32)
+        else:
+            kcodes = pg[ko:ko + 8 * 64 * lb].reshape(8, 64, lb)
+            vcodes = pg[vo:vo + 8 * 64 * lb].reshape(8, 64, lb)
         kscl = pg[kso:kso + 512].reshape(64, 8)
-        vcodes = pg[vo:vo + 8 * 64 * lb].reshape(8, 64, lb)
         vscl = pg[vso:vso + 512].reshape(64, 8)
         for j in range(8):
             tok = 128 * p + 64 * (j // 4) + 16 * (rho // 4) + 4 * (j % 4) + rho % 4

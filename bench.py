@@ -380,17 +380,18 @@ def _ktime(U, torch, stream, fn, reps=10):
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def _qbytes(n, cfg):
-    """Algorithmic bytes of one quantize pass over n bf16 elements."""
+def _qbytes(n, cfg, elt=2):
+    """Algorithmic bytes of one quantize pass over n input elements of elt
+    bytes (bf16 by default)."""
     scale = 4 * n // cfg.block if cfg.scale == "fp32" else n // cfg.block
-    return 2 * n + n // 2 + scale
+    return elt * n + n // 2 + scale
 
 
 def _leg(U, torch, stream, x, cfg, amax=None):
     """Kernel time and HBM rate of one quantize call (amax given for E4M3)."""
     q = U.alloc_qtensor(x.shape[0], x.shape[1], cfg)
     ms = _ktime(U, torch, stream, lambda: U.ufp4_quantize(x, cfg, amax=amax, out=q))
-    b = _qbytes(x.numel(), cfg)
+    b = _qbytes(x.numel(), cfg, x.element_size())
     return {"us": round(ms * 1e3, 2), "bytes": b, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}, q
 
@@ -425,6 +426,20 @@ def bench_configs(U, S, torch, dev, stream):
     ms = _ktime(U, torch, stream, lambda: U.ufp4_amax(x, cfg, out=amax, ws=ws))
     c2["amax_pass"] = {"us": round(ms * 1e3, 2), "GBps": round(2 * x.numel() / (ms * 1e-3) / 1e9, 1)}
     c2["rht_overhead_e2m1"] = round(c2["e2m1_random"]["us"] / c2["e2m1_none"]["us"] - 1, 4)
+    # unfused: the RHT as a kernel of its own, then the quantize reading its
+    # output without the RHT; an fp32 intermediate gives the fused kernel's codes
+    # exactly, a bf16 one (what a bf16 pipeline would store) rounds y first
+    cfg_y = U.Cfg("e2m1", "e4m3", rht="none")
+    unfused = {}
+    for name, dt in (("fp32_intermediate", torch.float32), ("bf16_intermediate", torch.bfloat16)):
+        y = U.ufp4_rht(x, rht="random", seed=0, out_dtype=dt)
+        ms_rht = _ktime(U, torch, stream, lambda: U.ufp4_rht(x, rht="random", seed=0, y=y))
+        q_leg = _leg(U, torch, stream, y, cfg_y, U.ufp4_amax(y, cfg_y))[0]
+        tot = ms_rht * 1e3 + q_leg["us"]
+        unfused[name] = {"rht_us": round(ms_rht * 1e3, 2), "quantize_us": q_leg["us"], "total_us": round(tot, 2),
+                         "over_fused": round(tot / c2["e2m1_random"]["us"] - 1, 4)}
+        del y
+    c2["unfused_e2m1"] = unfused
     out["activations_8192x8192"] = c2
     del x
     # llama linear: E1M2, FP32 1x16, RHT-16 on all; SR (stream 0 row, 1 col) on dY

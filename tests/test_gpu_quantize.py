@@ -197,3 +197,19 @@ def test_empty_tensor_is_a_no_op():
     x = torch.empty((64, 0), dtype=torch.bfloat16, device="cuda")
     q = U.ufp4_quantize(x, U.Cfg("e1m2", axis="col"))
     assert q.codes.numel() == 0
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e1m2"])
+def test_unfused_rht_then_quantize_equals_fused(fmt):
+    """The RHT as its own call (fp32 output) followed by a quantization
+    without it gives the fused kernel's codes and scales bit for bit."""
+    import torch
+    import block_scaled_bit_ufp4_amd as U
+    x = to_device_bf16(S.activations_t3(512, 1024, seed=3))
+    fused_cfg = U.Cfg(fmt, "e4m3", rht="random", rht_seed=5)
+    fused = U.ufp4_quantize(x, fused_cfg)
+    y = U.ufp4_rht(x, rht="random", seed=5, out_dtype=torch.float32)
+    plain = U.ufp4_quantize(y, U.Cfg(fmt, "e4m3", rht="none"))
+    np.testing.assert_array_equal(host(fused.codes), host(plain.codes))
+    np.testing.assert_array_equal(host(fused.scales).view(np.uint8), host(plain.scales).view(np.uint8))
+    np.testing.assert_array_equal(host(fused.tensor_scale), host(plain.tensor_scale))

@@ -225,15 +225,21 @@ __device__ __forceinline__ uint32_t rtne_code(float a)
 template <int F>
 __device__ __forceinline__ uint32_t sr_code(float a, uint32_t w)
 {
-    const float fu = (float)(w >> 8);
     if constexpr (F == FMT_E1M2 || F == FMT_INT4) {
+        // Uniform grids, in integers.  With t = a in grid units (a x 2 for
+        // E1M2, exact) and T = ceil(t 2^24) (exact: t 2^24 < 2^27 is a
+        // binary32 value and its ceiling an integer below 2^32),
+        // T = k_lo 2^24 + ceil(frac 2^24), so
+        //   (T + 2^24 - 1 - (w >> 8)) >> 24 = k_lo + ((w >> 8) < ceil(frac 2^24))
+        //                                  = k_lo + (u < frac),
+        // since for an integer W, W < x holds exactly when W < ceil(x).
+        // Clamping a to the grid maximum gives code 7.
         constexpr float G = grid_max(F);
-        const float t = (F == FMT_E1M2) ? a * 2.0f : a;  // grid units (step 1)
-        const float kl = __builtin_floorf(t);
-        const float frac = t - kl;
-        const uint32_t k = (uint32_t)kl + (fu < frac * 0x1p24f ? 1u : 0u);
-        return a >= G ? 7u : k;
+        constexpr float SC = F == FMT_E1M2 ? 0x1p25f : 0x1p24f;
+        const uint32_t T = (uint32_t)__builtin_ceilf(fminf(a, G) * SC);
+        return (T + 0xFFFFFFu - (w >> 8)) >> 24;
     } else {
+        const float fu = (float)(w >> 8);
         if (a >= 6.0f) return 7u;
         if (a < 1.0f) {
             const float t = a * 2.0f;

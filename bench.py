@@ -12,11 +12,13 @@ input three times and writes two sets of codes and scales.  Inputs rotate over
 step reads HBM.
 
 value = bf16 input bytes quantized per second (2 bytes x 2 quantizations x n
-per step / step time).  The roofline object is for the dominant kernel, the
-fused RHT + quantize kernel: algorithmic bytes per launch (bf16 in + packed
-codes + E4M3 scales = 171,966,464 B) over its average duration in the timed
-steps, from HIP events that the launch itself timestamps (hipExtLaunchKernel,
-through ufp4_time_next_launch) on the stream it runs on.  The secondary `qgemm` object times the
+per step / step time), from K steps with events only at the ends of the
+timed region.  The roofline object is for the dominant kernel, the fused RHT
++ quantize kernel: algorithmic bytes per launch (bf16 in + packed codes + E4M3
+scales = 171,966,464 B) over its mean duration in a second timed region of K
+back-to-back launches over the rotating copies (inputs cold in HBM), with HIP
+events on the launch stream at the ends; a plain device copy of the input,
+timed the same way, gives the rate a copy reaches.  The `qgemm` object times the
 MXFP4 block-scaled GEMM at 8192^3 (A, B: N(0,1) bf16 -> RHT -> MXFP4).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
@@ -121,34 +123,52 @@ def main():
     amax_ws = torch.empty(U.ufp4_workspace_size(U.OP_AMAX, ROWS, COLS, cfgs[0]), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         j = i % args.copies
         # the tensor amax after the RHT depends on the rotation and axis only,
         # not on the element format: one pass serves both quantizations (each
         # derives its own alpha = amax / (gridmax x 448) from it)
         U.ufp4_amax(xs[j], cfgs[0], out=amaxes[j], ws=amax_ws)
         for f, cfg in enumerate(cfgs):
-            if ev is not None:
-                # the quantize kernel timestamps its own dispatch on these events
-                U.ufp4_time_next_launch(ev[f][0], ev[f][1])
             U.ufp4_quantize(xs[j], cfg, amax=amaxes[j], out=outs[j][f])
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in cfgs] for _ in range(args.steps)]
-    for e in (e for step_ev in evs for pair in step_ev for e in pair):
-        e.record(stream)  # create the events before the timed region
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region 1: the K steps as a user runs them, events only at the ends
+    # (this gives value and ms_per_step)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    q_ms = [np.mean([evs[i][f][0].elapsed_time(evs[i][f][1]) for i in range(args.steps)]) for f in range(len(cfgs))]
+    # timed region 2: the roofline.  K back-to-back launches of each quantize
+    # kernel over the rotating copies, events on the launch stream at the
+    # ends only, with no amax pass before them: every launch reads its input
+    # cold from HBM.  A plain device copy of the input over the same copies,
+    # timed the same way, gives the rate a copy reaches.  (Inside the step the
+    # kernel runs a few microseconds faster, just after the amax pass has read
+    # the same input; events that a launch timestamps itself add a gap and
+    # read several microseconds high, so neither serves as the kernel's HBM
+    # rate.)
+    def b2b(fn):
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            fn(i % args.copies)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+    q_ms = [b2b(lambda j, f=f, cfg=cfg: U.ufp4_quantize(xs[j], cfg, amax=amaxes[j], out=outs[j][f]))
+            for f, cfg in enumerate(cfgs)]
+    dst = [torch.empty_like(x0) for _ in range(args.copies)]
+    copy_ms = b2b(lambda j: dst[j].copy_(xs[(3 * j + 1) % args.copies]))
+    del dst
+    copy_gbs = 2 * 2 * N_ELEM / (copy_ms * 1e-3) / 1e9
     value = 2 * N_ELEM * len(cfgs) / (ms_step * 1e-3) / 1e9
     achieved = QUANT_BYTES / (q_ms[0] * 1e-3) / 1e9
     traffic = traffic_from_profile()
@@ -174,7 +194,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "row_kernel (fused RHT + E2M1 + E4M3 two-level quantize)",
                      "bytes_per_launch": QUANT_BYTES, "avg_launch_ms": round(q_ms[0], 5),
-                     "e1m2_avg_launch_ms": round(q_ms[1], 5)},
+                     "e1m2_avg_launch_ms": round(q_ms[1], 5),
+                     "timing": "second timed region: K back-to-back launches over the rotating copies (inputs "
+                               "cold in HBM), HIP events on the launch stream at its ends",
+                     "device_copy_GBps": round(copy_gbs, 1),
+                     "frac_of_device_copy": round(achieved / copy_gbs, 4)},
     }
     if not args.no_gemm:
         out["qgemm"] = bench_gemm(U, S, torch, dev, stream)
@@ -189,30 +213,19 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _time(fn, torch, stream, reps, U=None):
-    """Milliseconds per call over reps back-to-back calls; with U, also the
-    mean duration of the first kernel each call launches, from events that
-    launch timestamps itself."""
+def _time(fn, torch, stream, reps):
+    """Milliseconds per call over reps back-to-back calls, HIP events on the
+    stream at the ends only."""
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ks:
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
     e0.record(stream)
-    for a, b in ks:
-        if U is not None:
-            U.ufp4_time_next_launch(a, b)
+    for _ in range(reps):
         fn()
     e1.record(stream)
     torch.cuda.synchronize()
-    per_call = e0.elapsed_time(e1) / reps
-    if U is None:
-        return per_call
-    return per_call, float(np.mean([a.elapsed_time(b) for a, b in ks]))
+    return e0.elapsed_time(e1) / reps
 
 
 def bench_gemm(U, S, torch, dev, stream, reps=10):
@@ -225,13 +238,13 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
     cfg = U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=0)
     qa, qb = U.ufp4_quantize(a, cfg), U.ufp4_quantize(b, cfg)
     c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ms_call, ms = _time(lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c), torch, stream, reps, U)
+    ms_call = _time(lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c), torch, stream, reps)
     cfg2 = U.Cfg("e1m2", "fp32", rht="random", rht_seed=0)
     ea, eb = U.ufp4_quantize(a, cfg2), U.ufp4_quantize(b, cfg2)
     ws = torch.empty(U.ufp4_workspace_size(U.OP_QGEMM, M + N, K, cfg2), dtype=torch.uint8, device=dev)
     ms_e1m2 = _time(lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws), torch, stream, reps)
-    _, ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps, U)
-    tf = flop / (ms * 1e-3) / 1e12
+    ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps)
+    tf = flop / (ms_call * 1e-3) / 1e12
     # IF4 against NVFP4 and MXFP4 on the MXFP4/IF4 workload's data: A, B are
     # its two 8192-row halves (N(0,1) with uniform 1x32 blocks)
     xh, _ = S.mx_if4(2 * M, K, seed=0)
@@ -248,8 +261,8 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
         sm = U.ufp4_eta(c, zref).cpu().numpy()
         c4[name] = {"ms": round(ms_, 4), "eta": round(float(sm[0] / sm[1]), 6),
                     "sqnr_db": round(float(10 * np.log10(sm[1] / sm[2])), 3)}
-    return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out", "ms": round(ms, 4),
-            "ms_per_call_back_to_back": round(ms_call, 4),
+    return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out",
+            "ms": round(ms_call, 4), "timing": "back-to-back calls (one kernel each), events at the ends",
             "tflops": round(tf, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tf / FP4_PEAK_TFLOPS, 4),
             "e1m2_dequant_bf16": {"ms": round(ms_e1m2, 4), "tflops": round(flop / (ms_e1m2 * 1e-3) / 1e12, 1),
                                   "note": "dequantize both operands to bf16 (workspace) + bf16 MFMA GEMM"},
@@ -340,14 +353,15 @@ def bench_kv(U, S, torch, dev, stream, reps=20):
         o = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         need = U.ufp4_kv_decode_workspace_size(B, Hq, Hkv, L)
         ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
-        ms_step, ms_kernel = _time(lambda: U.ufp4_kv_decode(qd, cache, lens, Hkv, L, sm, rot, out=o, ws=ws, fmt=fmt),
-                                   torch, stream, reps, U)
+        ms_step = _time(lambda: U.ufp4_kv_decode(qd, cache, lens, Hkv, L, sm, rot, out=o, ws=ws, fmt=fmt),
+                        torch, stream, reps)
         ms_quant = _time(lambda: U.ufp4_kv_cache_quantize(kd, vd, lens, rot, cache, fmt=fmt), torch, stream, 3)
         err = float(torch.linalg.norm(o - exact) / torch.linalg.norm(exact))
         nbytes = U.ufp4_kv_cache_bytes(B, Hkv, L, D, fmt) + B * Hq * D * 6
-        gbs = nbytes / (ms_kernel * 1e-3) / 1e9
+        # one kernel per call here (B * Hkv >= 256 workgroups: no split, no
+        # combine), so the back-to-back call time is the kernel's duration
+        gbs = nbytes / (ms_step * 1e-3) / 1e9
         out[name] = {"cache_format": fmt, "step_us": round(ms_step * 1e3, 2),
-                     "decode_kernel_us": round(ms_kernel * 1e3, 2),
                      "decode_kernel_GBps": round(gbs, 1),
                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -358,26 +372,9 @@ def bench_kv(U, S, torch, dev, stream, reps=20):
                      "cache_quantize_us": round(ms_quant * 1e3, 2),
                      "rel_err_vs_exact_attention": round(err, 5)}
         del cache
-    out["fp4_over_fp8_decode_speedup"] = round(out["fp8_baseline_rotated_keys"]["decode_kernel_us"] /
-                                               out["rotated_keys"]["decode_kernel_us"], 3)
+    out["fp4_over_fp8_decode_speedup"] = round(out["fp8_baseline_rotated_keys"]["step_us"] /
+                                               out["rotated_keys"]["step_us"], 3)
     return out
-
-
-def _ktime(U, torch, stream, fn, reps=10):
-    """Mean duration (ms) of the first kernel fn launches, over reps calls,
-    from events that kernel's dispatch timestamps itself."""
-    fn()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    for a, b in evs:
-        U.ufp4_time_next_launch(a, b)
-        fn()
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
 def _qbytes(n, cfg, elt=2):
@@ -388,9 +385,10 @@ def _qbytes(n, cfg, elt=2):
 
 
 def _leg(U, torch, stream, x, cfg, amax=None):
-    """Kernel time and HBM rate of one quantize call (amax given for E4M3)."""
+    """Kernel time and HBM rate of one quantize call (amax given for E4M3:
+    the call is then one kernel), from back-to-back calls."""
     q = U.alloc_qtensor(x.shape[0], x.shape[1], cfg)
-    ms = _ktime(U, torch, stream, lambda: U.ufp4_quantize(x, cfg, amax=amax, out=q))
+    ms = _time(lambda: U.ufp4_quantize(x, cfg, amax=amax, out=q), torch, stream, 10)
     b = _qbytes(x.numel(), cfg, x.element_size())
     return {"us": round(ms * 1e3, 2), "bytes": b, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}, q
@@ -409,8 +407,8 @@ def bench_configs(U, S, torch, dev, stream):
     for fmt in ("e2m1", "e1m2"):
         cfg = U.Cfg(fmt, "fp32")
         leg, q = _leg(U, torch, stream, x, cfg)
-        leg["dequant_us"] = round(_ktime(U, torch, stream, lambda: U.ufp4_dequantize(q)) * 1e3, 2)
-        leg["stats_us"] = round(_ktime(U, torch, stream, lambda: U.ufp4_stats(x, q)) * 1e3, 2)
+        leg["dequant_us"] = round(_time(lambda: U.ufp4_dequantize(q), torch, stream, 10) * 1e3, 2)
+        leg["stats_us"] = round(_time(lambda: U.ufp4_stats(x, q), torch, stream, 10) * 1e3, 2)
         c1[fmt] = leg
     out["quantize_x_256x1024"] = c1
     # activations 8192^2: two-level E4M3, with and without RHT, and INT4
@@ -423,7 +421,7 @@ def bench_configs(U, S, torch, dev, stream):
     cfg = U.Cfg("e2m1", "e4m3", rht="random", rht_seed=0)
     amax = torch.empty(1, dtype=torch.float32, device=dev)
     ws = torch.empty(U.ufp4_workspace_size(U.OP_AMAX, ROWS, COLS, cfg), dtype=torch.uint8, device=dev)
-    ms = _ktime(U, torch, stream, lambda: U.ufp4_amax(x, cfg, out=amax, ws=ws))
+    ms = _time(lambda: U.ufp4_amax(x, cfg, out=amax, ws=ws), torch, stream, 10)
     c2["amax_pass"] = {"us": round(ms * 1e3, 2), "GBps": round(2 * x.numel() / (ms * 1e-3) / 1e9, 1)}
     c2["rht_overhead_e2m1"] = round(c2["e2m1_random"]["us"] / c2["e2m1_none"]["us"] - 1, 4)
     # unfused: the RHT as a kernel of its own, then the quantize reading its
@@ -433,7 +431,7 @@ def bench_configs(U, S, torch, dev, stream):
     unfused = {}
     for name, dt in (("fp32_intermediate", torch.float32), ("bf16_intermediate", torch.bfloat16)):
         y = U.ufp4_rht(x, rht="random", seed=0, out_dtype=dt)
-        ms_rht = _ktime(U, torch, stream, lambda: U.ufp4_rht(x, rht="random", seed=0, y=y))
+        ms_rht = _time(lambda: U.ufp4_rht(x, rht="random", seed=0, y=y), torch, stream, 10)
         q_leg = _leg(U, torch, stream, y, cfg_y, U.ufp4_amax(y, cfg_y))[0]
         tot = ms_rht * 1e3 + q_leg["us"]
         unfused[name] = {"rht_us": round(ms_rht * 1e3, 2), "quantize_us": q_leg["us"], "total_us": round(tot, 2),
@@ -472,11 +470,13 @@ def bench_configs(U, S, torch, dev, stream):
     c5 = {"mxfp4_rht": _leg(U, torch, stream, x, U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=0))[0]}
     leg, q = _leg(U, torch, stream, x, U.Cfg("e1m2", "fp32", rht="random", rht_seed=0))
     y = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device=dev)
-    ms = _ktime(U, torch, stream, lambda: U.ufp4_dequantize(q, y=y))
+    ms = _time(lambda: U.ufp4_dequantize(q, y=y), torch, stream, 10)
     leg["dequant_bf16_us"] = round(ms * 1e3, 2)
     c5["e1m2_rht"] = leg
     out["gemm_operands_8192x8192"] = c5
     out["formats"] = bench_formats(U, S, torch, dev)
+    out["note"] = ("each leg launches one call back to back on one tensor; tensors that fit the 256 MB "
+                   "last-level cache are partly served from it")
     return out
 
 

@@ -245,6 +245,29 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
     ms_e1m2 = _time(lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws), torch, stream, reps)
     ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps)
     tf = flop / (ms_call * 1e-3) / 1e12
+    # attenuation and output SQNR of both paths against Z = A B^T of the bf16
+    # inputs, and the whole path (quantize both operands, then the GEMM)
+    zc5 = U.ufp4_gemm_bf16(a, b)
+    quality = {}
+    for name, fn in (("mxfp4", lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c)),
+                     ("e1m2", lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws))):
+        fn()
+        sm = U.ufp4_eta(c, zc5).cpu().numpy()
+        quality[name] = {"eta": round(float(sm[0] / sm[1]), 6), "sqnr_db": round(float(10 * np.log10(sm[1] / sm[2])), 3)}
+    del zc5
+
+    def e2e_mx():
+        U.ufp4_quantize(a, cfg, out=qa)
+        U.ufp4_quantize(b, cfg, out=qb)
+        U.ufp4_qgemm(qa, qb, "mxfp4", c=c)
+
+    def e2e_e1m2():
+        U.ufp4_quantize(a, cfg2, out=ea)
+        U.ufp4_quantize(b, cfg2, out=eb)
+        U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws)
+
+    ms_e2e_mx = _time(e2e_mx, torch, stream, reps)
+    ms_e2e_e1m2 = _time(e2e_e1m2, torch, stream, reps)
     # IF4 against NVFP4 and MXFP4 on the MXFP4/IF4 workload's data: A, B are
     # its two 8192-row halves (N(0,1) with uniform 1x32 blocks)
     xh, _ = S.mx_if4(2 * M, K, seed=0)
@@ -264,7 +287,12 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
     return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out",
             "ms": round(ms_call, 4), "timing": "back-to-back calls (one kernel each), events at the ends",
             "tflops": round(tf, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tf / FP4_PEAK_TFLOPS, 4),
+            "eta": quality["mxfp4"]["eta"], "sqnr_db": quality["mxfp4"]["sqnr_db"],
+            "quantize_and_gemm_ms": round(ms_e2e_mx, 4),
+            "quantize_and_gemm_tflops": round(flop / (ms_e2e_mx * 1e-3) / 1e12, 1),
             "e1m2_dequant_bf16": {"ms": round(ms_e1m2, 4), "tflops": round(flop / (ms_e1m2 * 1e-3) / 1e12, 1),
+                                  "eta": quality["e1m2"]["eta"], "sqnr_db": quality["e1m2"]["sqnr_db"],
+                                  "quantize_and_gemm_ms": round(ms_e2e_e1m2, 4),
                                   "note": "dequantize both operands to bf16 (workspace) + bf16 MFMA GEMM"},
             "bf16_reference": {"ms": round(ms_bf16, 4), "tflops": round(flop / (ms_bf16 * 1e-3) / 1e12, 1),
                                "peak_tflops": 2500.0},
@@ -485,7 +513,9 @@ def bench_formats(U, S, torch, dev):
     and MXFP4 (16384x8192 N(0,1) + uniform blocks) tensors, NVFP4-style
     two-level scale, with and without RHT: SQNR, signal factor alpha and mean
     shrinkage, from the statistics kernel.  The capped E2M1 grids are the
-    pages' attempt to emulate a uniform grid on E2M1; int4 is NVINT4."""
+    pages' attempt to emulate a uniform grid on E2M1; int4 is NVINT4.  Then
+    the llama-shaped linear layer's X, W and dY with the single-level FP32
+    scale, E2M1 and E1M2, with the SQNR gain from the RHT."""
     def dev_bf16(h):
         return torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev)
 
@@ -502,6 +532,26 @@ def bench_formats(U, S, torch, dev):
                                      "mean_shrink": float(f"{r['mean_shrink']:.4e}")}
         res[name] = d
         del x
+    # the linear layer's operands with the UFP4 recipe's single-level FP32
+    # scale (row axis), E2M1 for contrast; dY also with stochastic rounding
+    d = {}
+    for name, xh in (("x_16384x4096", S.llama_x(16384, 4096)), ("w_14336x4096", S.llama_w(14336, 4096)),
+                     ("dy_16384x14336", S.llama_dy(16384, 14336))):
+        x = dev_bf16(xh)
+        del xh
+        e = {}
+        for rht in ("none", "random"):
+            for fmt, rnd in (("e2m1", "rtne"), ("e1m2", "rtne")) + ((("e1m2", "sr"),) if name.startswith("dy") else ()):
+                cfg = U.Cfg(fmt, "fp32", rht=rht, rht_seed=0, rounding=rnd)
+                r = U.ufp4_stats_finalize(U.ufp4_stats(x, U.ufp4_quantize(x, cfg)))
+                e[f"{fmt}_{rht}" + ("_sr" if rnd == "sr" else "")] = {
+                    "sqnr_db": round(r["sqnr_db"], 3), "alpha": round(r["alpha"], 6),
+                    "mean_shrink": float(f"{r['mean_shrink']:.4e}")}
+        for fmt in ("e2m1", "e1m2"):
+            e[f"{fmt}_rht_gain_db"] = round(e[f"{fmt}_random"]["sqnr_db"] - e[f"{fmt}_none"]["sqnr_db"], 3)
+        d[name] = e
+        del x
+    res["llama_linear_operands_fp32_scale"] = d
     return res
 
 

@@ -35,6 +35,16 @@ namespace ufp4 {
 constexpr int RT = 256;  // row kernel: threads per workgroup
 constexpr int RU = 2;    // row kernel: 16-element chunks per lane (quantize, transform)
 constexpr int RUA = 8;   // row kernel: chunks per lane in the amax pass
+// Outputs are written with non-temporal stores: no pass reads its own codes
+// and scales back, and keeping them out of the caches leaves room for the
+// input, which the next quantization of the same tensor re-reads.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void nt_store16(void *p, uint32_t x, uint32_t y, uint32_t z, uint32_t w)
+{
+    const u32x4 v = {x, y, z, w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
 constexpr int CT = 256;  // column kernel: threads per workgroup
 constexpr int CTR = 512; // column kernel: source rows per workgroup
 constexpr int CTC = 64;  // column kernel: source columns per workgroup
@@ -393,13 +403,14 @@ __device__ __forceinline__ void row_chunk(const RowArgs &a, int64_t ch, float *v
         float sval;
         const uint2 codes = quant_chunk<F, S, SR, FOLD>(v, tc, (uint64_t)ch * 16, a.sr_seed, a.sr_stream, true,
                                                         sbyte, sval);
-        reinterpret_cast<uint2 *>(a.codes)[ch] = codes;
+        const u32x2 cv = {codes.x, codes.y};
+        __builtin_nontemporal_store(cv, reinterpret_cast<u32x2 *>(a.codes) + ch);
         if constexpr (S == SC_E8M0) {
-            if ((ch & 1) == 0) static_cast<uint8_t *>(a.scales)[ch >> 1] = (uint8_t)sbyte;
+            if ((ch & 1) == 0) __builtin_nontemporal_store((uint8_t)sbyte, static_cast<uint8_t *>(a.scales) + (ch >> 1));
         } else if constexpr (S == SC_E4M3) {
-            static_cast<uint8_t *>(a.scales)[ch] = (uint8_t)sbyte;
+            __builtin_nontemporal_store((uint8_t)sbyte, static_cast<uint8_t *>(a.scales) + ch);
         } else {
-            static_cast<float *>(a.scales)[ch] = sval;
+            __builtin_nontemporal_store(sval, static_cast<float *>(a.scales) + ch);
         }
     }
 }
@@ -622,8 +633,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         for (int q = 0; q < CTC * 16 / CT; ++q) {
             const int idx = q * CT + tid, cl = idx >> 4, part = idx & 15;
             const uint2 u = st_codes[cl * CP + 2 * part], w = st_codes[cl * CP + 2 * part + 1];
-            *reinterpret_cast<uint4 *>(a.codes + (cv0 + cl) * (a.R >> 1) + (rs0 >> 1) + 16 * part) =
-                make_uint4(u.x, u.y, w.x, w.y);
+            nt_store16(a.codes + (cv0 + cl) * (a.R >> 1) + (rs0 >> 1) + 16 * part, u.x, u.y, w.x, w.y);
         }
         if constexpr (S == SC_FP32) {
             // 64 view rows x 32 scales (128 bytes), 8 lanes of 16 bytes per view row
@@ -631,21 +641,25 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
             for (int q = 0; q < CTC * 8 / CT; ++q) {
                 const int idx = q * CT + tid, cl = idx >> 3, part = idx & 7;
                 const float *p = st_scale + cl * CP + 4 * part;
-                *reinterpret_cast<float4 *>(static_cast<float *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) +
-                                            4 * part) = make_float4(p[0], p[1], p[2], p[3]);
+                nt_store16(static_cast<float *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) + 4 * part,
+                           __float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3]));
             }
         } else if constexpr (S == SC_E4M3) {
             // 64 view rows x 32 bytes, 2 lanes per view row
             if (tid < CTC * 2) {
                 const int cl = tid >> 1, part = tid & 1;
-                *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) +
-                                           16 * part) = *reinterpret_cast<const uint4 *>(st_sbyte + cl * NB + 16 * part);
+                const uint4 q4 = *reinterpret_cast<const uint4 *>(st_sbyte + cl * NB + 16 * part);
+                nt_store16(static_cast<uint8_t *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) + 16 * part, q4.x,
+                           q4.y, q4.z, q4.w);
             }
         } else {
             // E8M0: 64 view rows x 16 bytes, one lane per view row
             if (tid < CTC)
-                *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.scales) + (cv0 + tid) * (a.R >> 5) + (rs0 >> 5)) =
-                    *reinterpret_cast<const uint4 *>(st_sbyte + tid * NB);
+            {
+                const uint4 q4 = *reinterpret_cast<const uint4 *>(st_sbyte + tid * NB);
+                nt_store16(static_cast<uint8_t *>(a.scales) + (cv0 + tid) * (a.R >> 5) + (rs0 >> 5), q4.x, q4.y, q4.z,
+                           q4.w);
+            }
         }
     }
     if constexpr (MODE == MODE_AMAX) {

@@ -208,6 +208,21 @@ struct KvQuantArgs {
     uint8_t *cache;
 };
 
+// The cache is written with non-temporal stores: the pass does not read it
+// back, and a decode reads it later from HBM.
+typedef unsigned int kv_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int kv_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void nt_store16(uint8_t *p, uint4 v)
+{
+    const kv_u32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<kv_u32x4 *>(p));
+}
+__device__ __forceinline__ void nt_store8(uint8_t *p, uint32_t lo, uint32_t hi)
+{
+    const kv_u32x2 x = {lo, hi};
+    __builtin_nontemporal_store(x, reinterpret_cast<kv_u32x2 *>(p));
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
 {
@@ -242,19 +257,19 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
                 eb = q_codes32(y, cw);
                 fp8_operand_order(cw, lane, ow);
                 uint8_t *dst = out + KV8_K_CODES + j * 2048 + lane * 16;
-                *reinterpret_cast<uint4 *>(dst) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-                *reinterpret_cast<uint4 *>(dst + 1024) = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+                nt_store16(dst, make_uint4(ow[0], ow[1], ow[2], ow[3]));
+                nt_store16(dst + 1024, make_uint4(ow[4], ow[5], ow[6], ow[7]));
             } else {
                 const int e = mx_exp(absmax32(y), 2);
                 const float inv = pow2_neg(e);
 #pragma unroll
                 for (int i = 0; i < 32; ++i) y[i] = y[i] * inv;
-                *reinterpret_cast<uint4 *>(out + KV_K_CODES + j * 1024 + lane * 16) = pack32_e2m1(y);
+                nt_store16(out + KV_K_CODES + j * 1024 + lane * 16, pack32_e2m1(y));
                 eb = (uint32_t)(e + 127);
             }
             sc[j >> 2] |= eb << (8 * (j & 3));
         }
-        *reinterpret_cast<uint2 *>(out + (FP8 ? KV8_K_SCALES : KV_K_SCALES) + lane * 8) = make_uint2(sc[0], sc[1]);
+        nt_store8(out + (FP8 ? KV8_K_SCALES : KV_K_SCALES) + lane * 8, sc[0], sc[1]);
     }
     // V: lane (rho, g) holds channels 8 rho .. 8 rho + 7 of tokens 32g .. 32g+31.
     {
@@ -281,19 +296,19 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
                 eb = q_codes32(y, cw);
                 fp8_operand_order(cw, lane, ow);
                 uint8_t *dst = out + KV8_V_CODES + n * 2048 + lane * 16;
-                *reinterpret_cast<uint4 *>(dst) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-                *reinterpret_cast<uint4 *>(dst + 1024) = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+                nt_store16(dst, make_uint4(ow[0], ow[1], ow[2], ow[3]));
+                nt_store16(dst + 1024, make_uint4(ow[4], ow[5], ow[6], ow[7]));
             } else {
                 const int e = mx_exp(absmax32(y), 2);
                 const float inv = pow2_neg(e);
 #pragma unroll
                 for (int u = 0; u < 32; ++u) y[u] = y[u] * inv;
-                *reinterpret_cast<uint4 *>(out + KV_V_CODES + n * 1024 + lane * 16) = pack32_e2m1(y);
+                nt_store16(out + KV_V_CODES + n * 1024 + lane * 16, pack32_e2m1(y));
                 eb = (uint32_t)(e + 127);
             }
             sc[n >> 2] |= eb << (8 * (n & 3));
         }
-        *reinterpret_cast<uint2 *>(out + (FP8 ? KV8_V_SCALES : KV_V_SCALES) + lane * 8) = make_uint2(sc[0], sc[1]);
+        nt_store8(out + (FP8 ? KV8_V_SCALES : KV_V_SCALES) + lane * 8, sc[0], sc[1]);
     }
 }
 

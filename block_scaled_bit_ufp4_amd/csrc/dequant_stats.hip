@@ -2,7 +2,7 @@
 // attenuation reductions.
 //
 // Dequantization is code x scale, with IF4's INT4 blocks scaled by 6/7 (IF4
-// page, 3.1.1).  The statistics are those the pages use to judge a format:
+// page, 3.1.1).  The statistics are those the pages use to compare formats:
 // SQNR and the signal factor alpha of A_hat = alpha A + R ("当你的 GPU 学不会
 // 算账" sections "治病药反而喂养了病菌" and "复利效应的反向版本"), per-cell
 // rounding bias (section "E2M1：一块刻度不均的尺子"; "蚂蚁集团揭秘" 二) and IF4's

@@ -151,22 +151,18 @@ __device__ __forceinline__ void block_reduce_store(double (&acc)[NV], double *ou
     }
 }
 
-// One workgroup adds nwg rows of NV partial sums (fixed order).
+// One workgroup adds nwg rows of NV partial sums in a fixed order: wave w
+// takes sums w, w + 4, ...; for each, lane l adds rows l, l + 64, ... and the
+// wave adds its lanes by shuffles.  No barriers.
 template <int NV>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const double *partials, int nwg, double *sums)
 {
-    __shared__ double red[256];
-    for (int k = 0; k < NV; ++k) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int k = wave; k < NV; k += 4) {
         double v = 0.0;
-        for (int i = threadIdx.x; i < nwg; i += 256) v += partials[(int64_t)i * NV + k];
-        red[threadIdx.x] = v;
-        __syncthreads();
-        for (int w = 128; w >= 1; w >>= 1) {
-            if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-            __syncthreads();
-        }
-        if (threadIdx.x == 0) sums[k] = red[0];
-        __syncthreads();
+        for (int i = lane; i < nwg; i += 64) v += partials[(int64_t)i * NV + k];
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0) sums[k] = v;
     }
 }
 

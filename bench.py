@@ -451,6 +451,15 @@ def bench_configs(U, S, torch, dev, stream):
     ws = torch.empty(U.ufp4_workspace_size(U.OP_AMAX, ROWS, COLS, cfg), dtype=torch.uint8, device=dev)
     ms = _time(lambda: U.ufp4_amax(x, cfg, out=amax, ws=ws), torch, stream, 10)
     c2["amax_pass"] = {"us": round(ms * 1e3, 2), "GBps": round(2 * x.numel() / (ms * 1e-3) / 1e9, 1)}
+    # the statistics and the dequantize (with the inverse RHT) of the E2M1 quantization
+    q = U.ufp4_quantize(x, cfg, amax=U.ufp4_amax(x, cfg))
+    sums = torch.empty(U.NSUMS, dtype=torch.float64, device=dev)
+    sws = torch.empty(U.ufp4_workspace_size(U.OP_STATS, ROWS, COLS, cfg), dtype=torch.uint8, device=dev)
+    c2["stats_e2m1_us"] = round(_time(lambda: U.ufp4_stats(x, q, sums=sums, ws=sws), torch, stream, 5) * 1e3, 2)
+    y = torch.empty((ROWS, COLS), dtype=torch.float32, device=dev)
+    c2["dequant_inverse_rht_f32_us"] = round(
+        _time(lambda: U.ufp4_dequantize(q, inverse_rht=True, y=y), torch, stream, 10) * 1e3, 2)
+    del y
     c2["rht_overhead_e2m1"] = round(c2["e2m1_random"]["us"] / c2["e2m1_none"]["us"] - 1, 4)
     # unfused: the RHT as a kernel of its own, then the quantize reading its
     # output without the RHT; an fp32 intermediate gives the fused kernel's codes

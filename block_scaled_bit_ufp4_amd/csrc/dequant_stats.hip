@@ -168,24 +168,37 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const double *part
 
 // ---------------------------------------------------------------------------
 // Statistics: one thread per block of the view.  Row axis: consecutive lanes
-// take consecutive blocks of a view row; column axis: consecutive lanes take
-// consecutive view rows (= source columns), so the loads x[l][v] coalesce.
+// take consecutive blocks of a view row, and a block's elements are one
+// vector load; column axis: consecutive lanes take consecutive view rows (=
+// source columns), so the loads x[l][v] coalesce.  The per-code counts and
+// rounding-bias sums (32 of the 48) live in LDS bins private to each thread:
+// an element adds to its own code's bin with one LDS atomic, in element order,
+// so every bin is the same binary64 sum as a register accumulator would hold.
 // ---------------------------------------------------------------------------
 constexpr int NS = 48;
+constexpr int STATS_T = 256;
 
 template <int F, int S, int IN, bool RHT>
-__global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a)
+__global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
 {
     constexpr int B = block_of(S);
     constexpr int FG = F == FMT_IF4 ? FMT_E2M1 : F;
-    double acc[NS];
+    __shared__ double bias_bin[16][STATS_T];   // code k (FP4) or 8 + k (INT4 blocks of IF4)
+    __shared__ uint32_t count_bin[16][STATS_T];
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int k = 0; k < NS; ++k) acc[k] = 0.0;
+    for (int q = 0; q < 16; ++q) {
+        bias_bin[q][tid] = 0.0;
+        count_bin[q][tid] = 0u;
+    }
+    double acc[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) acc[k] = 0.0;
     float alpha = 0.0f;
     if constexpr (S == SC_E4M3) alpha = *a.tensor_scale;
     const int64_t nb_row = a.L / B;
     const int64_t nblocks = a.V * nb_row;
-    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < nblocks; t += (int64_t)gridDim.x * 256) {
+    for (int64_t t = (int64_t)blockIdx.x * STATS_T + tid; t < nblocks; t += (int64_t)gridDim.x * STATS_T) {
         int64_t v, j;
         if (a.axis == 0) {
             v = t / nb_row;
@@ -195,14 +208,41 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a)
             v = t - j * a.V;
         }
         float y[B];
+        if (a.axis == 0) {
+            // the block is contiguous and 16-byte aligned (x aligned, ldx a multiple of 8)
+            const int64_t idx = v * a.ldx + j * B;
+            if constexpr (IN == IN_BF16) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + idx);
 #pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const int64_t l = j * B + i;
-            const int64_t idx = a.axis == 0 ? v * a.ldx + l : l * a.ldx + v;
-            if constexpr (IN == IN_BF16)
-                y[i] = u2f((uint32_t)static_cast<const uint16_t *>(a.x)[idx] << 16);
-            else
-                y[i] = static_cast<const float *>(a.x)[idx];
+                for (int c = 0; c < B / 8; ++c) {
+                    const uint4 w = p[c];
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        y[8 * c + 2 * h] = u2f(ws[h] << 16);
+                        y[8 * c + 2 * h + 1] = u2f(ws[h] & 0xFFFF0000u);
+                    }
+                }
+            } else {
+                const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + idx);
+#pragma unroll
+                for (int c = 0; c < B / 4; ++c) {
+                    const float4 w = p[c];
+                    y[4 * c] = w.x;
+                    y[4 * c + 1] = w.y;
+                    y[4 * c + 2] = w.z;
+                    y[4 * c + 3] = w.w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                const int64_t idx = (j * B + i) * a.ldx + v;
+                if constexpr (IN == IN_BF16)
+                    y[i] = u2f((uint32_t)static_cast<const uint16_t *>(a.x)[idx] << 16);
+                else
+                    y[i] = static_cast<const float *>(a.x)[idx];
+            }
         }
         if constexpr (RHT) {
 #pragma unroll
@@ -227,12 +267,17 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a)
         }
         const float inv = s == 0.0f ? 0.0f : 1.0f / s;
         const bool fast = fast_div_ok(s);
-        const uint8_t *cp = a.codes + (v * a.L + j * B) / 2;
+        // the block's B / 2 code bytes as 32-bit words (codes are 4-byte aligned)
+        uint32_t cw[B / 8];
+        const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.codes + (v * a.L + j * B) / 2);
+#pragma unroll
+        for (int i = 0; i < B / 8; ++i) cw[i] = cp[i];
         acc[7] += 1.0;
         acc[8] += int4 ? 1.0 : 0.0;
+        const int bin0 = int4 ? 8 : 0;
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const uint32_t c = (cp[i >> 1] >> (4 * (i & 1))) & 15u;
+            const uint32_t c = (cw[i >> 3] >> (4 * (i & 7))) & 15u;
             const uint32_t k = c & 7u;
             float xm, g, ta;
             if (int4) {
@@ -262,40 +307,49 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a)
             acc[4] += (yy > 0.0 ? e : (yy < 0.0 ? -e : 0.0));
             acc[5] += xh * yy;
             acc[6] += fabs(e);
-            const double bias = (double)g - (double)z;
-            const int tb = int4 ? 8 : 0;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const bool hit = (int)k == q;
-                acc[16 + q] += (hit && !int4) ? 1.0 : 0.0;
-                acc[24 + q] += (hit && int4) ? 1.0 : 0.0;
-                acc[32 + q] += (hit && !int4) ? bias : 0.0;
-                acc[40 + q] += (hit && int4) ? bias : 0.0;
-            }
-            (void)tb;
+            atomicAdd(&bias_bin[bin0 + k][tid], (double)g - (double)z);
+            atomicAdd(&count_bin[bin0 + k][tid], 1u);
         }
     }
-    block_reduce_store<NS>(acc, a.partials + (int64_t)blockIdx.x * NS);
+    double out[NS];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) out[k] = acc[k];
+#pragma unroll
+    for (int k = 9; k < 16; ++k) out[k] = 0.0;
+    // each thread reads back only its own bins (its own LDS atomics are done
+    // in order before these reads)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        out[16 + q] = (double)count_bin[q][tid];
+        out[24 + q] = (double)count_bin[8 + q][tid];
+        out[32 + q] = bias_bin[q][tid];
+        out[40 + q] = bias_bin[8 + q][tid];
+    }
+    block_reduce_store<NS>(out, a.partials + (int64_t)blockIdx.x * NS);
 }
 
 template <int F, int S>
 static hipError_t stats_pick(int in_dtype, int rht, const StatsArgs &a, hipStream_t st)
 {
     const int64_t nblocks = a.V * (a.L / block_of(S));
-    int64_t g = (nblocks + 255) / 256;
-    if (g > STATS_WGS) g = STATS_WGS;
+    int64_t g = (nblocks + STATS_T - 1) / STATS_T;
+    // the 48 KiB of LDS bins fit three workgroups on a CU: one full wave of
+    // them over the 256 CUs, no tail (the workspace holds STATS_WGS rows)
+    constexpr int64_t kResident = 3 * 256;
+    static_assert(kResident <= STATS_WGS, "stats grid");
+    if (g > kResident) g = kResident;
     if (g < 1) g = 1;
     const dim3 grid((unsigned)g);
     if (in_dtype == IN_BF16) {
         if (rht)
-            launch_kernel((stats_kernel<F, S, IN_BF16, true>), grid, dim3(256), st, a);
+            launch_kernel((stats_kernel<F, S, IN_BF16, true>), grid, dim3(STATS_T), st, a);
         else
-            launch_kernel((stats_kernel<F, S, IN_BF16, false>), grid, dim3(256), st, a);
+            launch_kernel((stats_kernel<F, S, IN_BF16, false>), grid, dim3(STATS_T), st, a);
     } else {
         if (rht)
-            launch_kernel((stats_kernel<F, S, IN_F32, true>), grid, dim3(256), st, a);
+            launch_kernel((stats_kernel<F, S, IN_F32, true>), grid, dim3(STATS_T), st, a);
         else
-            launch_kernel((stats_kernel<F, S, IN_F32, false>), grid, dim3(256), st, a);
+            launch_kernel((stats_kernel<F, S, IN_F32, false>), grid, dim3(STATS_T), st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -1,4 +1,4 @@
-"""The library's calls under HIP graph capture: they allocate nothing and
+"""Reentrancy and graph capture.  The library's calls allocate nothing and
 record no memset, so a captured sequence (tensor amax, quantize with RTNE and
 with stochastic rounding, column quantize, dequantize, statistics, both GEMM
 modes, KV-cache quantize and a split KV decode) replays to the eager results
@@ -142,3 +142,53 @@ def test_graph_replays_match_eager():
                 g_ = g_.reshape(B, Hkv, npages, pb)[keep]
                 w_ = w_.reshape(B, Hkv, npages, pb)[keep]
             np.testing.assert_array_equal(g_, w_, err_msg=f"replay {rep}: {name}")
+
+
+def test_concurrent_streams_and_threads_match_sequential():
+    """Calls are reentrant: different quantizations and GEMMs issued at once on
+    two streams, from two host threads, give the sequential results bit for
+    bit (the library keeps no state between calls besides a per-thread
+    last error)."""
+    import threading
+    import torch
+    import block_scaled_bit_ufp4_amd as U
+    x = to_device_bf16(S.activations_t3(1024, 2048, seed=31))
+    a = to_device_bf16(S.normal(512, 1024, 1.0, 32, "gemm_a"))
+    b = to_device_bf16(S.normal(512, 1024, 1.0, 32, "gemm_b"))
+    jobs = [
+        lambda st: U.ufp4_quantize(x, U.Cfg("e2m1", "e4m3", rht="random", rht_seed=1),
+                                   amax=U.ufp4_amax(x, U.Cfg("e2m1", "e4m3", rht="random", rht_seed=1), stream=st),
+                                   stream=st).codes,
+        lambda st: U.ufp4_quantize(x, U.Cfg("e1m2", "fp32", rht="random", rht_seed=1, rounding="sr", sr_seed=5,
+                                            axis="col"), stream=st).codes,
+        lambda st: U.ufp4_qgemm(U.ufp4_quantize(a, U.Cfg("e2m1", "e8m0", 32), stream=st),
+                                U.ufp4_quantize(b, U.Cfg("e2m1", "e8m0", 32), stream=st), "mxfp4", stream=st),
+        lambda st: U.ufp4_quantize(x, U.Cfg("if4", "e4m3"), stream=st).scales,
+    ]
+    torch.cuda.synchronize()
+    want = []
+    for job in jobs:
+        want.append(host(job(torch.cuda.current_stream())))
+    torch.cuda.synchronize()
+
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None] * len(jobs)
+
+    def worker(w):
+        torch.cuda.set_device(0)
+        st = streams[w]
+        with torch.cuda.stream(st):
+            for i in range(w, len(jobs), 2):
+                for _ in range(3):  # overlapping repeats on the same stream
+                    got[i] = job_out = jobs[i](st)
+                got[i] = job_out
+        st.synchronize()
+
+    threads = [threading.Thread(target=worker, args=(w,)) for w in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for i in range(len(jobs)):
+        np.testing.assert_array_equal(host(got[i]), want[i], err_msg=f"job {i}")

@@ -79,9 +79,27 @@ __global__ __launch_bounds__(DT) void dequant_kernel(const DeqArgs a)
             off = vr * a.ldy + (o - vr * L8) * 8;
         }
         if constexpr (OUT == IN_F32) {
-            float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.y) + off);
-            p[0] = make_float4(v[0], v[1], v[2], v[3]);
-            p[1] = make_float4(v[4], v[5], v[6], v[7]);
+            // A whole wave of consecutive octets in a contiguous output goes
+            // through LDS, so each of its two stores writes 1 KiB contiguously
+            // (per lane they would be 16-byte pieces 32 bytes apart).  The
+            // wave's LDS write and read execute in order: no barrier.
+            __shared__ float4 stage[DT / 64][128];
+            const int w = tid >> 6, l = tid & 63;
+            const int64_t o0 = o - l;  // the octet of lane 0
+            if (a.ldy == a.L && o0 + 63 < a.n_oct) {
+                stage[w][2 * l] = make_float4(v[0], v[1], v[2], v[3]);
+                stage[w][2 * l + 1] = make_float4(v[4], v[5], v[6], v[7]);
+                const float4 q0 = stage[w][l], q1 = stage[w][64 + l];
+                typedef float f32x4 __attribute__((ext_vector_type(4)));
+                f32x4 *p = reinterpret_cast<f32x4 *>(static_cast<float *>(a.y) + o0 * 8);
+                const f32x4 r0 = {q0.x, q0.y, q0.z, q0.w}, r1 = {q1.x, q1.y, q1.z, q1.w};
+                __builtin_nontemporal_store(r0, p + l);
+                __builtin_nontemporal_store(r1, p + 64 + l);
+            } else {
+                float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.y) + off);
+                p[0] = make_float4(v[0], v[1], v[2], v[3]);
+                p[1] = make_float4(v[4], v[5], v[6], v[7]);
+            }
         } else {
             uint4 w;
             w.x = to_bf16(v[0]) | (to_bf16(v[1]) << 16);

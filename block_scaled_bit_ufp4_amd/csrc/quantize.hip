@@ -40,6 +40,7 @@ constexpr int RUA = 8;   // row kernel: chunks per lane in the amax pass
 // input, which the next quantization of the same tensor re-reads.
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void nt_store16(void *p, uint32_t x, uint32_t y, uint32_t z, uint32_t w)
 {
     const u32x4 v = {x, y, z, w};
@@ -386,9 +387,30 @@ __device__ __forceinline__ void row_chunk(const RowArgs &a, int64_t ch, float *v
             off = vr * a.ldy + (ch - vr * L16) * 16;
         }
         if constexpr (OUT == IN_F32) {
-            float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.y) + off);
+            // A whole wave of consecutive chunks in a contiguous output goes
+            // through LDS, so each of its four stores writes 1 KiB contiguously
+            // (per lane they would be 16-byte pieces 64 bytes apart); the
+            // stores are non-temporal.  The wave's LDS write and read execute
+            // in order: no barrier.
+            __shared__ float4 stage[RT / 64][256];
+            const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+            const int64_t ch0 = ch - l;  // the chunk of lane 0
+            if (a.ldy == a.L && ch0 + 63 < a.n_ch) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+                for (int q = 0; q < 4; ++q)
+                    stage[w][4 * l + q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+                f32x4 *p = reinterpret_cast<f32x4 *>(static_cast<float *>(a.y) + ch0 * 16);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 t = stage[w][64 * q + l];
+                    const f32x4 r = {t.x, t.y, t.z, t.w};
+                    __builtin_nontemporal_store(r, p + 64 * q + l);
+                }
+            } else {
+                float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.y) + off);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            }
         } else {
             uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + off);
 #pragma unroll

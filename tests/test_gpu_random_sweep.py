@@ -1,8 +1,10 @@
-"""Seeded random sweep of the quantizer against the oracle: random view
+"""Seeded random sweeps against the oracle.  The quantizer: random view
 shapes (ragged against every tile), every supported configuration, random
 transform and rounding seeds and streams, input kinds from heavy-tailed to
 tiny (1e-30) and sparse, bf16 and binary32 sources.  Codes, scales, tensor
-scale and the dequantized values must match bit for bit."""
+scale and the dequantized values must match bit for bit.  The GEMMs: random
+shapes and operand formats in both modes.  The KV decode: random shapes,
+lengths, splits, rotation and cache format."""
 import random
 
 import numpy as np
@@ -64,3 +66,62 @@ def test_random_sweep_bit_exact(master):
         got = host(U.ufp4_dequantize(q))
         ref = O.dequantize(want, ocfg, xo.shape)
         np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32), err_msg=tag)
+
+
+def _rel_fro(got, want):
+    return float(np.linalg.norm(got.astype(np.float64) - want) / np.linalg.norm(want))
+
+
+@pytest.mark.parametrize("master", [21, 22])
+def test_random_gemm_sweep(master):
+    """Random GEMM shapes (M, N multiples of 256, K of 128) and operand
+    formats in both modes, against the oracle's binary64 product of its own
+    dequantized (for the bf16 mode, bf16-rounded) operands."""
+    import block_scaled_bit_ufp4_amd as U
+    rng = random.Random(master)
+    for it in range(8):
+        M, N, K = 256 * rng.randint(1, 5), 256 * rng.randint(1, 5), 128 * rng.randint(1, 16)
+        mode = rng.choice(["mxfp4", "bf16"])
+        seed = rng.randint(0, 10 ** 6)
+        rht = rng.choice(["none", "random", "det"])
+        if mode == "mxfp4":
+            cfg = U.Cfg("e2m1", "e8m0", 32, rht=rht, rht_seed=seed)
+        else:
+            fmt = rng.choice(["e1m2", "int4", "e2m1", "if4", "e2m1_max3"])
+            scale = "e4m3" if fmt == "if4" else rng.choice(["fp32", "e4m3"])
+            cfg = U.Cfg(fmt, scale, rht=rht, rht_seed=seed)
+        a = S.activations_t3(M, K, seed=seed)
+        b = S.normal(N, K, 1.0, seed + 1, "gemm_b")
+        qa, qb = U.ufp4_quantize(to_device_bf16(a), cfg), U.ufp4_quantize(to_device_bf16(b), cfg)
+        z = host(U.ufp4_qgemm(qa, qb, mode))
+        ocfg = oracle_cfg(cfg)
+        bf = mode == "bf16"
+        opa = O.dequantize(O.quantize(a, ocfg), ocfg, a.shape)
+        opb = O.dequantize(O.quantize(b, ocfg), ocfg, b.shape)
+        want = O.gemm_nt(O.bf16_round(opa) if bf else opa, O.bf16_round(opb) if bf else opb)
+        err = _rel_fro(z, want)
+        assert err < 1e-5, f"case {it}: {mode} {cfg} {(M, N, K)}: {err}"
+
+
+@pytest.mark.parametrize("master", [31, 32])
+def test_random_kv_decode_sweep(master):
+    """Random batches, heads, group sizes, capacities, ragged lengths (zero
+    and full included), splits, rotation and cache format, against the
+    oracle's decode within its bound."""
+    import math
+    import torch
+    import block_scaled_bit_ufp4_amd as U
+    from test_gpu_kv import check_against_oracle
+    rng = random.Random(master)
+    for it in range(5):
+        B, Hkv, G = rng.randint(1, 3), rng.randint(1, 3), rng.choice([1, 2, 4, 8, 16])
+        L = 128 * rng.randint(1, 12)
+        lens = np.array([rng.choice([0, L, rng.randint(1, L)]) for _ in range(B)], np.int32)
+        rotate, fmt, pps = rng.choice([True, False]), rng.choice(["fp4", "fp8"]), rng.choice([0, 1, 2, 3, 8])
+        q, k, v = S.kv_decode(B, G * Hkv, Hkv, L, seed=rng.randint(0, 10 ** 6))
+        sm = 1.0 / math.sqrt(128)
+        d_lens = torch.from_numpy(lens).cuda()
+        cache = U.ufp4_kv_cache_quantize(to_device_bf16(k), to_device_bf16(v), d_lens, rotate, fmt=fmt)
+        out = host(U.ufp4_kv_decode(to_device_bf16(q), cache, d_lens, Hkv, L, sm, rotate, pages_per_split=pps,
+                                    fmt=fmt))
+        check_against_oracle(out, q, k, v, lens, Hkv, rotate, sm, fmt=fmt)

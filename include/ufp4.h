@@ -28,7 +28,9 @@
  * Conventions shared by every call
  *   - Device pointers are HIP device memory owned by the caller; the library
  *     allocates nothing, keeps no pointer after a call returns and has no
- *     global state except the per-thread last HIP error.
+ *     global state except, per host thread, the last HIP error and a pending
+ *     ufp4_time_next_launch request.  Calls are reentrant and can be captured
+ *     in a HIP graph (no allocation, no memset).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; results are ordered by the stream.
  *   - Arguments are validated on the host before anything is enqueued; on a
@@ -341,9 +343,11 @@ int ufp4_version(void);
 
 /* Timing aid.  The next kernel this library launches from the calling thread
  * records its own start and end on start_event and stop_event (hipEvent_t
- * handles the caller created; hipExtLaunchKernel timestamps the dispatch
- * itself, so hipEventElapsedTime between them is the kernel's duration
- * without the gaps around it).  For ufp4_quantize that kernel is the
+ * handles the caller created; hipExtLaunchKernel attaches them to the
+ * dispatch itself, so no separate event commands run around it).  The events
+ * bracket the dispatch: on MI355X they read a few microseconds longer than
+ * the kernel's duration in a profiler's kernel trace, and the timed launch
+ * starts after a short gap.  For ufp4_quantize that kernel is the
  * quantize kernel, for ufp4_amax the amax pass, for ufp4_qgemm in
  * UFP4_GEMM_NATIVE_MXFP4 mode the GEMM.  The request is consumed by that
  * launch; passing two NULLs clears a pending one.  Per thread, no other

@@ -89,6 +89,11 @@ static_assert(ROWS_PER_WAVE == 64, "one scale row per lane");
 // copies each wave issues: operand data of one stage, scales of one group
 constexpr int DATA_COPIES = 2 * (ROWS_PER_WAVE / 16);
 constexpr int scale_copies(bool fp4, bool pad) { return fp4 ? (pad ? 8 : 2) : 0; }
+// The bf16 path issues each stage's operand copy in two halves at two points
+// of the step (see gemm_step), which shortens its step by about a fifth at
+// 8192^3; the FP4 path, held back by its clock rather than by issue, keeps
+// one copy point.
+constexpr bool split_copies(bool fp4) { return !fp4; }
 
 // Asynchronous global -> LDS copy of one stage's operand data, shared by the
 // waves: wave w copies tile rows 64 w .. 64 w + 63 of A and of B, 16 rows
@@ -132,28 +137,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_buffer(const uint8_t *bas
 // s0 .. s0 + 3 (each clamped to the last stage) into the slot's scale area:
 // wave w copies the 16 bytes of rows 64 w .. 64 w + 63, one row per lane, of
 // A's and B's scale rows; stage by stage (4 bytes a row) where K is not a
-// multiple of four stages.  (All copies of a call go through one restrict
+// multiple of four stages.  PART 0 and 1 copy only the first or the second
+// half of each wave's operand rows (and PART 1 no scales); PART 2 copies
+// everything.  (All copies of a call go through one restrict
 // pointer: the compiler tells LDS copies apart by the alias scopes of their
 // destinations and tracks only a few such scopes.)
-template <bool SCALES, bool PAD>
+template <bool SCALES, bool PAD, int PART = 2>
 __device__ __forceinline__ void copy_stage(uint8_t *__restrict__ st, __amdgpu_buffer_rsrc_t At,
                                            __amdgpu_buffer_rsrc_t Bt, __amdgpu_buffer_rsrc_t SAt,
                                            __amdgpu_buffer_rsrc_t SBt, const CopyOffsets &o, int kb, int s0, int nk,
                                            int wave)
 {
 #pragma unroll
-    for (int i = 0; i < ROWS_PER_WAVE / 16; ++i) {
+    for (int i = (PART == 1 ? ROWS_PER_WAVE / 32 : 0); i < (PART == 0 ? ROWS_PER_WAVE / 32 : ROWS_PER_WAVE / 16);
+         ++i) {
         const int R0 = ROWS_PER_WAVE * wave + 16 * i;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(At, (lds_void *)(st + ST_A + R0 * GKB), 16, o.a[i], kb, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(Bt, (lds_void *)(st + ST_B + R0 * GKB), 16, o.b[i], kb, 0, 0);
     }
-    if constexpr (SCALES && !PAD) {
+    if constexpr (SCALES && !PAD && PART != 1) {
         const int s = min(s0, nk - 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(SAt, (lds_void *)(st + SG_A + 16 * ROWS_PER_WAVE * wave), 16, o.sa,
                                                  4 * s, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(SBt, (lds_void *)(st + SG_B + 16 * ROWS_PER_WAVE * wave), 16, o.sb,
                                                  4 * s, 0, 0);
-    } else if constexpr (SCALES) {
+    } else if constexpr (SCALES && PART != 1) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s = min(s0 + j, nk - 1);
@@ -275,10 +283,16 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags &f, c
 // of four multiply zeroed fragments.  So the body has no branches around
 // matrix work and the scheduling barriers hold the order within it.  Restrict
 // slot pointers tell the compiler which slot each access touches, so the
-// copies into the other slots stay in flight.
+// copies into the other slots stay in flight.  Where the copies are split
+// (bf16), the barrier's copy takes the first half of each wave's rows of
+// stage k + 4, and the second half follows at the start of the next step,
+// into the same slot (pv there): every wave has passed the barrier behind
+// its last read of that slot, and the copies in flight at each wait are
+// still the four halves of stages k + 2 and k + 3.
 template <bool FP4, bool PAD>
 __device__ __forceinline__ void gemm_step(v16f (&acc)[TM][TN], Frags &f0, Frags &f1, ScaleGroup &g,
                                           uint8_t *__restrict__ cur, const uint8_t *__restrict__ nx,
+                                          uint8_t *__restrict__ pv,
                                           __amdgpu_buffer_rsrc_t At, __amdgpu_buffer_rsrc_t Bt,
                                           __amdgpu_buffer_rsrc_t SAt, __amdgpu_buffer_rsrc_t SBt, const CopyOffsets &o,
                                           int k, int nk, int j, int wave, int wm, int wn, int r32, int h)
@@ -286,6 +300,9 @@ __device__ __forceinline__ void gemm_step(v16f (&acc)[TM][TN], Frags &f0, Frags 
     // j = k mod 4, a constant at each call (one function for the four
     // positions: the compiler then keeps the slots' alias scopes apart)
     constexpr int SC = scale_copies(FP4, PAD);
+    constexpr int CP = split_copies(FP4) ? 0 : 2;
+    if constexpr (split_copies(FP4))
+        copy_stage<false, PAD, 1>(pv, At, Bt, SAt, SBt, o, min(k + 3, nk - 1) * GKB, 0, nk, wave);
     read_frags(f1, cur, 1, wm, wn, r32, h);
     if constexpr (PAD) mask_frags(f1, k < nk ? ~0u : 0u);  // a step past the end adds exact zeros
     mfma_step<FP4, 0>(acc, f0, g, j);
@@ -304,9 +321,9 @@ __device__ __forceinline__ void gemm_step(v16f (&acc)[TM][TN], Frags &f0, Frags 
     UFP4_CFENCE();
     UFP4_SCHED_FENCE();
     if (FP4 && j == 0)
-        copy_stage<true, PAD>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, k + 4, nk, wave);
+        copy_stage<true, PAD, CP>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, k + 4, nk, wave);
     else
-        copy_stage<false, PAD>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, 0, nk, wave);
+        copy_stage<false, PAD, CP>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, 0, nk, wave);
     read_frags(f0, nx, 0, wm, wn, r32, h);
     ScaleGroup gn;
     if (FP4 && j == 3) read_scales<PAD>(gn, nx, wm, wn, r32, h);
@@ -332,8 +349,14 @@ __device__ __forceinline__ void gemm_main(v16f (&acc)[TM][TN], uint8_t *__restri
     copy_stage<FP4, PAD>(P0, At, Bt, SAt, SBt, o, 0, 0, nk, wave);
     copy_stage<false, PAD>(P1, At, Bt, SAt, SBt, o, min(1, nk - 1) * GKB, 0, nk, wave);
     copy_stage<false, PAD>(P2, At, Bt, SAt, SBt, o, min(2, nk - 1) * GKB, 0, nk, wave);
-    copy_stage<false, PAD>(P3, At, Bt, SAt, SBt, o, min(3, nk - 1) * GKB, 0, nk, wave);
-    UFP4_WAIT_VM(3 * DATA_COPIES);
+    if constexpr (split_copies(FP4)) {
+        // stage 3's second half goes out at the start of step 0
+        copy_stage<false, PAD, 0>(P3, At, Bt, SAt, SBt, o, min(3, nk - 1) * GKB, 0, nk, wave);
+        UFP4_WAIT_VM(2 * DATA_COPIES + DATA_COPIES / 2);
+    } else {
+        copy_stage<false, PAD>(P3, At, Bt, SAt, SBt, o, min(3, nk - 1) * GKB, 0, nk, wave);
+        UFP4_WAIT_VM(3 * DATA_COPIES);
+    }
     UFP4_CFENCE();
     __builtin_amdgcn_s_barrier();
     UFP4_CFENCE();
@@ -341,14 +364,14 @@ __device__ __forceinline__ void gemm_main(v16f (&acc)[TM][TN], uint8_t *__restri
     ScaleGroup g{};
     read_frags(f0, P0, 0, wm, wn, r32, h);
     if constexpr (FP4) read_scales<PAD>(g, P0, wm, wn, r32, h);
-#define UFP4_STEP(J, CUR, NX) \
-    gemm_step<FP4, PAD>(acc, f0, f1, g, CUR, NX, At, Bt, SAt, SBt, o, kt + (J), nk, J, wave, wm, wn, r32, h)
+#define UFP4_STEP(J, CUR, NX, PV) \
+    gemm_step<FP4, PAD>(acc, f0, f1, g, CUR, NX, PV, At, Bt, SAt, SBt, o, kt + (J), nk, J, wave, wm, wn, r32, h)
     // whole groups of four steps; the steps past the end multiply zeros
     for (int kt = 0; kt < nk; kt += 4) {
-        UFP4_STEP(0, P0, P1);
-        UFP4_STEP(1, P1, P2);
-        UFP4_STEP(2, P2, P3);
-        UFP4_STEP(3, P3, P0);
+        UFP4_STEP(0, P0, P1, P3);
+        UFP4_STEP(1, P1, P2, P0);
+        UFP4_STEP(2, P2, P3, P1);
+        UFP4_STEP(3, P3, P0, P2);
     }
 #undef UFP4_STEP
     // no copy may still be writing LDS when the workgroup ends

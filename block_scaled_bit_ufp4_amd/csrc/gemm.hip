@@ -405,7 +405,10 @@ __global__ __launch_bounds__(GTH, 1) void gemm_kernel(const uint8_t *__restrict_
         gemm_main<FP4, PAD>(acc, ring[0], ring[1], ring[2], ring[3], A, B, SA, SB, lda, ldb, lds_a, lds_b, m0, n0, nk, wave, lane, wm, wn,
                             r32, h);
 
-    // epilogue: accumulator element e of lane l is C[8(e/4) + 4h + e%4][l%32]
+    // epilogue: accumulator element e of lane l is C[8(e/4) + 4h + e%4][l%32].
+    // The output is written once and not read back here, so its stores are
+    // non-temporal: they do not displace operand lines that the workgroups
+    // still running read from L2 (the bf16 GEMM gains 2-3 % at 8192^3).
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -413,7 +416,8 @@ __global__ __launch_bounds__(GTH, 1) void gemm_kernel(const uint8_t *__restrict_
             const int64_t rbase = m0 + (wm * TM + i) * 32 + 4 * h;
             const int64_t col = n0 + (wn * TN + j) * 32 + r32;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) C[(rbase + 8 * (e >> 2) + (e & 3)) * ldc + col] = acc[i][j][e];
+            for (int e = 0; e < 16; ++e)
+                __builtin_nontemporal_store(acc[i][j][e], &C[(rbase + 8 * (e >> 2) + (e & 3)) * ldc + col]);
         }
 }
 #undef UFP4_WAIT_VM

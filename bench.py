@@ -20,7 +20,9 @@ back-to-back launches over the rotating copies (inputs cold in HBM), with HIP
 events on the launch stream at the ends; a plain device copy of the input,
 timed the same way, gives the rate a copy reaches.  The `qgemm` object times the
 MXFP4 block-scaled GEMM at 8192^3 (A, B: N(0,1) bf16 -> RHT -> MXFP4).
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload,
+and `qgemm.cpu_baseline` the oracle's binary64 GEMM on 256 sampled rows of the
+8192^3 product (extrapolated to the full product, and labelled so).
 """
 import argparse
 import hashlib
@@ -60,6 +62,8 @@ def parse():
     p.add_argument("--no-kv", action="store_true", help="skip the FP4 KV-cache decode attention")
     p.add_argument("--cpu-rows", type=int, default=ROWS)
     p.add_argument("--cpu-reps", type=int, default=2)
+    p.add_argument("--cpu-gemm-rows", type=int, default=256,
+                   help="rows of the 8192^3 product the oracle GEMM computes for its cpu_baseline")
     p.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
                    help="host threads of the row-partitioned oracle timing (the box's CPU share is 16)")
     return p.parse_args()
@@ -124,6 +128,37 @@ def cpu_baseline(x_bits, rows, reps, threads):
             "seconds": round(dtn, 2),
             "single_thread": {"value": round(nbytes / dt1 / 1e9, 6), "seconds": round(dt1, 2), "cores": 1},
             "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+
+
+def cpu_gemm_baseline(S, rows, threads, M=8192, N=8192, K=8192):
+    """The oracle's binary64 GEMM (the plain triple loop) on the first `rows`
+    rows of Z = A B^T for the 8192^3 GEMM's bf16 inputs, row-partitioned over
+    `threads` host threads, and on rows / 16 of them on one thread; both
+    extrapolated to the full product and labelled so."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle as O
+
+    def widen(bits):  # bf16 bits -> the float32 values they hold
+        return (bits.astype(np.uint32) << 16).view(np.float32)
+
+    a = widen(S.gemm_a(M, K)[:rows])
+    b = np.ascontiguousarray(widen(S.gemm_b(N, K)))
+    r1 = max(1, rows // 16)
+    t0 = time.perf_counter()
+    O.gemm_nt(a[:r1], b)
+    dt1 = time.perf_counter() - t0
+    parts = [np.ascontiguousarray(a[i * rows // threads:(i + 1) * rows // threads]) for i in range(threads)]
+    with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(O.gemm_nt, parts, [b] * threads))
+        dtn = time.perf_counter() - t0
+    gf = 2.0 * rows * N * K / 1e9
+    return {"value": round(gf / dtn, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"binary64 Z = A B^T on {rows} of {M} rows ({gf:.1f} GFLOP), plain C, row-partitioned "
+                      f"over {threads} host threads: {dtn:.2f} s",
+            "extrapolated_full_product_s": round(dtn * M / rows, 1),
+            "single_thread": {"value": round(2.0 * r1 * N * K / 1e9 / dt1, 3), "rows": r1,
+                              "seconds": round(dt1, 2), "extrapolated_full_product_s": round(dt1 * M / r1, 1)}}
 
 
 def main():
@@ -237,6 +272,8 @@ def main():
         out["kv_decode"] = bench_kv(U, S, torch, dev, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x_bits, args.cpu_rows, args.cpu_reps, args.cpu_threads)
+        if not args.no_gemm:
+            out["qgemm"]["cpu_baseline"] = cpu_gemm_baseline(S, args.cpu_gemm_rows, args.cpu_threads)
     print(json.dumps(out), flush=True)
 
 

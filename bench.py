@@ -21,7 +21,7 @@ events on the launch stream at the ends; a plain device copy of the input,
 timed the same way, gives the rate a copy reaches.  The `qgemm` object times the
 MXFP4 block-scaled GEMM at 8192^3 (A, B: N(0,1) bf16 -> RHT -> MXFP4).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload,
-and `qgemm.cpu_baseline` the oracle's binary64 GEMM on 256 sampled rows of the
+and `qgemm.cpu_baseline` the oracle's binary64 GEMM on 1024 sampled rows of the
 8192^3 product (extrapolated to the full product, and labelled so).
 """
 import argparse
@@ -62,7 +62,7 @@ def parse():
     p.add_argument("--no-kv", action="store_true", help="skip the FP4 KV-cache decode attention")
     p.add_argument("--cpu-rows", type=int, default=ROWS)
     p.add_argument("--cpu-reps", type=int, default=2)
-    p.add_argument("--cpu-gemm-rows", type=int, default=256,
+    p.add_argument("--cpu-gemm-rows", type=int, default=1024,
                    help="rows of the 8192^3 product the oracle GEMM computes for its cpu_baseline")
     p.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
                    help="host threads of the row-partitioned oracle timing (the box's CPU share is 16)")

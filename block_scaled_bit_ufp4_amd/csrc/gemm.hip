@@ -18,8 +18,11 @@
 // asynchronous global -> LDS copies three stages ahead of the
 // multiplications.  The
 // 16-byte chunks of each row are XOR-swizzled so the 16-byte fragment reads
-// are free of bank conflicts.  Workgroups are ordered so that
-// the eight XCDs each work on a compact band of output tiles.
+// are free of bank conflicts.  The grid is persistent, one workgroup per
+// compute unit, each taking its tiles in turn through the same ring; tiles
+// are ordered so that the eight XCDs each work on a compact band of them.
+#include <atomic>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -131,6 +134,21 @@ __device__ __forceinline__ CopyOffsets copy_offsets(int64_t lda, int64_t ldb, in
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_buffer(const uint8_t *base)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, -1, 0x00020000);
+}
+
+// Buffer descriptors of one output tile: its A rows, B rows and (FP4) their
+// scale rows.
+struct TileBufs {
+    __amdgpu_buffer_rsrc_t a, b, sa, sb;
+};
+
+template <bool FP4>
+__device__ __forceinline__ TileBufs tile_bufs(const uint8_t *A, const uint8_t *B, const uint8_t *SA,
+                                              const uint8_t *SB, int64_t lda, int64_t ldb, int64_t lds_a,
+                                              int64_t lds_b, int64_t m0, int64_t n0)
+{
+    return TileBufs{tile_buffer(A + m0 * lda), tile_buffer(B + n0 * ldb), tile_buffer(FP4 ? SA + m0 * lds_a : A),
+                    tile_buffer(FP4 ? SB + n0 * lds_b : B)};
 }
 
 // One stage's copies into slot st; with SCALES, also the scales of stages
@@ -292,17 +310,21 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags &f, c
 template <bool FP4, bool PAD>
 __device__ __forceinline__ void gemm_step(v16f (&acc)[TM][TN], Frags &f0, Frags &f1, ScaleGroup &g,
                                           uint8_t *__restrict__ cur, const uint8_t *__restrict__ nx,
-                                          uint8_t *__restrict__ pv,
-                                          __amdgpu_buffer_rsrc_t At, __amdgpu_buffer_rsrc_t Bt,
-                                          __amdgpu_buffer_rsrc_t SAt, __amdgpu_buffer_rsrc_t SBt, const CopyOffsets &o,
-                                          int k, int nk, int j, int wave, int wm, int wn, int r32, int h)
+                                          uint8_t *__restrict__ pv, const TileBufs &tc, const TileBufs &tn,
+                                          const CopyOffsets &o, int k, int nk, int nk4, int j, int wave, int wm,
+                                          int wn, int r32, int h)
 {
     // j = k mod 4, a constant at each call (one function for the four
     // positions: the compiler then keeps the slots' alias scopes apart)
     constexpr int SC = scale_copies(FP4, PAD);
     constexpr int CP = split_copies(FP4) ? 0 : 2;
+    // ring stage s is this tile's stage s (clamped to its last) below nk4 and
+    // the next tile's stage s - nk4 from there (wave-uniform choices)
+    const bool n3 = k + 3 >= nk4, n4 = k + 4 >= nk4;
+    const int s3 = n3 ? k + 3 - nk4 : k + 3, s4 = n4 ? k + 4 - nk4 : k + 4;
+    const TileBufs b3 = n3 ? tn : tc, b4 = n4 ? tn : tc;
     if constexpr (split_copies(FP4))
-        copy_stage<false, PAD, 1>(pv, At, Bt, SAt, SBt, o, min(k + 3, nk - 1) * GKB, 0, nk, wave);
+        copy_stage<false, PAD, 1>(pv, b3.a, b3.b, b3.sa, b3.sb, o, min(s3, nk - 1) * GKB, 0, nk, wave);
     read_frags(f1, cur, 1, wm, wn, r32, h);
     if constexpr (PAD) mask_frags(f1, k < nk ? ~0u : 0u);  // a step past the end adds exact zeros
     mfma_step<FP4, 0>(acc, f0, g, j);
@@ -321,63 +343,114 @@ __device__ __forceinline__ void gemm_step(v16f (&acc)[TM][TN], Frags &f0, Frags 
     UFP4_CFENCE();
     UFP4_SCHED_FENCE();
     if (FP4 && j == 0)
-        copy_stage<true, PAD, CP>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, k + 4, nk, wave);
+        copy_stage<true, PAD, CP>(cur, b4.a, b4.b, b4.sa, b4.sb, o, min(s4, nk - 1) * GKB, s4, nk, wave);
     else
-        copy_stage<false, PAD, CP>(cur, At, Bt, SAt, SBt, o, min(k + 4, nk - 1) * GKB, 0, nk, wave);
+        copy_stage<false, PAD, CP>(cur, b4.a, b4.b, b4.sa, b4.sb, o, min(s4, nk - 1) * GKB, 0, nk, wave);
     read_frags(f0, nx, 0, wm, wn, r32, h);
     ScaleGroup gn;
     if (FP4 && j == 3) read_scales<PAD>(gn, nx, wm, wn, r32, h);
-    if constexpr (PAD) mask_frags(f0, k + 1 < nk ? ~0u : 0u);
+    if constexpr (PAD) mask_frags(f0, k + 1 < nk || k + 1 >= nk4 ? ~0u : 0u);
     mfma_step<FP4, 1>(acc, f1, g, j);
     UFP4_SCHED_FENCE();
     if (FP4 && j == 3) g = gn;
 }
 
+// The output tiles of a workgroup, one after another through one ring: the
+// copies that would re-read a tile's last stage past its end (steps nk4 - 4
+// .. nk4 - 1, nk4 = nk rounded up to whole groups of four) fetch the next
+// tile's stages 0 .. 3 into the slots that tile's steps use, so only the
+// first tile waits for a prologue, and the fragments and scales read at a
+// tile's last step are the next tile's first.
 template <bool FP4, bool PAD>
-__device__ __forceinline__ void gemm_main(v16f (&acc)[TM][TN], uint8_t *__restrict__ P0, uint8_t *__restrict__ P1,
-                                          uint8_t *__restrict__ P2, uint8_t *__restrict__ P3, const uint8_t *A, const uint8_t *B, const uint8_t *SA, const uint8_t *SB,
-                                          int64_t lda, int64_t ldb, int64_t lds_a, int64_t lds_b, int64_t m0,
-                                          int64_t n0, int nk, int wave, int lane, int wm, int wn, int r32, int h)
+__device__ __forceinline__ void gemm_tiles(uint8_t *__restrict__ P0, uint8_t *__restrict__ P1,
+                                           uint8_t *__restrict__ P2, uint8_t *__restrict__ P3, const uint8_t *A,
+                                           const uint8_t *B, const uint8_t *SA, const uint8_t *SB, int MT, int NT,
+                                           int64_t lda, int64_t ldb, int64_t lds_a, int64_t lds_b, int nk,
+                                           float *__restrict__ C, int64_t ldc, int wave, int lane, int wm, int wn,
+                                           int r32, int h)
 {
+    const int T = MT * NT, G = (int)gridDim.x;
+    const int nk4 = (nk + 3) & ~3;
     const CopyOffsets o = copy_offsets(lda, ldb, lds_a, lds_b, wave, lane);
-    // wave-uniform tile bases
-    const __amdgpu_buffer_rsrc_t At = tile_buffer(A + m0 * lda), Bt = tile_buffer(B + n0 * ldb);
-    const __amdgpu_buffer_rsrc_t SAt = tile_buffer(FP4 ? SA + m0 * lds_a : A);
-    const __amdgpu_buffer_rsrc_t SBt = tile_buffer(FP4 ? SB + n0 * lds_b : B);
-    // prologue: stages 0 .. 3 (the last stage again where there are fewer)
-    // and the scales of the first group
-    copy_stage<FP4, PAD>(P0, At, Bt, SAt, SBt, o, 0, 0, nk, wave);
-    copy_stage<false, PAD>(P1, At, Bt, SAt, SBt, o, min(1, nk - 1) * GKB, 0, nk, wave);
-    copy_stage<false, PAD>(P2, At, Bt, SAt, SBt, o, min(2, nk - 1) * GKB, 0, nk, wave);
-    if constexpr (split_copies(FP4)) {
-        // stage 3's second half goes out at the start of step 0
-        copy_stage<false, PAD, 0>(P3, At, Bt, SAt, SBt, o, min(3, nk - 1) * GKB, 0, nk, wave);
-        UFP4_WAIT_VM(2 * DATA_COPIES + DATA_COPIES / 2);
-    } else {
-        copy_stage<false, PAD>(P3, At, Bt, SAt, SBt, o, min(3, nk - 1) * GKB, 0, nk, wave);
-        UFP4_WAIT_VM(3 * DATA_COPIES);
-    }
-    UFP4_CFENCE();
-    __builtin_amdgcn_s_barrier();
-    UFP4_CFENCE();
+    int t = (int)blockIdx.x, tm, tn;
+    tile_of(t, MT, NT, tm, tn);
+    TileBufs tc = tile_bufs<FP4>(A, B, SA, SB, lda, ldb, lds_a, lds_b, (int64_t)tm * GBM, (int64_t)tn * GBN);
+
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
     Frags f0, f1;
     ScaleGroup g{};
-    read_frags(f0, P0, 0, wm, wn, r32, h);
-    if constexpr (FP4) read_scales<PAD>(g, P0, wm, wn, r32, h);
-#define UFP4_STEP(J, CUR, NX, PV) \
-    gemm_step<FP4, PAD>(acc, f0, f1, g, CUR, NX, PV, At, Bt, SAt, SBt, o, kt + (J), nk, J, wave, wm, wn, r32, h)
-    // whole groups of four steps; the steps past the end multiply zeros
-    for (int kt = 0; kt < nk; kt += 4) {
-        UFP4_STEP(0, P0, P1, P3);
-        UFP4_STEP(1, P1, P2, P0);
-        UFP4_STEP(2, P2, P3, P1);
-        UFP4_STEP(3, P3, P0, P2);
+    if (nk > 0) {
+        // prologue of the first tile: stages 0 .. 3 (the last stage again
+        // where there are fewer) and the scales of the first group
+        copy_stage<FP4, PAD>(P0, tc.a, tc.b, tc.sa, tc.sb, o, 0, 0, nk, wave);
+        copy_stage<false, PAD>(P1, tc.a, tc.b, tc.sa, tc.sb, o, min(1, nk - 1) * GKB, 0, nk, wave);
+        copy_stage<false, PAD>(P2, tc.a, tc.b, tc.sa, tc.sb, o, min(2, nk - 1) * GKB, 0, nk, wave);
+        if constexpr (split_copies(FP4)) {
+            // stage 3's second half goes out at the start of step 0
+            copy_stage<false, PAD, 0>(P3, tc.a, tc.b, tc.sa, tc.sb, o, min(3, nk - 1) * GKB, 0, nk, wave);
+            UFP4_WAIT_VM(2 * DATA_COPIES + DATA_COPIES / 2);
+        } else {
+            copy_stage<false, PAD>(P3, tc.a, tc.b, tc.sa, tc.sb, o, min(3, nk - 1) * GKB, 0, nk, wave);
+            UFP4_WAIT_VM(3 * DATA_COPIES);
+        }
+        UFP4_CFENCE();
+        __builtin_amdgcn_s_barrier();
+        UFP4_CFENCE();
+        read_frags(f0, P0, 0, wm, wn, r32, h);
+        if constexpr (FP4) read_scales<PAD>(g, P0, wm, wn, r32, h);
     }
+    for (;;) {
+        const int64_t m0 = (int64_t)tm * GBM, n0 = (int64_t)tn * GBN;
+        const bool more = t + G < T;
+        int tm2 = tm, tn2 = tn;
+        if (more) tile_of(t + G, MT, NT, tm2, tn2);
+        // the last tile's steps past its end re-read its own stages
+        const TileBufs tx = more ? tile_bufs<FP4>(A, B, SA, SB, lda, ldb, lds_a, lds_b, (int64_t)tm2 * GBM,
+                                                  (int64_t)tn2 * GBN)
+                                 : tc;
+#define UFP4_STEP(J, CUR, NX, PV) \
+    gemm_step<FP4, PAD>(acc, f0, f1, g, CUR, NX, PV, tc, tx, o, kt + (J), nk, nk4, J, wave, wm, wn, r32, h)
+        // whole groups of four steps; the steps past the end multiply zeros
+        for (int kt = 0; kt < nk; kt += 4) {
+            UFP4_STEP(0, P0, P1, P3);
+            UFP4_STEP(1, P1, P2, P0);
+            UFP4_STEP(2, P2, P3, P1);
+            UFP4_STEP(3, P3, P0, P2);
+        }
 #undef UFP4_STEP
+        // epilogue: accumulator element e of lane l is C[8(e/4) + 4h + e%4][l%32].
+        // The output is written once and not read back here, so its stores
+        // are non-temporal: they do not displace operand lines that the
+        // workgroups still running read from L2 (the bf16 GEMM gains 2-3 % at
+        // 8192^3).
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t rbase = m0 + (wm * TM + i) * 32 + 4 * h;
+                const int64_t col = n0 + (wn * TN + j) * 32 + r32;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    __builtin_nontemporal_store(acc[i][j][e], &C[(rbase + 8 * (e >> 2) + (e & 3)) * ldc + col]);
+                acc[i][j] = v16f{};
+            }
+        if (!more) break;
+        t += G;
+        tm = tm2;
+        tn = tn2;
+        tc = tx;
+    }
     // no copy may still be writing LDS when the workgroup ends
     UFP4_WAIT_VM(0);
 }
 
+// Persistent grid: workgroup w computes output tiles w, w + G, w + 2G, ...
+// (G = the grid size, at most one workgroup per compute unit; a multiple of
+// 8 keeps each workgroup's tiles in its XCD's band).
 template <bool FP4, bool PAD>
 __global__ __launch_bounds__(GTH, 1) void gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
                                                       const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
@@ -390,45 +463,39 @@ __global__ __launch_bounds__(GTH, 1) void gemm_kernel(const uint8_t *__restrict_
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / GWN, wn = wave % GWN;
     const int r32 = lane & 31, h = lane >> 5;
-    int tm, tn;
-    tile_of(blockIdx.x, M / GBM, N / GBN, tm, tn);
-    const int64_t m0 = (int64_t)tm * GBM, n0 = (int64_t)tn * GBN;
-
-    v16f acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
-
-    const int nk = (int)(kbytes / GKB);
-    if (nk > 0)
-        gemm_main<FP4, PAD>(acc, ring[0], ring[1], ring[2], ring[3], A, B, SA, SB, lda, ldb, lds_a, lds_b, m0, n0, nk, wave, lane, wm, wn,
-                            r32, h);
-
-    // epilogue: accumulator element e of lane l is C[8(e/4) + 4h + e%4][l%32].
-    // The output is written once and not read back here, so its stores are
-    // non-temporal: they do not displace operand lines that the workgroups
-    // still running read from L2 (the bf16 GEMM gains 2-3 % at 8192^3).
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t rbase = m0 + (wm * TM + i) * 32 + 4 * h;
-            const int64_t col = n0 + (wn * TN + j) * 32 + r32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                __builtin_nontemporal_store(acc[i][j][e], &C[(rbase + 8 * (e >> 2) + (e & 3)) * ldc + col]);
-        }
+    gemm_tiles<FP4, PAD>(ring[0], ring[1], ring[2], ring[3], A, B, SA, SB, M / GBM, N / GBN, lda, ldb, lds_a, lds_b,
+                         (int)(kbytes / GKB), C, ldc, wave, lane, wm, wn, r32, h);
 }
 #undef UFP4_WAIT_VM
 #undef UFP4_WAIT_VM_LDS
 #undef UFP4_CFENCE
 #undef UFP4_SCHED_FENCE
 
+// Workgroups of the persistent grid: one per compute unit of the current
+// device (the kernel's LDS ring fills a CU), at most one per tile.
+static unsigned gemm_grid(int64_t tiles)
+{
+    static std::atomic<int> cus[64];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        n = cus[dev].load(std::memory_order_relaxed);
+        if (n <= 0) {
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+                (void)hipGetLastError();  // fall back to the MI355X count below
+                n = 0;
+            } else {
+                cus[dev].store(n, std::memory_order_relaxed);
+            }
+        }
+    }
+    if (n <= 0) n = 256;
+    return (unsigned)(tiles < n ? tiles : n);
+}
+
 hipError_t launch_gemm_mxfp4(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb, int64_t M,
                              int64_t N, int64_t K, float *c, int64_t ldc, hipStream_t st)
 {
-    const dim3 grid((unsigned)((M / GBM) * (N / GBN)));
+    const dim3 grid(gemm_grid((M / GBM) * (N / GBN)));
     const int64_t nk = K / 2 / GKB;
     // whole groups of four stages with 16-byte aligned scale rows take the
     // 16-byte scale copies; any other K the per-stage ones
@@ -445,7 +512,7 @@ hipError_t launch_gemm_mxfp4(const uint8_t *a, const uint8_t *sa, const uint8_t 
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t M, int64_t N, int64_t K, int64_t lda,
                             int64_t ldb, float *c, int64_t ldc, hipStream_t st)
 {
-    const dim3 grid((unsigned)((M / GBM) * (N / GBN)));
+    const dim3 grid(gemm_grid((M / GBM) * (N / GBN)));
     const uint8_t *a8 = reinterpret_cast<const uint8_t *>(a), *b8 = reinterpret_cast<const uint8_t *>(b);
     if (((K * 2 / GKB) % 4) != 0)
         launch_kernel((gemm_kernel<false, true>), grid, dim3(GTH), st, a8, nullptr, b8, nullptr, (int)M,

@@ -75,6 +75,39 @@ def test_bf16_gemm_matches_oracle(M, N, K):
     assert rel_fro(z, want) < 1e-5
 
 
+
+@pytest.mark.parametrize("mode,K", [("mxfp4", 512), ("mxfp4", 384), ("bf16", 512), ("bf16", 384),
+                                    ("plain_bf16", 320), ("plain_bf16", 512)])
+def test_gemm_more_tiles_than_workgroups(mode, K):
+    """17 x 16 = 272 output tiles of 256 x 256, more than the persistent grid's
+    one workgroup per compute unit (256 on MI355X): the first workgroups go on
+    to a second tile, whose first stages they fetch during the first tile's
+    last steps.  K = 384 (MXFP4) and 320 (bf16) round the stage count up to a
+    whole group of four.  One sampled row in each tile row, all columns, so
+    every tile is checked against the oracle."""
+    U = lib()
+    M, N = 17 * 256, 16 * 256
+    a = S.normal(M, K, 1.0, 5, "gemm_a")
+    b = S.normal(N, K, 1.0, 5, "gemm_b")
+    rows = np.arange(17) * 256 + np.random.default_rng(7).integers(0, 256, 17)
+    import torch
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    if mode == "plain_bf16":
+        z = host(U.ufp4_gemm_bf16(to_device_bf16(a), to_device_bf16(b), c=c))
+        want = O.gemm_nt(S.bf16_bits_to_f32(a[rows]), S.bf16_bits_to_f32(b))
+    else:
+        cfg = U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=2) if mode == "mxfp4" else \
+            U.Cfg("e1m2", "fp32", rht="random", rht_seed=2)
+        z = host(U.ufp4_qgemm(U.ufp4_quantize(to_device_bf16(a), cfg), U.ufp4_quantize(to_device_bf16(b), cfg),
+                              mode, c=c))
+        ocfg = oracle_cfg(cfg)
+        bf = mode == "bf16"
+        want = O.gemm_nt(oracle_operand(a, ocfg, bf16=bf)[rows], oracle_operand(b, ocfg, bf16=bf))
+    assert rel_fro(z[rows], want) < 1e-5, rel_fro(z[rows], want)
+    # every element of every tile was written (the output starts as NaN)
+    assert np.isfinite(z).all()
+
+
 def test_eta_sums():
     U = lib()
     import torch

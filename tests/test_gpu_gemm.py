@@ -76,17 +76,19 @@ def test_bf16_gemm_matches_oracle(M, N, K):
 
 
 
-@pytest.mark.parametrize("mode,K", [("mxfp4", 512), ("mxfp4", 384), ("bf16", 512), ("bf16", 384),
-                                    ("plain_bf16", 320), ("plain_bf16", 512)])
-def test_gemm_more_tiles_than_workgroups(mode, K):
+@pytest.mark.parametrize("mode,K,nt", [("mxfp4", 512, 16), ("mxfp4", 384, 16), ("bf16", 512, 16), ("bf16", 384, 16),
+                                       ("plain_bf16", 320, 16), ("plain_bf16", 512, 16), ("mxfp4", 512, 17),
+                                       ("plain_bf16", 320, 17)])
+def test_gemm_more_tiles_than_workgroups(mode, K, nt):
     """17 x 16 = 272 output tiles of 256 x 256, more than the persistent grid's
     one workgroup per compute unit (256 on MI355X): the first workgroups go on
     to a second tile, whose first stages they fetch during the first tile's
     last steps.  K = 384 (MXFP4) and 320 (bf16) round the stage count up to a
-    whole group of four.  One sampled row in each tile row, all columns, so
-    every tile is checked against the oracle."""
+    whole group of four; 17 x 17 = 289 tiles, not a multiple of the eight
+    XCDs, take the plain grouped raster.  One sampled row in each tile row,
+    all columns, so every tile is checked against the oracle."""
     U = lib()
-    M, N = 17 * 256, 16 * 256
+    M, N = 17 * 256, nt * 256
     a = S.normal(M, K, 1.0, 5, "gemm_a")
     b = S.normal(N, K, 1.0, 5, "gemm_b")
     rows = np.arange(17) * 256 + np.random.default_rng(7).integers(0, 256, 17)

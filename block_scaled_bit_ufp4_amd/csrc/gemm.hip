@@ -295,10 +295,11 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags &f, c
 // copy latency hidden) while stage k + 1's first fragments are read under the
 // second K step.  Slot 0 receives the first stage of each group of four, and
 // with it the group's scales, which the wave reads into registers one step
-// ahead of the group.  Every step has the same shape: past the last stage,
-// the copy re-reads the last stage into the free slot and the reads of
-// "stage k + 1" go unused; the steps that round the count up to a multiple
-// of four multiply zeroed fragments.  So the body has no branches around
+// ahead of the group.  Every step has the same shape: past the last stage
+// the copy fetches the next tile's first stages (on a workgroup's last tile
+// it re-reads the last stage into the free slot, and the reads of "stage
+// k + 1" go unused); the steps that round the count up to a multiple of
+// four multiply zeroed fragments.  So the body has no branches around
 // matrix work and the scheduling barriers hold the order within it.  Restrict
 // slot pointers tell the compiler which slot each access touches, so the
 // copies into the other slots stay in flight.  Where the copies are split

@@ -187,3 +187,22 @@ def test_kv_decode_workspace_sizes():
     # of 128 pages need no split, 4 sequences are cut into 16 splits of 8 pages
     assert U.ufp4_kv_decode_workspace_size(32, 32, 8, 16384) == 0
     assert U.ufp4_kv_decode_workspace_size(1, 16, 4, 16384) == 1 * 16 * 16 * 130 * 4
+
+
+def test_package_without_the_library_fails_loudly(tmp_path):
+    """A copy of the package without libufp4.so refuses to import (no CPU
+    fallback exists to route to)."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.dirname(os.path.abspath(U.__file__))
+    dst = tmp_path / "block_scaled_bit_ufp4_amd"
+    dst.mkdir()
+    for name in os.listdir(src):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(src, name), dst / name)
+    assert not (dst / "libufp4.so").exists()
+    r = subprocess.run([sys.executable, "-c", "import block_scaled_bit_ufp4_amd"], cwd=str(tmp_path),
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)}, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libufp4.so not built" in r.stderr

@@ -34,7 +34,7 @@ namespace ufp4 {
 
 constexpr int RT = 256;  // row kernel: threads per workgroup
 constexpr int RU = 2;    // row kernel: 16-element chunks per lane (quantize, transform)
-constexpr int RUA = 8;   // row kernel: chunks per lane in the amax pass
+constexpr int RUA = 4;   // row kernel: chunks per lane in the amax pass (4 read cold fastest of 1-16)
 // Outputs are written with non-temporal stores: no pass reads its own codes
 // and scales back, and keeping them out of the caches leaves room for the
 // input, which the next quantization of the same tensor re-reads.

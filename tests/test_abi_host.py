@@ -119,7 +119,7 @@ def test_empty_inputs_are_no_ops():
 def test_workspace_sizes():
     assert U.ufp4_workspace_size(U.OP_STATS, 100, 64) == 1024 * 48 * 8
     assert U.ufp4_workspace_size(U.OP_ETA, 100, 64) == 1024 * 3 * 8
-    assert U.ufp4_workspace_size(U.OP_AMAX, 8192, 8192, U.Cfg()) == 2048 * 4      # one per 2048 chunks
+    assert U.ufp4_workspace_size(U.OP_AMAX, 8192, 8192, U.Cfg()) == 4096 * 4      # one per 1024 chunks
     assert U.ufp4_workspace_size(U.OP_AMAX, 16384, 4096, U.Cfg(axis="col")) == 64 * 32 * 4
     assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, U.Cfg("e1m2")) == 512 * 256 * 2
     assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, U.Cfg("e2m1", "e8m0", 32)) == 0

@@ -4,9 +4,9 @@
 // with their UE8M0 block scales straight into the scaled MFMA (FP4 tensors
 // with UE8M0 group scales on the native scaled-MFMA path: "FP4 训练 vs FP4
 // 推理", UltraQuant; MXFP4 blocks of 32 sharing an E8M0 exponent: MXFP4
-// page).  The bf16 path multiplies bf16 operands on the bf16 MFMA (the
-// software route for E1M2/INT4 that FP4-only hardware needs: same page, "保留
-// FP4 计算，用软件模拟 E1M2 / INT4 路径").  Both accumulate in binary32.
+// page).  The bf16 path multiplies bf16 operands on the bf16 MFMA: matrix
+// cores with no E1M2/INT4 input take those formats through software, as the
+// UFP4 section of the same page describes.  Both accumulate in binary32.
 //
 // Both paths move operands as bytes: a K-major row supplies 64 bytes per
 // pipeline stage (128 E2M1 codes or 32 bf16 values), and one 32x32 MFMA step

@@ -88,6 +88,7 @@ def lib():
         L.orc_dequantize.argtypes = [C.POINTER(OrcConfig), i64, i64, p, p, C.c_float, i32, i64, i64, p]
         L.orc_stats.argtypes = [p, i32, i64, i64, i64, C.POINTER(OrcConfig), C.c_float, i64, i64, p]
         L.orc_gemm_nt_f32.argtypes = [p, p, i64, i64, i64, i64, p]
+        L.orc_eta_sums.argtypes = [p, p, i64, p]
         L.orc_round_rtne_array.argtypes = [p, i64, i32, p]
         L.orc_round_sr_array.argtypes = [p, p, i64, i32, p]
         L.orc_e4m3_encode_array.argtypes = [p, i64, p]
@@ -271,6 +272,102 @@ def gemm_nt(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     Z = np.empty((M, N), dtype=np.float64)
     lib().orc_gemm_nt_f32(_ptr(A), _ptr(B), N, K, 0, M, _ptr(Z))
     return Z
+
+
+def eta_sums(zq: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """(<Zq,Z>, <Z,Z>, ||Zq-Z||^2) in binary64, summed in index order."""
+    zq = np.ascontiguousarray(zq, dtype=np.float64).ravel()
+    z = np.ascontiguousarray(z, dtype=np.float64).ravel()
+    assert zq.size == z.size
+    out = np.zeros(3, dtype=np.float64)
+    lib().orc_eta_sums(_ptr(zq), _ptr(z), zq.size, _ptr(out))
+    return out
+
+
+def eta_report(sums) -> dict:
+    """eta = <Zq,Z>/<Z,Z> and the output SQNR 10 log10(<Z,Z>/||Zq-Z||^2)."""
+    s = np.asarray(sums, dtype=np.float64)
+    return {"eta": s[0] / s[1] if s[1] > 0 else float("nan"),
+            "sqnr_db": 10.0 * np.log10(s[1] / s[2]) if s[2] > 0 else float("inf")}
+
+
+# ---- row-partitioned forms (threads) ----------------------------------------
+# The rows of a quantization view are independent once the tensor amax is
+# known, and the C functions run outside the interpreter lock, so whole
+# full-size tensors are checked by splitting the view rows over host threads.
+# Each thread writes its own rows of the shared output arrays.
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _row_ranges(V: int, threads: int):
+    threads = max(1, min(threads, V)) if V else 1
+    return [(i * V // threads, (i + 1) * V // threads) for i in range(threads)]
+
+
+def _run_parallel(fn, ranges):
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(ranges)) as ex:
+        return list(ex.map(lambda r: fn(*r), ranges))
+
+
+def amax_threads(x: np.ndarray, cfg: Cfg, threads: int = 0) -> float:
+    """Tensor amax, the max of the amaxes of row (or column) slices."""
+    x = np.ascontiguousarray(x)
+    V, _ = view_shape(x, cfg.axis)
+    parts = _row_ranges(V, threads or default_threads())
+    if cfg.axis == "row":
+        slices = [np.ascontiguousarray(x[a:b]) for a, b in parts]
+    else:
+        slices = [np.ascontiguousarray(x[:, a:b]) for a, b in parts]
+    return float(max(_run_parallel(lambda s: amax(s, cfg), [(s,) for s in slices])))
+
+
+def quantize_threads(x: np.ndarray, cfg: Cfg, amax_value=None, threads: int = 0) -> QResult:
+    """quantize() of the whole view, its rows split over host threads."""
+    x = np.ascontiguousarray(x)
+    V, L = view_shape(x, cfg.axis)
+    if cfg.scale == "e4m3" and amax_value is None:
+        amax_value = amax_threads(x, cfg, threads)
+    amax_value = 0.0 if amax_value is None else float(amax_value)
+    c = cfg.c()
+    codes = np.zeros((V, L // 2), dtype=np.uint8)
+    scales = np.zeros((V, L // cfg.block), dtype=np.float32 if cfg.scale == "fp32" else np.uint8)
+    alphas = _run_parallel(
+        lambda v0, v1: lib().orc_quantize(_ptr(x), _src(x), x.shape[0], x.shape[1], x.shape[1], C.byref(c),
+                                          amax_value, v0, v1, _ptr(codes), _ptr(scales)),
+        _row_ranges(V, threads or default_threads()))
+    if min(alphas) < 0:
+        raise ValueError(f"unsupported configuration {cfg}")
+    return QResult(codes, scales, float(np.float32(alphas[0])), amax_value)
+
+
+def dequantize_threads(q: QResult, cfg: Cfg, shape, inverse: bool = False, threads: int = 0) -> np.ndarray:
+    R, Cc = shape
+    V, L = (R, Cc) if cfg.axis == "row" else (Cc, R)
+    out = np.empty((V, L), dtype=np.float32)
+    c = cfg.c()
+    codes = np.ascontiguousarray(q.codes)
+    scales = np.ascontiguousarray(q.scales)
+    rcs = _run_parallel(
+        lambda v0, v1: lib().orc_dequantize(C.byref(c), R, Cc, _ptr(codes), _ptr(scales), q.alpha, int(inverse),
+                                            v0, v1, _ptr(out[v0:v1])),
+        _row_ranges(V, threads or default_threads()))
+    if any(rcs):
+        raise ValueError("bad configuration")
+    return out
+
+
+def stats_threads(x: np.ndarray, cfg: Cfg, amax_value=None, threads: int = 0) -> np.ndarray:
+    """stats() of the whole view: the sums of each thread's rows, added."""
+    x = np.ascontiguousarray(x)
+    V, _ = view_shape(x, cfg.axis)
+    if cfg.scale == "e4m3" and amax_value is None:
+        amax_value = amax_threads(x, cfg, threads)
+    parts = _run_parallel(lambda v0, v1: stats(x, cfg, v0, v1, amax_value),
+                          _row_ranges(V, threads or default_threads()))
+    return np.sum(parts, axis=0)
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:

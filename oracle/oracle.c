@@ -262,7 +262,7 @@ uint32_t orc_sr_word(uint64_t seed, uint32_t stream, uint64_t n)
  * random orthogonal rotation before quantization; [UFP4-TW] 六: Hadamard block
  * = quantization block = 16.  Reading: one diagonal d of 16 signs per tensor,
  * d_i = -1 iff bit i of Philox word 0 at key = seed, counter = (0,0,"RHT\0",0).
- * The deterministic H16 of [MXFP4] ("确定性Hadamard旋转") has d = +1.
+ * The deterministic H16 of [MXFP4] (its fixed, unrandomised rotation) has d = +1.
  * Returns the 16-bit mask of negative positions. */
 uint32_t orc_rht_sign_mask(int rht_kind, uint64_t seed)
 {
@@ -378,8 +378,8 @@ typedef struct {
  * correctly rounded binary32 division; a zero scale gives z = +0. */
 static float scaled(float y, float s) { return s == 0.0f ? 0.0f : y / s; }
 
-/* Dequantized value of a code on a plain grid: x_hat = v * s  ([IF4] 3.1.1
- * "dequantized = int_values * scale"). */
+/* Dequantized value of a code on a plain grid: its grid value times the
+ * block's effective scale ([IF4] 3.1.1). */
 static float deq_plain(int fmt, int code, float s)
 {
     float v = (float)orc_grid_value(fmt, code & 7);
@@ -387,14 +387,30 @@ static float deq_plain(int fmt, int code, float s)
     return v * s;
 }
 
-/* IF4 INT4 dequantization in the page's left-to-right order:
- * int_values * scale * (6/7)  ([IF4] 3.1.1). */
-static float deq_if4_int(int code, float s)
+/* IF4's INT4 candidate ([IF4] 3.1.1, 3.2).  The integer grid reaches 7 while
+ * E2M1 reaches 6, so with the shared block scale the integer levels are
+ * stretched: a value is enlarged by 7/6 before the scale divides it, and a
+ * level stands for 6/7 of (level x scale).  Reading in binary32 (each step
+ * rounded once): the level is |RN(RN(y * 7/6) / s)| rounded half to even and
+ * capped at 7; its value is RN(RN(level * s) * 6/7), where 7/6 and 6/7 are
+ * the binary32 constants nearest them. */
+static const float IF4_STRETCH = 7.0f / 6.0f;
+static const float IF4_SHRINK = 6.0f / 7.0f;
+
+static int if4_int_code(float y, float s)
 {
-    float k = (float)(code & 7);
-    if (code & 8) k = -k;
-    float t = k * s;
-    return t * (6.0f / 7.0f);
+    float z = (y * IF4_STRETCH) / s;
+    int level = (int)nearbyintf(fabsf(z)); /* default rounding mode: half to even */
+    if (level > 7) level = 7;
+    return (signbit(z) ? 8 : 0) | level;
+}
+
+static float if4_int_value(int code, float s)
+{
+    float level = (float)(code & 7);
+    if (code & 8) level = -level;
+    float scaled_level = level * s;
+    return scaled_level * IF4_SHRINK;
 }
 
 /* Quantize one block of B transformed values y[0..B). */
@@ -451,45 +467,42 @@ static void quantize_block(const orc_config *cfg, const float *y, int B, float a
         return;
     }
 
-    /* IF4 ([IF4] 3.1, 3.2): both candidates share the block scale; the INT4
-     * candidate stretches by 7/6 before rounding and shrinks by 6/7 on
-     * dequantization; the candidate with the smaller squared error wins and
-     * its type goes into the scale byte's sign bit (1 = INT4). */
-    int cf[16], ci[16];
-    float zf[16], zi[16], xf[16], xi[16], ef[16], ei[16];
+    /* IF4 ([IF4] 3.1, 3.2): every block gets both an E2M1 and an INT4
+     * candidate under the same scale; the one whose reconstruction is closer
+     * (smaller sum of squared errors) is kept, and bit 7 of the scale byte
+     * records which (1 = INT4).  Readings: the squared errors are binary32,
+     * summed as a balanced tree over neighbours (pairs, then pairs of pairs:
+     * four levels for 16 values), and an exact tie keeps E2M1. */
+    int fp4_code[16], int_code[16];
+    float fp4_z[16], int_z[16], fp4_val[16], int_val[16], fp4_sq[16], int_sq[16];
     for (int i = 0; i < B; ++i) {
         if (s == 0.0f) {
-            cf[i] = ci[i] = 0;
-            zf[i] = zi[i] = 0.0f;
+            fp4_code[i] = int_code[i] = 0;
+            fp4_z[i] = int_z[i] = 0.0f;
         } else {
-            zf[i] = y[i] / s;                          /* values / scale            */
-            float t = y[i] * (7.0f / 6.0f);            /* values * (7/6) / scale    */
-            zi[i] = t / s;
-            cf[i] = orc_round_rtne(zf[i], ORC_E2M1);
-            int k = (int)nearbyintf(fabsf(zi[i]));     /* round(): half to even    */
-            if (k > 7) k = 7;
-            ci[i] = (signbit(zi[i]) ? 8 : 0) | k;
+            fp4_z[i] = scaled(y[i], s);
+            fp4_code[i] = orc_round_rtne(fp4_z[i], ORC_E2M1);
+            int_code[i] = if4_int_code(y[i], s);
+            int_z[i] = (y[i] * IF4_STRETCH) / s;
         }
-        xf[i] = deq_plain(ORC_E2M1, cf[i], s);
-        xi[i] = deq_if4_int(ci[i], s);
-        float df = xf[i] - y[i], di = xi[i] - y[i];
-        ef[i] = df * df;
-        ei[i] = di * di;
+        fp4_val[i] = deq_plain(ORC_E2M1, fp4_code[i], s);
+        int_val[i] = if4_int_value(int_code[i], s);
+        float dev_fp4 = fp4_val[i] - y[i], dev_int = int_val[i] - y[i];
+        fp4_sq[i] = dev_fp4 * dev_fp4;
+        int_sq[i] = dev_int * dev_int;
     }
-    /* Squared-error sums in binary32, pairwise: (0+1),(2+3),... then pairs of
-     * pairs, four levels for 16 values. */
-    for (int w = 1; w < B; w <<= 1)
-        for (int i = 0; i < B; i += 2 * w) {
-            ef[i] = ef[i] + ef[i + w];
-            ei[i] = ei[i] + ei[i + w];
+    for (int span = 1; span < B; span <<= 1)
+        for (int i = 0; i < B; i += 2 * span) {
+            fp4_sq[i] = fp4_sq[i] + fp4_sq[i + span];
+            int_sq[i] = int_sq[i] + int_sq[i + span];
         }
-    int use_int = (s != 0.0f) && (ei[0] < ef[0]);      /* ties keep FP4 */
+    int use_int = (s != 0.0f) && (int_sq[0] < fp4_sq[0]);
     out->int4 = use_int;
     out->scale_b = (uint8_t)(out->scale_b | (use_int ? 0x80 : 0));
     for (int i = 0; i < B; ++i) {
-        out->code[i] = use_int ? ci[i] : cf[i];
-        out->zabs[i] = use_int ? fabsf(zi[i]) : fabsf(zf[i]);
-        out->xhat[i] = use_int ? xi[i] : xf[i];
+        out->code[i] = use_int ? int_code[i] : fp4_code[i];
+        out->zabs[i] = use_int ? fabsf(int_z[i]) : fabsf(fp4_z[i]);
+        out->xhat[i] = use_int ? int_val[i] : fp4_val[i];
     }
 }
 
@@ -567,7 +580,7 @@ int orc_dequantize(const orc_config *cfg, int64_t R, int64_t C, const uint8_t *c
             int code = (codes[e / 2] >> (4 * (e & 1))) & 15;
             int int4;
             float s = stored_scale(cfg, scales, v * (L / B) + l / B, alpha, &int4);
-            o[l] = int4 ? deq_if4_int(code, s) : deq_plain(cfg->format, code, s);
+            o[l] = int4 ? if4_int_value(code, s) : deq_plain(cfg->format, code, s);
         }
         if (inverse && cfg->rht != ORC_RHT_NONE) {
             for (int64_t c0 = 0; c0 < L; c0 += 16) {
@@ -650,6 +663,28 @@ void orc_gemm_nt_f32(const float *A, const float *B, int64_t N, int64_t K, int64
             for (int64_t k = 0; k < K; ++k) acc += (double)a[k] * (double)b[k];
             Z[(m - m0) * N + n] = acc;
         }
+}
+
+/* Attenuation of a GEMM output ([UFP4-ZC] "复利效应的反向版本"): a quantized
+ * operand behaves like a shrunk copy of the exact one plus noise that is
+ * uncorrelated with it, so the quantized product Zq carries a factor eta of
+ * the exact product Z = A B^T (both operands' factors multiplied) plus noise.
+ * eta is the least-squares factor <Zq, Z> / <Z, Z>; the output SQNR is
+ * 10 log10(<Z, Z> / ||Zq - Z||^2).  The three binary64 sums, element by
+ * element in index order: out[0] = <Zq, Z>, out[1] = <Z, Z>,
+ * out[2] = ||Zq - Z||^2. */
+void orc_eta_sums(const double *zq, const double *z, int64_t n, double out[3])
+{
+    double cross = 0.0, ref = 0.0, err = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double d = zq[i] - z[i];
+        cross += zq[i] * z[i];
+        ref += z[i] * z[i];
+        err += d * d;
+    }
+    out[0] = cross;
+    out[1] = ref;
+    out[2] = err;
 }
 
 /* Number of sums in a statistics record. */

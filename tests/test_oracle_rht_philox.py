@@ -50,6 +50,53 @@ def test_fwht_is_an_involution_and_keeps_the_norm():
     np.testing.assert_array_equal(O.fwht16(O.fwht16(v)), v)
 
 
+def _sylvester_f32(v: np.ndarray, halves_first: bool) -> np.ndarray:
+    """The Sylvester definition H_2n = [[H_n, H_n], [H_n, -H_n]] applied to
+    the rows of v (float32, any power-of-two length) with float32 rounding
+    at every addition.  halves_first: transform each half, then combine the
+    two (H_n a + H_n b, H_n a - H_n b); otherwise combine first and transform
+    the sum and the difference (H_n (a + b), H_n (a - b)).  Both equal H v in
+    exact arithmetic; they round differently."""
+    n = v.shape[-1]
+    if n == 1:
+        return v
+    a, b = v[..., : n // 2], v[..., n // 2:]
+    if halves_first:
+        ta, tb = _sylvester_f32(a, True), _sylvester_f32(b, True)
+        return np.concatenate([ta + tb, ta - tb], axis=-1)
+    return np.concatenate([_sylvester_f32(a + b, False), _sylvester_f32(a - b, False)], axis=-1)
+
+
+def _mixed_vectors(n: int, seed: int) -> np.ndarray:
+    """16-vectors whose entries span many binades and signs, so that most
+    float32 additions round."""
+    rng = np.random.default_rng(seed)
+    mag = 10.0 ** rng.uniform(-4, 4, size=(n, 16))
+    return np.float32(rng.standard_normal((n, 16)) * mag)
+
+
+def test_fwht_stage_order_matches_recursive_definition():
+    """The oracle's butterflies run spans 1, 2, 4, 8 in that order.  Written
+    as the recursion of the Sylvester definition, that order is "transform
+    each half, then combine the halves": the oracle must equal that recursion
+    (in float32, then x 1/4) bit for bit on 10^5 mixed-magnitude vectors.
+    The other order (spans 8, 4, 2, 1: combine first, then transform) rounds
+    differently on many of the same vectors, so the comparison can tell the
+    two orders apart."""
+    v = _mixed_vectors(100_000, 11)
+    want = _sylvester_f32(v, halves_first=True) * np.float32(0.25)
+    other = _sylvester_f32(v, halves_first=False) * np.float32(0.25)
+    got = np.stack([O.fwht16(r) for r in v])
+    assert want.dtype == np.float32 and got.dtype == np.float32
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    differ = np.any(other.view(np.uint32) != want.view(np.uint32), axis=1).mean()
+    assert differ > 0.5, differ
+    # the two recursions agree with scipy's matrix where nothing rounds
+    e = np.eye(16, dtype=np.float32)
+    np.testing.assert_array_equal(_sylvester_f32(e, True).astype(np.float64), H16)
+    np.testing.assert_array_equal(_sylvester_f32(e, False).astype(np.float64), H16)
+
+
 @pytest.mark.parametrize("axis", ["row", "col"])
 @pytest.mark.parametrize("kind", ["random", "det"])
 def test_rht_view_is_signed_hadamard(axis, kind):

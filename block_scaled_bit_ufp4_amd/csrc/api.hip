@@ -34,6 +34,14 @@ static int hip_fail(hipError_t e)
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The GEMM kernels address a 256-row tile of an operand through a buffer
+// descriptor with 32-bit offsets: row (< 256) times the row stride plus the
+// K offset must stay below 2^32 bytes.
+static bool gemm_offsets_fit(int64_t row_stride_bytes, int64_t k_bytes)
+{
+    return 256 * row_stride_bytes + k_bytes < ((int64_t)1 << 32);
+}
+
 // Host-side Philox4x32-10 word 0 for the sign diagonal (SC'11 round function).
 static uint32_t host_philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1)
 {
@@ -150,9 +158,9 @@ size_t ufp4_workspace_size(int op, int64_t rows, int64_t cols, const ufp4_config
         return (size_t)(t > 0 ? t : 1) * sizeof(float);
     }
     case UFP4_OP_QGEMM:
-        // dequantize-to-bf16 path: both operands as bf16 ((M + N) x K)
-        if (cfg && cfg->scale != UFP4_SCALE_E8M0) return (size_t)(rows * cols * 2);
-        return 0;
+        // the dequantize-to-bf16 mode holds both operands as bf16 ((M + N) x K),
+        // whatever their format; the native MXFP4 mode uses none of it
+        return rows > 0 && cols > 0 ? (size_t)(rows * cols * 2) : 0;
     }
     (void)rows;
     (void)cols;
@@ -324,6 +332,7 @@ int ufp4_gemm_bf16(const void *a, const void *b, int64_t M, int64_t N, int64_t K
     if (M < 0 || N < 0 || K < 0) return UFP4_ERR_SHAPE;
     if (M % 256 || N % 256 || K % 64) return UFP4_ERR_SHAPE;
     if (lda < K || ldb < K || ldc < N) return UFP4_ERR_SHAPE;
+    if (!gemm_offsets_fit(2 * lda, 2 * K) || !gemm_offsets_fit(2 * ldb, 2 * K)) return UFP4_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(b) || !aligned16(c) || lda % 8 || ldb % 8 || ldc % 4) return UFP4_ERR_ALIGN;
     if (M == 0 || N == 0) return UFP4_OK;
     return hip_fail(launch_gemm_bf16(static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), M, N, K, lda,
@@ -348,6 +357,9 @@ int ufp4_qgemm(const ufp4_qtensor *a, const ufp4_qtensor *b, int mode, float *c,
         return UFP4_ERR_UNSUPPORTED;
     if (M % 256 || N % 256 || K % 128) return UFP4_ERR_SHAPE;
     if (ldc < N || ldc % 4) return UFP4_ERR_SHAPE;
+    // native mode: code rows of K/2 bytes; dequantize mode: bf16 rows of 2K
+    if (!gemm_offsets_fit(mode == UFP4_GEMM_NATIVE_MXFP4 ? K / 2 : 2 * K, mode == UFP4_GEMM_NATIVE_MXFP4 ? K / 2 : 2 * K))
+        return UFP4_ERR_SHAPE;
     if (!aligned16(c)) return UFP4_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     if (mode == UFP4_GEMM_NATIVE_MXFP4) {

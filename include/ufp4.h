@@ -29,8 +29,10 @@
  *   - Device pointers are HIP device memory owned by the caller; the library
  *     allocates nothing, keeps no pointer after a call returns and has no
  *     global state except, per host thread, the last HIP error and a pending
- *     ufp4_time_next_launch request.  Calls are reentrant and can be captured
- *     in a HIP graph (no allocation, no memset).
+ *     ufp4_time_next_launch request, and, per process, each device's
+ *     compute-unit count (read once by the first GEMM on that device, never
+ *     changed after).  Calls are reentrant and can be captured in a HIP graph
+ *     (no allocation, no memset).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; results are ordered by the stream.
  *   - Arguments are validated on the host before anything is enqueued; on a
@@ -185,6 +187,12 @@ int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld
 
 /* Block quantization (all steps fused in one kernel: load, signs, FWHT, block
  * amax, scale, RTNE/SR or IF4 selection, nibble packing, stores).
+ * Definitions: the fused 16-wide RHT + quantize of [UFP4-TW] 六; the per-block
+ * scale of [UFP4-ZC]'s recipe table (single FP32 scale per 1x16 block), of
+ * [IF4] 3.2 (E4M3 block scale under the FP32 tensor scale alpha) or of [MXFP4]
+ * (E8M0 per 32); rounding to the grids of [UFP4-ZC] "E2M1：一块刻度不均的尺子"
+ * and "UFP4：换一把尺子" by RTNE ([UFP4-TW] 二) or stochastic rounding
+ * ([IF4] 6.1; [UFP4-TW] 五: dY only); IF4's per-block choice ([IF4] 3.1.1).
  * out->codes, out->scales (and out->tensor_scale for E4M3) must point to
  * buffers of the sizes above; out->rows/cols/cfg are filled in by the call.
  * amax: device float from ufp4_amax (required for E4M3, ignored otherwise).
@@ -199,7 +207,11 @@ int ufp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_
 int ufp4_dequantize(const ufp4_qtensor *q, int inverse_rht, void *y, int y_dtype, int64_t ldy, void *stream);
 
 /* Quantization statistics of q against the source x it was made from (same
- * dtype/ldx as the quantize call).  Writes UFP4_NSUMS doubles to sums (device).
+ * dtype/ldx as the quantize call): the SQNR and the signal factor alpha of
+ * x_hat = alpha y + noise ([UFP4-ZC] "治病药反而喂养了病菌" and "复利效应的反向
+ * 版本"), the mean shrinkage and the rounding bias per grid cell ([UFP4-ZC]
+ * "E2M1：一块刻度不均的尺子"; [UFP4-TW] 二) and IF4's INT4 share ([IF4] 6.2).
+ * Writes UFP4_NSUMS doubles to sums (device), layout above.
  * ws: device workspace of ufp4_workspace_size(UFP4_OP_STATS, ...) bytes. */
 int ufp4_stats(const void *x, int x_dtype, int64_t ldx, const ufp4_qtensor *q, double *sums, void *ws,
                size_t ws_bytes, void *stream);
@@ -220,14 +232,20 @@ void ufp4_stats_finalize(const double *sums_host, ufp4_stats_report *report);
  *   INT4 blocks dequantize with the 6/7 factor, so a product of two INT4
  *   blocks carries 36/49 and a mixed one 6/7 ([IF4] 4.1, the MAC unit's
  *   scaling by operand types).
- * Sizes: M, N multiples of 256; K multiple of 128; ldc multiple of 4, >= N.
- * ws: ufp4_workspace_size(UFP4_OP_QGEMM, ...) bytes (0 for NATIVE_MXFP4). */
+ * Sizes: M, N multiples of 256; K multiple of 128; ldc multiple of 4, >= N;
+ * 256 operand rows must span less than 4 GiB (K below about 16.7 million
+ * elements), else UFP4_ERR_SHAPE.
+ * ws: UFP4_GEMM_DEQUANT_BF16 needs ufp4_workspace_size(UFP4_OP_QGEMM, M + N,
+ * K, cfg) bytes, whatever the operands' format; UFP4_GEMM_NATIVE_MXFP4 needs
+ * none (ws may be NULL). */
 int ufp4_qgemm(const ufp4_qtensor *a, const ufp4_qtensor *b, int mode, float *c, int64_t ldc, void *ws,
                size_t ws_bytes, void *stream);
 
 /* Plain bf16 GEMM Z = A B^T, fp32 accumulation and output (the unquantized
  * product the attenuation eta is measured against).  A[M][lda], B[N][ldb] bf16;
- * M, N multiples of 256, K multiple of 64; lda, ldb multiples of 8. */
+ * M, N multiples of 256, K multiple of 64; lda, ldb multiples of 8; 256 rows
+ * of A or B must span less than 4 GiB (lda, ldb below about 8.4 million),
+ * else UFP4_ERR_SHAPE. */
 int ufp4_gemm_bf16(const void *a, const void *b, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                    float *c, int64_t ldc, void *stream);
 
@@ -328,8 +346,8 @@ int ufp4_kv_decode(const void *q, const uint8_t *cache, const int32_t *lens, int
                    float *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes for op (UFP4_OP_*) on a rows x cols source (QGEMM: rows = M+N,
- * cols = K; ETA: rows = M, cols = N).  cfg may be NULL except for QGEMM and
- * AMAX (whose size depends on the axis). */
+ * cols = K, the dequantize-to-bf16 mode's need for any format; ETA: rows = M,
+ * cols = N).  cfg may be NULL except for AMAX (whose size depends on the axis). */
 size_t ufp4_workspace_size(int op, int64_t rows, int64_t cols, const ufp4_config *cfg);
 
 /* Text of an error code (static storage). */

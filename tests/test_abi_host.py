@@ -122,7 +122,19 @@ def test_workspace_sizes():
     assert U.ufp4_workspace_size(U.OP_AMAX, 8192, 8192, U.Cfg()) == 4096 * 4      # one per 1024 chunks
     assert U.ufp4_workspace_size(U.OP_AMAX, 16384, 4096, U.Cfg(axis="col")) == 64 * 32 * 4
     assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, U.Cfg("e1m2")) == 512 * 256 * 2
-    assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, U.Cfg("e2m1", "e8m0", 32)) == 0
+    # the dequantize-to-bf16 mode needs the same for MXFP4 operands
+    assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, U.Cfg("e2m1", "e8m0", 32)) == 512 * 256 * 2
+    assert U.ufp4_workspace_size(U.OP_QGEMM, 512, 256, None) == 512 * 256 * 2
+
+
+def test_gemm_rejects_row_offsets_past_32_bits():
+    """The GEMM kernels address 256 operand rows with 32-bit buffer offsets;
+    a row stride that makes them wrap is refused before any launch."""
+    L = U.lib()
+    big = (1 << 32) // 512 + 8          # bf16 elements: 256 rows x 2 B span > 4 GiB
+    assert L.ufp4_gemm_bf16(FAKE, FAKE, 256, 256, 64, big - big % 8, 64, FAKE, 256, None) == -2
+    assert L.ufp4_gemm_bf16(FAKE, FAKE, 256, 256, 64, 64, big - big % 8, FAKE, 256, None) == -2
+
 
 
 def test_stats_finalize_matches_oracle_report():

@@ -21,6 +21,10 @@ Recipe (all tensors row-major):
                         k, v [B][Hkv][L][D], one stream per (batch entry,
                         KV head); k N(0,1) with 4 seeded channels per KV head
                         scaled by 10 (the channel outliers of keys), v N(0,1);
+  * ``kv_peaked_q``     queries aimed at a few seeded tokens of their KV
+                        head (the sum of 4 key rows, scaled to length
+                        sqrt(D)), so the attention is peaked instead of
+                        near-uniform;
   * ``kv_lens``         per-sequence lengths: all L, or ragged, uniform in
                         [1, L] with the first entry L.
 Every generator takes ``rows``/``cols`` so tests can draw smaller tensors of
@@ -153,6 +157,25 @@ def kv_decode(B=32, Hq=32, Hkv=8, L=16384, D=128, seed=0):
     with ThreadPoolExecutor(min(8, B * Hkv)) as ex:
         list(ex.map(fill, range(B * Hkv)))
     return kv_q(B, Hq, D, seed), k, v
+
+
+def kv_peaked_q(k, Hq, ntop=4, gain=1.0, seed=0):
+    """Queries whose attention concentrates on a few tokens: for every query
+    head, the sum of ntop seeded key rows of its KV head (from k, bf16 bits
+    [B][Hkv][L][D]), scaled to length gain * sqrt(D).  With the usual
+    1/sqrt(D) score scale and the default gain, those tokens hold about 95 %
+    of the attention over 16k tokens (about two effective tokens), as a
+    retrieval-like decode step does.  Returns q [B][Hq][D] (bf16 bits)."""
+    B, Hkv, L, D = k.shape
+    G = Hq // Hkv
+    rng = np.random.default_rng([seed, TID["kv_q"], 1])
+    q = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            t = rng.choice(L, size=ntop, replace=False)
+            u = bf16_bits_to_f32(k[b, h // G, t]).astype(np.float64).sum(axis=0)
+            q[b, h] = u * (gain * np.sqrt(D) / np.linalg.norm(u))
+    return f32_to_bf16_bits(q.astype(np.float32))
 
 
 def kv_lens(B, L, seed=0, ragged=False):

@@ -188,24 +188,50 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const double *part
 // Statistics: one thread per block of the view.  Row axis: consecutive lanes
 // take consecutive blocks of a view row, and a block's elements are one
 // vector load; column axis: consecutive lanes take consecutive view rows (=
-// source columns), so the loads x[l][v] coalesce.  The per-code counts and
-// rounding-bias sums (32 of the 48) live in LDS bins private to each thread:
-// an element adds to its own code's bin with one LDS atomic, in element order,
-// so every bin is the same binary64 sum as a register accumulator would hold.
+// source columns), so the loads x[l][v] coalesce.  The next block's loads are
+// issued before the current block is processed.
+//
+// The tensor-wide sums are binary64 registers; each block's terms are first
+// summed in binary32 over its two halves (the element's products and the
+// error e = x_hat - y are binary32 operations), then scaled and added in
+// binary64.  The per-code counts and rounding-bias sums live in LDS bins
+// private to each thread (no two lanes share a bin, so the LDS adds never
+// conflict): counts as 32-bit integers, bias sums in binary64 (the LDS adds
+// 32-bit integers and binary64 at full rate; its binary32 add is much
+// slower).  Every sum is added in a fixed order, so the results are the same
+// on every run; they differ from the oracle's element-order binary64 sums
+// only by rounding: about 1e-7 relative for the whole-tensor sums, and for a
+// bucket's bias sum at most 1.5 units in the last place of z per element
+// (z = |y| / s from the rounded reciprocal), far below 1e-6 of its count.
 // ---------------------------------------------------------------------------
 constexpr int NS = 48;
 constexpr int STATS_T = 256;
+constexpr int stats_wg_per_cu(int B) { return B == 32 ? 3 : 4; }  // all resident: 16-blocks 4 waves/SIMD, 32-blocks 3
+
+template <int B, int IN>
+struct StatsRaw;
+template <int B>
+struct StatsRaw<B, IN_BF16> {
+    uint4 w[B / 8];
+};
+template <int B>
+struct StatsRaw<B, IN_F32> {
+    float4 w[B / 4];
+};
 
 template <int F, int S, int IN, bool RHT>
 __global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
 {
     constexpr int B = block_of(S);
-    constexpr int FG = F == FMT_IF4 ? FMT_E2M1 : F;
-    __shared__ double bias_bin[16][STATS_T];   // code k (FP4) or 8 + k (INT4 blocks of IF4)
-    __shared__ uint32_t count_bin[16][STATS_T];
+    constexpr bool IF4 = F == FMT_IF4;
+    constexpr int FG = IF4 ? FMT_E2M1 : F;
+    constexpr int NBIN = IF4 ? 16 : 8;  // code k, or 8 + k in IF4's INT4 blocks
+    constexpr bool FOLD = RHT && IN == IN_BF16;
+    __shared__ double bias_bin[NBIN][STATS_T];
+    __shared__ uint32_t count_bin[NBIN][STATS_T];
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NBIN; ++q) {
         bias_bin[q][tid] = 0.0;
         count_bin[q][tid] = 0u;
     }
@@ -214,149 +240,233 @@ __global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
     for (int k = 0; k < 9; ++k) acc[k] = 0.0;
     float alpha = 0.0f;
     if constexpr (S == SC_E4M3) alpha = *a.tensor_scale;
+    uint32_t sgn[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sgn[i] = RHT ? ((a.smask >> i) & 1u) << 31 : 0u;
     const int64_t nb_row = a.L / B;
     const int64_t nblocks = a.V * nb_row;
-    for (int64_t t = (int64_t)blockIdx.x * STATS_T + tid; t < nblocks; t += (int64_t)gridDim.x * STATS_T) {
-        int64_t v, j;
+    const int64_t step = (int64_t)gridDim.x * STATS_T;
+
+    // Block t is block j of view row v: t = v nb_row + j (row axis) or
+    // t = j V + v (column axis).  The position advances by a fixed step per
+    // iteration, so it is kept as a (major, minor) pair and stepped without
+    // divisions.
+    const int64_t minor_n = a.axis == 0 ? nb_row : a.V;
+    const int64_t d_major = step / minor_n, d_minor = step - d_major * minor_n;
+    auto load = [&](int64_t major, int64_t minor, StatsRaw<B, IN> &r, uint32_t (&cw)[B / 8], uint32_t &sraw) {
+        const int64_t v = a.axis == 0 ? major : minor, j = a.axis == 0 ? minor : major;
         if (a.axis == 0) {
-            v = t / nb_row;
-            j = t - v * nb_row;
-        } else {
-            j = t / a.V;
-            v = t - j * a.V;
-        }
-        float y[B];
-        if (a.axis == 0) {
-            // the block is contiguous and 16-byte aligned (x aligned, ldx a multiple of 8)
             const int64_t idx = v * a.ldx + j * B;
             if constexpr (IN == IN_BF16) {
                 const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + idx);
 #pragma unroll
-                for (int c = 0; c < B / 8; ++c) {
-                    const uint4 w = p[c];
-                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        y[8 * c + 2 * h] = u2f(ws[h] << 16);
-                        y[8 * c + 2 * h + 1] = u2f(ws[h] & 0xFFFF0000u);
-                    }
-                }
+                for (int c = 0; c < B / 8; ++c) r.w[c] = p[c];
             } else {
                 const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + idx);
 #pragma unroll
-                for (int c = 0; c < B / 4; ++c) {
-                    const float4 w = p[c];
-                    y[4 * c] = w.x;
-                    y[4 * c + 1] = w.y;
-                    y[4 * c + 2] = w.z;
-                    y[4 * c + 3] = w.w;
+                for (int c = 0; c < B / 4; ++c) r.w[c] = p[c];
+            }
+        } else {
+            if constexpr (IN == IN_BF16) {
+                const uint16_t *p = static_cast<const uint16_t *>(a.x) + (j * B) * a.ldx + v;
+                uint32_t h[B];
+#pragma unroll
+                for (int i = 0; i < B; ++i) h[i] = p[i * a.ldx];
+#pragma unroll
+                for (int c = 0; c < B / 8; ++c)
+                    r.w[c] = make_uint4(h[8 * c] | (h[8 * c + 1] << 16), h[8 * c + 2] | (h[8 * c + 3] << 16),
+                                        h[8 * c + 4] | (h[8 * c + 5] << 16), h[8 * c + 6] | (h[8 * c + 7] << 16));
+            } else {
+                const float *p = static_cast<const float *>(a.x) + (j * B) * a.ldx + v;
+#pragma unroll
+                for (int c = 0; c < B / 4; ++c)
+                    r.w[c] = make_float4(p[(4 * c) * a.ldx], p[(4 * c + 1) * a.ldx], p[(4 * c + 2) * a.ldx],
+                                         p[(4 * c + 3) * a.ldx]);
+            }
+        }
+        // the block's B / 2 code bytes as 32-bit words (codes are 4-byte aligned)
+        const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.codes + (v * a.L + j * B) / 2);
+#pragma unroll
+        for (int i = 0; i < B / 8; ++i) cw[i] = cp[i];
+        const int64_t sidx = v * nb_row + j;
+        if constexpr (S == SC_FP32)
+            sraw = __float_as_uint(static_cast<const float *>(a.scales)[sidx]);
+        else
+            sraw = static_cast<const uint8_t *>(a.scales)[sidx];
+    };
+
+    int64_t t = (int64_t)blockIdx.x * STATS_T + tid;
+    int64_t major = t / minor_n, minor = t - major * minor_n;
+    StatsRaw<B, IN> raw;
+    uint32_t cw[B / 8], sraw = 0;
+    if (t < nblocks) load(major, minor, raw, cw, sraw);
+    while (t < nblocks) {
+        // unpack and transform the current block, then start the next one's loads
+        float y[B];
+        if constexpr (IN == IN_BF16) {
+#pragma unroll
+            for (int c = 0; c < B / 8; ++c) {
+                const uint32_t ws[4] = {raw.w[c].x, raw.w[c].y, raw.w[c].z, raw.w[c].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const int i = 8 * c + 2 * h;
+                    y[i] = u2f((ws[h] << 16) ^ sgn[i & 15]);
+                    y[i + 1] = u2f((ws[h] & 0xFFFF0000u) ^ sgn[(i + 1) & 15]);
                 }
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < B; ++i) {
-                const int64_t idx = (j * B + i) * a.ldx + v;
-                if constexpr (IN == IN_BF16)
-                    y[i] = u2f((uint32_t)static_cast<const uint16_t *>(a.x)[idx] << 16);
-                else
-                    y[i] = static_cast<const float *>(a.x)[idx];
+            for (int c = 0; c < B / 4; ++c) {
+                const float4 w = raw.w[c];
+                y[4 * c] = u2f(f2u(w.x) ^ sgn[(4 * c) & 15]);
+                y[4 * c + 1] = u2f(f2u(w.y) ^ sgn[(4 * c + 1) & 15]);
+                y[4 * c + 2] = u2f(f2u(w.z) ^ sgn[(4 * c + 2) & 15]);
+                y[4 * c + 3] = u2f(f2u(w.w) ^ sgn[(4 * c + 3) & 15]);
             }
         }
+        uint32_t c_cur[B / 8];
+#pragma unroll
+        for (int i = 0; i < B / 8; ++i) c_cur[i] = cw[i];
+        const uint32_t s_cur = sraw;
+        const int64_t tn = t + step;
+        minor += d_minor;
+        major += d_major;
+        if (minor >= minor_n) {
+            minor -= minor_n;
+            ++major;
+        }
+        if (tn < nblocks) load(major, minor, raw, cw, sraw);
+        // the transform; for bf16 sources its final x 1/4 is folded into the
+        // scale (y = v / 4 exactly, every partial sum being a multiple of
+        // 2^-133), so the loop below works on v = 4y, 4 x_hat and 4e
         if constexpr (RHT) {
 #pragma unroll
             for (int c = 0; c < B; c += 16) {
+                fwht8(y + c);
+                fwht8(y + c + 8);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) y[c + i] = u2f(f2u(y[c + i]) ^ (((a.smask >> i) & 1u) << 31));
-                fwht16_local(y + c);
+                for (int i = 0; i < 8; ++i) {
+                    const float p = y[c + i], q = y[c + i + 8];
+                    y[c + i] = p + q;
+                    y[c + i + 8] = p - q;
+                }
+                if constexpr (!FOLD) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) y[c + i] = y[c + i] * 0.25f;
+                }
             }
         }
-        // stored scale
-        const int64_t sidx = v * nb_row + j;
+        // the stored scale
         float s;
         bool int4 = false;
         if constexpr (S == SC_FP32) {
-            s = static_cast<const float *>(a.scales)[sidx];
+            s = u2f(s_cur);
         } else if constexpr (S == SC_E8M0) {
-            s = __builtin_amdgcn_ldexpf(1.0f, (int)static_cast<const uint8_t *>(a.scales)[sidx] - 127);
+            s = __builtin_amdgcn_ldexpf(1.0f, (int)s_cur - 127);
         } else {
-            const uint32_t b = static_cast<const uint8_t *>(a.scales)[sidx];
-            s = alpha * e4m3_decode(b & 0x7Fu);
-            int4 = (F == FMT_IF4) && (b & 0x80u);
+            s = alpha * e4m3_decode_hw(s_cur & 0x7Fu);
+            int4 = IF4 && (s_cur & 0x80u);
         }
-        const float inv = s == 0.0f ? 0.0f : 1.0f / s;
-        const bool fast = fast_div_ok(s);
-        // the block's B / 2 code bytes as 32-bit words (codes are 4-byte aligned)
-        uint32_t cw[B / 8];
-        const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.codes + (v * a.L + j * B) / 2);
-#pragma unroll
-        for (int i = 0; i < B / 8; ++i) cw[i] = cp[i];
-        acc[7] += 1.0;
-        acc[8] += int4 ? 1.0 : 0.0;
+        const float sk = FOLD ? s * 4.0f : s;  // exact
+        // z = |y| s^-1 (IF4's INT4 blocks: |y| 7/6 s^-1) as one product with
+        // the rounded reciprocal: within 1.5 units in the last place of the
+        // correctly rounded quotient, far inside the bias sums' tolerance
+        const float zinv = s == 0.0f ? 0.0f : (int4 ? 7.0f / 6.0f : 1.0f) / sk;
+        const float post = int4 ? 6.0f / 7.0f : 1.0f;
         const int bin0 = int4 ? 8 : 0;
+        // grid values of the codes: E2M1 codes by the hardware FP4 decode
+        // (two per instruction, signed, exact), the uniform grids as k x step
+        float gv[B];
+        if constexpr (e2m1_codes(FG)) {
+#pragma unroll
+            for (int i = 0; i < B; i += 2) {
+                const v2f d = decode2_e2m1(c_cur[i >> 3], (i & 7) >> 1);
+                gv[i] = d.x;
+                gv[i + 1] = d.y;
+            }
+        }
+        // binary32 sums over the block's two halves, then binary64
+        float p1[2] = {0.f, 0.f}, p2[2] = {0.f, 0.f}, p3[2] = {0.f, 0.f}, p4[2] = {0.f, 0.f}, p5[2] = {0.f, 0.f},
+              p6[2] = {0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const uint32_t c = (cw[i >> 3] >> (4 * (i & 7))) & 15u;
-            const uint32_t k = c & 7u;
-            float xm, g, ta;
-            if (int4) {
-                xm = ((float)k * s) * (6.0f / 7.0f);
-                g = (float)k;
-                ta = fabsf(y[i]) * (7.0f / 6.0f);
+            const int h = (2 * i) / B;
+            const uint32_t sh = 4 * (i & 7);
+            const uint32_t k = (c_cur[i >> 3] >> sh) & 7u;
+            float gs;  // signed grid value
+            if constexpr (e2m1_codes(FG)) {
+                gs = gv[i];
+                if constexpr (IF4) {
+                    const float gi = u2f(f2u((float)k) | ((c_cur[i >> 3] << (28 - sh)) & 0x80000000u));
+                    gs = int4 ? gi : gs;
+                }
             } else {
-                xm = grid_value<FG>(k) * s;
-                g = grid_value<FG>(k);
-                ta = fabsf(y[i]);
+                gs = u2f(f2u(grid_value<FG>(k)) | ((c_cur[i >> 3] << (28 - sh)) & 0x80000000u));
             }
-            float z;
-            if (s == 0.0f)
-                z = 0.0f;
-            else if (S == SC_E8M0)
-                z = ta * inv;
-            else
-                z = fast ? div_fast(ta, s, inv) : ta / s;
-            if (s != 0.0f && z == 0.0f && ta > 0.0f) z = ta / s;
-            const double xh = (c & 8u) ? -(double)xm : (double)xm;
-            const double yy = (double)y[i];
-            const double e = xh - yy;
-            acc[0] += 1.0;
-            acc[1] += yy * yy;
-            acc[2] += e * e;
-            acc[3] += e;
-            acc[4] += (yy > 0.0 ? e : (yy < 0.0 ? -e : 0.0));
-            acc[5] += xh * yy;
-            acc[6] += fabs(e);
-            atomicAdd(&bias_bin[bin0 + k][tid], (double)g - (double)z);
-            atomicAdd(&count_bin[bin0 + k][tid], 1u);
+            // x_hat = (g s) post with the code's sign (post = 1 is exact); x 4 when folded
+            const float xk = (gs * sk) * post;
+            const float v = y[i];
+            const float ek = xk - v;
+            p1[h] = __builtin_fmaf(v, v, p1[h]);
+            p2[h] = __builtin_fmaf(ek, ek, p2[h]);
+            p3[h] += ek;
+            p4[h] += u2f(f2u(ek) ^ (f2u(v) & 0x80000000u));  // sign(y) e (y = +-0 gives e = +-0)
+            p5[h] = __builtin_fmaf(xk, v, p5[h]);
+            p6[h] += fabsf(ek);
+            const int bin = bin0 + (int)k;
+            atomicAdd(&bias_bin[bin][tid], (double)__builtin_fmaf(-fabsf(v), zinv, fabsf(gs)));
+            atomicAdd(&count_bin[bin][tid], 1u);
         }
+        constexpr double F2 = FOLD ? 1.0 / 16.0 : 1.0, F1 = FOLD ? 0.25 : 1.0;  // exact
+        acc[0] += (double)B;
+        acc[1] = __builtin_fma((double)(p1[0] + p1[1]), F2, acc[1]);
+        acc[2] = __builtin_fma((double)(p2[0] + p2[1]), F2, acc[2]);
+        acc[3] = __builtin_fma((double)(p3[0] + p3[1]), F1, acc[3]);
+        acc[4] = __builtin_fma((double)(p4[0] + p4[1]), F1, acc[4]);
+        acc[5] = __builtin_fma((double)(p5[0] + p5[1]), F2, acc[5]);
+        acc[6] = __builtin_fma((double)(p6[0] + p6[1]), F1, acc[6]);
+        acc[7] += 1.0;
+        if constexpr (IF4) acc[8] += int4 ? 1.0 : 0.0;
+        t = tn;
     }
     double out[NS];
 #pragma unroll
     for (int k = 0; k < 9; ++k) out[k] = acc[k];
 #pragma unroll
-    for (int k = 9; k < 16; ++k) out[k] = 0.0;
-    // each thread reads back only its own bins (its own LDS atomics are done
-    // in order before these reads)
+    for (int k = 9; k < NS; ++k) out[k] = 0.0;
+    // each thread reads back only its own bins (its own LDS adds are done in
+    // order before these reads)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NBIN; ++q) {
         out[16 + q] = (double)count_bin[q][tid];
-        out[24 + q] = (double)count_bin[8 + q][tid];
         out[32 + q] = bias_bin[q][tid];
-        out[40 + q] = bias_bin[8 + q][tid];
     }
     block_reduce_store<NS>(out, a.partials + (int64_t)blockIdx.x * NS);
+}
+
+// Workgroups of the statistics grid: as many per compute unit of the current
+// device as are resident at once, at most one per STATS_T blocks, at most
+// STATS_WGS (the workspace rows).
+static int stats_grid(int64_t nblocks, int per_cu)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    int64_t g = (nblocks + STATS_T - 1) / STATS_T;
+    const int64_t resident = (int64_t)cus * per_cu;
+    if (g > resident) g = resident;
+    if (g > STATS_WGS) g = STATS_WGS;
+    return g < 1 ? 1 : (int)g;
 }
 
 template <int F, int S>
 static hipError_t stats_pick(int in_dtype, int rht, const StatsArgs &a, hipStream_t st)
 {
     const int64_t nblocks = a.V * (a.L / block_of(S));
-    int64_t g = (nblocks + STATS_T - 1) / STATS_T;
-    // the 48 KiB of LDS bins fit three workgroups on a CU: one full wave of
-    // them over the 256 CUs, no tail (the workspace holds STATS_WGS rows)
-    constexpr int64_t kResident = 3 * 256;
-    static_assert(kResident <= STATS_WGS, "stats grid");
-    if (g > kResident) g = kResident;
-    if (g < 1) g = 1;
+    const int g = stats_grid(nblocks, stats_wg_per_cu(block_of(S)));
     const dim3 grid((unsigned)g);
     if (in_dtype == IN_BF16) {
         if (rht)
@@ -371,7 +481,7 @@ static hipError_t stats_pick(int in_dtype, int rht, const StatsArgs &a, hipStrea
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(256), st, a.partials, (int)g, a.sums);
+    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(256), st, a.partials, g, a.sums);
     return hipGetLastError();
 }
 

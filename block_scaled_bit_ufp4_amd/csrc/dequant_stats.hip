@@ -368,12 +368,39 @@ __global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
             int4 = IF4 && (s_cur & 0x80u);
         }
         const float sk = FOLD ? s * 4.0f : s;  // exact
-        // z = |y| s^-1 (IF4's INT4 blocks: |y| 7/6 s^-1) as one product with
+        // z = |y| / s (IF4's INT4 blocks: |y| 7/6 / s) as one product with
         // the rounded reciprocal: within 1.5 units in the last place of the
-        // correctly rounded quotient, far inside the bias sums' tolerance
-        const float zinv = s == 0.0f ? 0.0f : (int4 ? 7.0f / 6.0f : 1.0f) / sk;
+        // correctly rounded quotient, far inside the bias sums' tolerance.
+        // Scales outside [2^-75, 2^125] (where the reciprocal would leave the
+        // normal range) take the true quotient.
+        const float pre = int4 ? 7.0f / 6.0f : 1.0f;
+        const float zinv = s == 0.0f ? 0.0f : pre / sk;
+        float z[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) z[i] = fabsf(y[i]) * zinv;
+        if constexpr (S != SC_E8M0) {
+            const bool slow = s != 0.0f && !fast_div_ok(s);
+            if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+                if (slow) {
+#pragma unroll
+                    for (int i = 0; i < B; ++i) z[i] = (fabsf(y[i]) * pre) / sk;
+                }
+            }
+        }
         const float post = int4 ? 6.0f / 7.0f : 1.0f;
         const int bin0 = int4 ? 8 : 0;
+        // The block's terms are summed in binary32 after scaling the block by
+        // a power of two P near 1 / s (exact), so that squares of values up to
+        // the binary32 maximum neither overflow nor lose precision; the sums
+        // are scaled back exactly in binary64.  With s = 0 (an all-zero block,
+        // or an E4M3 block scale that rounded to zero) P comes from the tensor
+        // scale alpha, above every such block's values.
+        const float pref = s != 0.0f ? s : (S == SC_E4M3 ? alpha : 1.0f);
+        int pe = pref != 0.0f ? __builtin_amdgcn_frexp_expf(pref) : 0;
+        pe = pe > 126 ? 126 : (pe < -126 ? -126 : pe);
+        const float P = __builtin_amdgcn_ldexpf(1.0f, -pe);
+        const float skp = sk * P;  // exact
+        const double Pinv = __builtin_amdgcn_ldexp(1.0, pe), Pinv2 = Pinv * Pinv;
         // grid values of the codes: E2M1 codes by the hardware FP4 decode
         // (two per instruction, signed, exact), the uniform grids as k x step
         float gv[B];
@@ -403,9 +430,9 @@ __global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
             } else {
                 gs = u2f(f2u(grid_value<FG>(k)) | ((c_cur[i >> 3] << (28 - sh)) & 0x80000000u));
             }
-            // x_hat = (g s) post with the code's sign (post = 1 is exact); x 4 when folded
-            const float xk = (gs * sk) * post;
-            const float v = y[i];
+            // P x_hat = (g s P) post with the code's sign (post = 1 is exact); x 4 when folded
+            const float xk = (gs * skp) * post;
+            const float v = y[i] * P;
             const float ek = xk - v;
             p1[h] = __builtin_fmaf(v, v, p1[h]);
             p2[h] = __builtin_fmaf(ek, ek, p2[h]);
@@ -414,17 +441,18 @@ __global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
             p5[h] = __builtin_fmaf(xk, v, p5[h]);
             p6[h] += fabsf(ek);
             const int bin = bin0 + (int)k;
-            atomicAdd(&bias_bin[bin][tid], (double)__builtin_fmaf(-fabsf(v), zinv, fabsf(gs)));
+            atomicAdd(&bias_bin[bin][tid], (double)(fabsf(gs) - z[i]));
             atomicAdd(&count_bin[bin][tid], 1u);
         }
         constexpr double F2 = FOLD ? 1.0 / 16.0 : 1.0, F1 = FOLD ? 0.25 : 1.0;  // exact
+        const double G2 = F2 * Pinv2, G1 = F1 * Pinv;                             // exact
         acc[0] += (double)B;
-        acc[1] = __builtin_fma((double)(p1[0] + p1[1]), F2, acc[1]);
-        acc[2] = __builtin_fma((double)(p2[0] + p2[1]), F2, acc[2]);
-        acc[3] = __builtin_fma((double)(p3[0] + p3[1]), F1, acc[3]);
-        acc[4] = __builtin_fma((double)(p4[0] + p4[1]), F1, acc[4]);
-        acc[5] = __builtin_fma((double)(p5[0] + p5[1]), F2, acc[5]);
-        acc[6] = __builtin_fma((double)(p6[0] + p6[1]), F1, acc[6]);
+        acc[1] = __builtin_fma((double)(p1[0] + p1[1]), G2, acc[1]);
+        acc[2] = __builtin_fma((double)(p2[0] + p2[1]), G2, acc[2]);
+        acc[3] = __builtin_fma((double)(p3[0] + p3[1]), G1, acc[3]);
+        acc[4] = __builtin_fma((double)(p4[0] + p4[1]), G1, acc[4]);
+        acc[5] = __builtin_fma((double)(p5[0] + p5[1]), G2, acc[5]);
+        acc[6] = __builtin_fma((double)(p6[0] + p6[1]), G1, acc[6]);
         acc[7] += 1.0;
         if constexpr (IF4) acc[8] += int4 ? 1.0 : 0.0;
         t = tn;

@@ -135,6 +135,21 @@ def compare_sums(got, want):
             assert abs(got[k] - want[k]) <= 1e-6 * abs(want[k]) + 1e-300, (k, got[k], want[k])
 
 
+@pytest.mark.parametrize("d", [c for c in all_configs() if c["rht"] != "det" and c["rounding"] == "rtne"], ids=cfg_id)
+def test_stats_corner_case_inputs(d):
+    """Statistics on the corner-case blocks (zeros, subnormal blocks whose scale
+    is subnormal, huge and tiny magnitudes, ties) against the oracle."""
+    x = S.edge_cases(64, 256)
+    if d["axis"] == "col":
+        x = np.ascontiguousarray(x.T)
+    U, cfg, ocfg, xd, xo, q, want = check_quant(x, d)
+    got = host(U.ufp4_stats(xd, q))
+    ref = O.stats(xo, ocfg)
+    assert np.all(np.isfinite(got)), got
+    compare_sums(got, ref)
+    np.testing.assert_array_equal(got[[0, 7, 8] + list(range(16, 32))], ref[[0, 7, 8] + list(range(16, 32))])
+
+
 @pytest.mark.parametrize("d", all_configs()[::3] + all_configs()[-12:], ids=cfg_id)
 def test_stats_match_oracle(d):
     U, cfg, ocfg, xd, xo, q, want = check_quant(make_input("t3", seed=7), d)

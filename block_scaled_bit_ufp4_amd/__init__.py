@@ -59,6 +59,7 @@ _lib = C.CDLL(LIB_PATH)
 _p, _i64, _u64, _i32, _sz = C.c_void_p, C.c_int64, C.c_uint64, C.c_int, C.c_size_t
 _lib.ufp4_rht.argtypes = [_p, _i32, _i64, _i64, _i64, _i32, _i32, _u64, _p, _i32, _i64, _p]
 _lib.ufp4_amax.argtypes = [_p, _i32, _i64, _i64, _i64, C.POINTER(ufp4_config), _p, _p, _sz, _p]
+_lib.ufp4_amax_noalloc.argtypes = [_p, _i32, _i64, _i64, _i64, C.POINTER(ufp4_config), _p, _p]
 _lib.ufp4_quantize.argtypes = [_p, _i32, _i64, _i64, _i64, C.POINTER(ufp4_config), _p, C.POINTER(ufp4_qtensor), _p]
 _lib.ufp4_dequantize.argtypes = [C.POINTER(ufp4_qtensor), _i32, _p, _i32, _i64, _p]
 _lib.ufp4_stats.argtypes = [_p, _i32, _i64, C.POINTER(ufp4_qtensor), _p, _p, _sz, _p]
@@ -83,7 +84,7 @@ _lib.ufp4_kv_decode_workspace_size.restype = _sz
 _lib.ufp4_kv_decode.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, C.c_float, _i32, _i64, _p, _p, _sz,
                                 _p]
 
-EXPORTS = ["ufp4_rht", "ufp4_amax", "ufp4_quantize", "ufp4_dequantize", "ufp4_stats", "ufp4_stats_finalize",
+EXPORTS = ["ufp4_rht", "ufp4_amax", "ufp4_amax_noalloc", "ufp4_quantize", "ufp4_dequantize", "ufp4_stats", "ufp4_stats_finalize",
            "ufp4_qgemm", "ufp4_gemm_bf16", "ufp4_eta", "ufp4_workspace_size", "ufp4_strerror",
            "ufp4_last_hip_error", "ufp4_version", "ufp4_time_next_launch", "ufp4_kv_cache_bytes",
            "ufp4_kv_cache_quantize", "ufp4_kv_q_quantize", "ufp4_kv_decode_workspace_size", "ufp4_kv_decode"]
@@ -198,6 +199,16 @@ def ufp4_amax(x: torch.Tensor, cfg: Cfg, out: Optional[torch.Tensor] = None, ws:
     rc = _lib.ufp4_amax(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], _ld(x), C.byref(c), out.data_ptr(),
                         ws.data_ptr(), ws.numel(), _stream(stream))
     _check(rc, "ufp4_amax")
+    return out
+
+
+def ufp4_amax_noalloc(x: torch.Tensor, cfg: Cfg, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """ufp4_amax with the library's built-in scratch instead of a workspace
+    (out: a device float the caller allocated)."""
+    c = cfg.c()
+    rc = _lib.ufp4_amax_noalloc(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], _ld(x), C.byref(c),
+                                out.data_ptr(), _stream(stream))
+    _check(rc, "ufp4_amax_noalloc")
     return out
 
 

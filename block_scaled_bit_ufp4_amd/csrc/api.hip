@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ufp4.h"
 #include "device.hpp"
 #include "kernels.hpp"
@@ -120,6 +122,35 @@ static void fill_args(const void *x, int dtype, int64_t rows, int64_t cols, int6
     ca.smask = smask;
 }
 
+// Built-in scratch of ufp4_amax_noalloc: room for the partial maxima of the
+// amax pass (one per workgroup), 256 KiB on every device the library runs
+// on, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it only stands for the symbol); it looks up the
+// array's device address once per device, with that device current, and
+// uses that address.
+static constexpr int64_t AMAX_SCRATCH_FLOATS = 65536;
+static __device__ __align__(256) float amax_scratch[AMAX_SCRATCH_FLOATS];
+static constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_lock;
+static float *g_amax_scratch[MAX_DEVICES];  // device address per device, null until looked up
+
+static int amax_scratch_of_current_device(float **out)
+{
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= MAX_DEVICES) return UFP4_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> guard(g_scratch_lock);
+    if (!g_amax_scratch[dev]) {
+        void *p = nullptr;
+        const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(amax_scratch));
+        if (g != hipSuccess || !p) return hip_fail(g != hipSuccess ? g : hipErrorInvalidSymbol);
+        g_amax_scratch[dev] = static_cast<float *>(p);
+    }
+    *out = g_amax_scratch[dev];
+    return UFP4_OK;
+}
+
 extern "C" {
 
 int ufp4_version(void) { return (0 << 16) | 1; }
@@ -190,24 +221,51 @@ int ufp4_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx
     return hip_fail(launch_rht(sp, y_dtype, ra, ca, (hipStream_t)stream));
 }
 
-int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
-              float *amax, void *ws, size_t ws_bytes, void *stream)
+// The amax pass once its arguments and its partial-maxima buffer (ws, ws
+// checked by the caller) are settled.
+static int amax_run(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+                    float *amax, float *ws, void *stream)
+{
+    RowArgs ra;
+    ColArgs ca;
+    fill_args(x, x_dtype, rows, cols, ldx, cfg->axis, sign_mask(cfg->rht, cfg->rht_seed), ra, ca);
+    ra.partials = ws;
+    ca.partials = ws;
+    LaunchSpec sp{0, 0, 0, x_dtype, cfg->rht != UFP4_RHT_NONE, cfg->axis};
+    return hip_fail(launch_amax(sp, ra, ca, amax, (hipStream_t)stream));
+}
+
+static int amax_check(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+                      const float *amax)
 {
     int rc = check_config(cfg);
     if (rc) return rc;
     if (!amax) return UFP4_ERR_INVALID_ARG;
-    rc = check_source(x, x_dtype, rows, cols, ldx, cfg->axis, 16);
+    return check_source(x, x_dtype, rows, cols, ldx, cfg->axis, 16);
+}
+
+int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+              float *amax, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = amax_check(x, x_dtype, rows, cols, ldx, cfg, amax);
     if (rc) return rc;
     const size_t need = ufp4_workspace_size(UFP4_OP_AMAX, rows, cols, cfg);
     if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
     if ((uintptr_t)ws & 3u) return UFP4_ERR_ALIGN;
-    RowArgs ra;
-    ColArgs ca;
-    fill_args(x, x_dtype, rows, cols, ldx, cfg->axis, sign_mask(cfg->rht, cfg->rht_seed), ra, ca);
-    ra.partials = static_cast<float *>(ws);
-    ca.partials = static_cast<float *>(ws);
-    LaunchSpec sp{0, 0, 0, x_dtype, cfg->rht != UFP4_RHT_NONE, cfg->axis};
-    return hip_fail(launch_amax(sp, ra, ca, amax, (hipStream_t)stream));
+    return amax_run(x, x_dtype, rows, cols, ldx, cfg, amax, static_cast<float *>(ws), stream);
+}
+
+int ufp4_amax_noalloc(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+                      float *amax, void *stream)
+{
+    int rc = amax_check(x, x_dtype, rows, cols, ldx, cfg, amax);
+    if (rc) return rc;
+    if (ufp4_workspace_size(UFP4_OP_AMAX, rows, cols, cfg) > sizeof(float) * AMAX_SCRATCH_FLOATS)
+        return UFP4_ERR_WORKSPACE;
+    float *scratch = nullptr;
+    rc = amax_scratch_of_current_device(&scratch);
+    if (rc) return rc;
+    return amax_run(x, x_dtype, rows, cols, ldx, cfg, amax, scratch, stream);
 }
 
 int ufp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,

@@ -185,6 +185,22 @@ int ufp4_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx
 int ufp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
               float *amax, void *ws, size_t ws_bytes, void *stream);
 
+/* ufp4_amax without a workspace argument, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.  The partial maxima go to a scratch array
+ * built into the library: 256 KiB of device memory on each device the library
+ * runs on, held until the process ends; its address is looked up once per
+ * device on the first call there.  The call allocates nothing.  Sizes: the
+ * pass may need at most 65536 partial maxima, i.e. rows x cols up to 2^30
+ * along rows, or ceil(cols/64) x ceil(rows/512) <= 65536 down columns;
+ * larger tensors return UFP4_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap on one device (other streams, other host threads) race and must
+ * be ordered by the caller.  Otherwise as ufp4_amax (same result, bit for
+ * bit). */
+int ufp4_amax_noalloc(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const ufp4_config *cfg,
+                      float *amax, void *stream);
+
 /* Block quantization (all steps fused in one kernel: load, signs, FWHT, block
  * amax, scale, RTNE/SR or IF4 selection, nibble packing, stores).
  * Definitions: the fused 16-wide RHT + quantize of [UFP4-TW] 六; the per-block

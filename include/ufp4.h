@@ -31,8 +31,10 @@
  *     global state except, per host thread, the last HIP error and a pending
  *     ufp4_time_next_launch request, and, per process, each device's
  *     compute-unit count (read once by the first GEMM on that device, never
- *     changed after).  Calls are reentrant and can be captured in a HIP graph
- *     (no allocation, no memset).
+ *     changed after) and the device address of ufp4_amax_noalloc's built-in
+ *     scratch array (looked up once per device).  Calls are reentrant and
+ *     can be captured in a HIP graph (no allocation, no memset); calls of
+ *     ufp4_amax_noalloc that overlap on one device share its scratch.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; results are ordered by the stream.
  *   - Arguments are validated on the host before anything is enqueued; on a

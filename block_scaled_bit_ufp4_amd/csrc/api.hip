@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/ufp4.h"
@@ -24,6 +25,24 @@ LaunchTiming &launch_timing()
 {
     static thread_local LaunchTiming t;
     return t;
+}
+
+int cu_count()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        n = cus[dev].load(std::memory_order_relaxed);
+        if (n <= 0) {
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+                (void)hipGetLastError();
+                n = 0;
+            } else {
+                cus[dev].store(n, std::memory_order_relaxed);
+            }
+        }
+    }
+    return n > 0 ? n : 256;
 }
 }  // namespace ufp4
 
@@ -348,7 +367,7 @@ int ufp4_stats(const void *x, int x_dtype, int64_t ldx, const ufp4_qtensor *q, d
     const size_t need = ufp4_workspace_size(UFP4_OP_STATS, q->rows, q->cols, &q->cfg);
     if (!ws || ws_bytes < need) return UFP4_ERR_WORKSPACE;
     if ((uintptr_t)ws & 7u || (uintptr_t)sums & 7u) return UFP4_ERR_ALIGN;
-    StatsArgs a;
+    StatsArgs a = {};
     a.x = x;
     a.ldx = ldx;
     a.V = q->cfg.axis == UFP4_ROW ? q->rows : q->cols;

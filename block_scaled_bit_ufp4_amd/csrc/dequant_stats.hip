@@ -8,6 +8,8 @@
 // rounding bias (section "E2M1：一块刻度不均的尺子"; "蚂蚁集团揭秘" 二) and IF4's
 // type shares (IF4 page 6.2).  The attenuation eta = <Zq,Z>/<Z,Z> is the
 // identity of section "复利效应的反向版本".
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -151,8 +153,8 @@ hipError_t launch_dequant(int format, int scale, int inverse_rht, int out_dtype,
 // ---------------------------------------------------------------------------
 // Reductions of binary64 partial sums
 // ---------------------------------------------------------------------------
-template <int NV>
-__device__ __forceinline__ void block_reduce_store(double (&acc)[NV], double *out)
+template <int NV, typename Slot>
+__device__ __forceinline__ void block_reduce_store(double (&acc)[NV], double *out, Slot slot, bool add = false)
 {
     __shared__ double red[4][NV];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -165,7 +167,8 @@ __device__ __forceinline__ void block_reduce_store(double (&acc)[NV], double *ou
     __syncthreads();
     if (threadIdx.x < NV) {
         const int k = threadIdx.x;
-        out[k] = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+        const double v = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+        out[slot(k)] = add ? out[slot(k)] + v : v;
     }
 }
 
@@ -191,22 +194,32 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const double *part
 // source columns), so the loads x[l][v] coalesce.  The next block's loads are
 // issued before the current block is processed.
 //
-// The tensor-wide sums are binary64 registers; each block's terms are first
-// summed in binary32 over its two halves (the element's products and the
-// error e = x_hat - y are binary32 operations), then scaled and added in
-// binary64.  The per-code counts and rounding-bias sums live in LDS bins
-// private to each thread (no two lanes share a bin, so the LDS adds never
-// conflict): counts as 32-bit integers, bias sums in binary64 (the LDS adds
-// 32-bit integers and binary64 at full rate; its binary32 add is much
-// slower).  Every sum is added in a fixed order, so the results are the same
-// on every run; they differ from the oracle's element-order binary64 sums
-// only by rounding: about 1e-7 relative for the whole-tensor sums, and for a
-// bucket's bias sum at most 1.5 units in the last place of z per element
-// (z = |y| / s from the rounded reciprocal), far below 1e-6 of its count.
+// Sums 1..6 are binary64 registers.  Each block's terms are first summed in
+// binary32 (the element's products and the error e = x_hat - y are binary32
+// operations), then scaled and added in binary64.  A wave whose blocks all
+// have scales in [2^-30, 2^30] sums the values as they are; otherwise every
+// block is first scaled by a power of two P near 1 / s (exact), so that
+// squares of values up to the binary32 maximum neither overflow nor lose
+// precision, and the sums are scaled back exactly.
+//
+// Per-code counts and rounding-bias sums: one 64-bit LDS word per thread and
+// code (no two lanes share a word, so the LDS adds never conflict), which
+// adds 2^48 + floor(z 2^26) per element, z = |y| / s in grid units.  A launch
+// adds at most STATS_CHUNK elements per thread, so the count (bits 48..63)
+// and the fixed-point sum of z (below 2^47 while z < 64; the quantizer's z
+// stay below 1.5 x the grid maximum) never meet, and the bias sum of code k
+// is count x g[k] - sum z.  Truncation moves a bias sum by less than 2^-26
+// per element.  Each thread reads back only its own words.
+//
+// Every sum is added in a fixed order, so the results are the same on every
+// run; they differ from the oracle's element-order binary64 sums only by
+// rounding: about 1e-7 relative for the whole-tensor sums, and for a bucket's
+// bias sum about one unit in the last place of z per element (z = |y| / s
+// with the refined reciprocal), far below 1e-6 of its count.
 // ---------------------------------------------------------------------------
 constexpr int NS = 48;
 constexpr int STATS_T = 256;
-constexpr int stats_wg_per_cu(int B) { return B == 32 ? 3 : 4; }  // all resident: 16-blocks 4 waves/SIMD, 32-blocks 3
+constexpr int64_t STATS_CHUNK = 1 << 15;  // elements per thread and launch
 
 template <int B, int IN>
 struct StatsRaw;
@@ -219,126 +232,76 @@ struct StatsRaw<B, IN_F32> {
     float4 w[B / 4];
 };
 
+// Signed values of the 8 codes of w on a uniform grid (sign << 3 | k per
+// nibble): each nibble becomes the FP8 E4M3 byte sign << 7 | k, the subnormal
+// k 2^-9, which the FP8 decode scaled by 2^9 x step turns into k x step
+// (exact).
+template <int F>
+__device__ __forceinline__ void decode8_uniform(uint32_t w, float *g)
+{
+    constexpr float SC = F == FMT_E1M2 ? 256.0f : 512.0f;
+    const uint32_t even = (w & 0x07070707u) | ((w << 4) & 0x80808080u);  // nibbles 0, 2, 4, 6
+    const uint32_t odd = ((w >> 4) & 0x07070707u) | (w & 0x80808080u);   // nibbles 1, 3, 5, 7
+    const v2f e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(even, SC, false);
+    const v2f e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(even, SC, true);
+    const v2f o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(odd, SC, false);
+    const v2f o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(odd, SC, true);
+    g[0] = e0.x;
+    g[2] = e0.y;
+    g[4] = e1.x;
+    g[6] = e1.y;
+    g[1] = o0.x;
+    g[3] = o0.y;
+    g[5] = o1.x;
+    g[7] = o1.y;
+}
+
+// 1 / x for normal x and normal 1 / x: the hardware reciprocal and one
+// Newton step (about half a unit in the last place).
+__device__ __forceinline__ float rcp_refined(float x)
+{
+    const float r = __builtin_amdgcn_rcpf(x);
+    return __builtin_fmaf(r, __builtin_fmaf(-x, r, 1.0f), r);
+}
+
+// Grid value g[q] of bin q (IF4: bins 8..15 are the INT4 blocks' codes).
+template <int F>
+__device__ __forceinline__ double bin_grid(int q)
+{
+    if constexpr (F == FMT_IF4) return q < 8 ? (double)grid_value<FMT_E2M1>(q) : (double)(q - 8);
+    return (double)grid_value<F>(q);
+}
+
 template <int F, int S, int IN, bool RHT>
-__global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
+__global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_of(S) == 16 ? 3 : 2))) void stats_kernel(const StatsArgs a)
 {
     constexpr int B = block_of(S);
     constexpr bool IF4 = F == FMT_IF4;
     constexpr int FG = IF4 ? FMT_E2M1 : F;
     constexpr int NBIN = IF4 ? 16 : 8;  // code k, or 8 + k in IF4's INT4 blocks
     constexpr bool FOLD = RHT && IN == IN_BF16;
-    __shared__ double bias_bin[NBIN][STATS_T];
-    __shared__ uint32_t count_bin[NBIN][STATS_T];
+    __shared__ uint64_t bins[NBIN][STATS_T];
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < NBIN; ++q) {
-        bias_bin[q][tid] = 0.0;
-        count_bin[q][tid] = 0u;
-    }
-    double acc[9];
+    for (int q = 0; q < NBIN; ++q) bins[q][tid] = 0u;
+    double acc[6];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) acc[k] = 0.0;
+    for (int k = 0; k < 6; ++k) acc[k] = 0.0;
+    uint32_t nblk = 0, nint4 = 0;
     float alpha = 0.0f;
     if constexpr (S == SC_E4M3) alpha = *a.tensor_scale;
     uint32_t sgn[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) sgn[i] = RHT ? ((a.smask >> i) & 1u) << 31 : 0u;
     const int64_t nb_row = a.L / B;
-    const int64_t nblocks = a.V * nb_row;
     const int64_t step = (int64_t)gridDim.x * STATS_T;
 
-    // Block t is block j of view row v: t = v nb_row + j (row axis) or
-    // t = j V + v (column axis).  The position advances by a fixed step per
-    // iteration, so it is kept as a (major, minor) pair and stepped without
-    // divisions.
-    const int64_t minor_n = a.axis == 0 ? nb_row : a.V;
-    const int64_t d_major = step / minor_n, d_minor = step - d_major * minor_n;
-    auto load = [&](int64_t major, int64_t minor, StatsRaw<B, IN> &r, uint32_t (&cw)[B / 8], uint32_t &sraw) {
-        const int64_t v = a.axis == 0 ? major : minor, j = a.axis == 0 ? minor : major;
-        if (a.axis == 0) {
-            const int64_t idx = v * a.ldx + j * B;
-            if constexpr (IN == IN_BF16) {
-                const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + idx);
-#pragma unroll
-                for (int c = 0; c < B / 8; ++c) r.w[c] = p[c];
-            } else {
-                const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + idx);
-#pragma unroll
-                for (int c = 0; c < B / 4; ++c) r.w[c] = p[c];
-            }
-        } else {
-            if constexpr (IN == IN_BF16) {
-                const uint16_t *p = static_cast<const uint16_t *>(a.x) + (j * B) * a.ldx + v;
-                uint32_t h[B];
-#pragma unroll
-                for (int i = 0; i < B; ++i) h[i] = p[i * a.ldx];
-#pragma unroll
-                for (int c = 0; c < B / 8; ++c)
-                    r.w[c] = make_uint4(h[8 * c] | (h[8 * c + 1] << 16), h[8 * c + 2] | (h[8 * c + 3] << 16),
-                                        h[8 * c + 4] | (h[8 * c + 5] << 16), h[8 * c + 6] | (h[8 * c + 7] << 16));
-            } else {
-                const float *p = static_cast<const float *>(a.x) + (j * B) * a.ldx + v;
-#pragma unroll
-                for (int c = 0; c < B / 4; ++c)
-                    r.w[c] = make_float4(p[(4 * c) * a.ldx], p[(4 * c + 1) * a.ldx], p[(4 * c + 2) * a.ldx],
-                                         p[(4 * c + 3) * a.ldx]);
-            }
-        }
-        // the block's B / 2 code bytes as 32-bit words (codes are 4-byte aligned)
-        const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.codes + (v * a.L + j * B) / 2);
-#pragma unroll
-        for (int i = 0; i < B / 8; ++i) cw[i] = cp[i];
-        const int64_t sidx = v * nb_row + j;
-        if constexpr (S == SC_FP32)
-            sraw = __float_as_uint(static_cast<const float *>(a.scales)[sidx]);
-        else
-            sraw = static_cast<const uint8_t *>(a.scales)[sidx];
-    };
-
-    int64_t t = (int64_t)blockIdx.x * STATS_T + tid;
-    int64_t major = t / minor_n, minor = t - major * minor_n;
-    StatsRaw<B, IN> raw;
-    uint32_t cw[B / 8], sraw = 0;
-    if (t < nblocks) load(major, minor, raw, cw, sraw);
-    while (t < nblocks) {
-        // unpack and transform the current block, then start the next one's loads
-        float y[B];
-        if constexpr (IN == IN_BF16) {
-#pragma unroll
-            for (int c = 0; c < B / 8; ++c) {
-                const uint32_t ws[4] = {raw.w[c].x, raw.w[c].y, raw.w[c].z, raw.w[c].w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const int i = 8 * c + 2 * h;
-                    y[i] = u2f((ws[h] << 16) ^ sgn[i & 15]);
-                    y[i + 1] = u2f((ws[h] & 0xFFFF0000u) ^ sgn[(i + 1) & 15]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < B / 4; ++c) {
-                const float4 w = raw.w[c];
-                y[4 * c] = u2f(f2u(w.x) ^ sgn[(4 * c) & 15]);
-                y[4 * c + 1] = u2f(f2u(w.y) ^ sgn[(4 * c + 1) & 15]);
-                y[4 * c + 2] = u2f(f2u(w.z) ^ sgn[(4 * c + 2) & 15]);
-                y[4 * c + 3] = u2f(f2u(w.w) ^ sgn[(4 * c + 3) & 15]);
-            }
-        }
-        uint32_t c_cur[B / 8];
-#pragma unroll
-        for (int i = 0; i < B / 8; ++i) c_cur[i] = cw[i];
-        const uint32_t s_cur = sraw;
-        const int64_t tn = t + step;
-        minor += d_minor;
-        major += d_major;
-        if (minor >= minor_n) {
-            minor -= minor_n;
-            ++major;
-        }
-        if (tn < nblocks) load(major, minor, raw, cw, sraw);
+    // One block: its values (the source's, signs applied), code words and
+    // stored scale.
+    auto block = [&](float (&y)[B], const uint32_t (&c_cur)[B / 8], uint32_t s_cur) {
         // the transform; for bf16 sources its final x 1/4 is folded into the
         // scale (y = v / 4 exactly, every partial sum being a multiple of
-        // 2^-133), so the loop below works on v = 4y, 4 x_hat and 4e
+        // 2^-133), so the sums below are of 4 y, 4 x_hat and 4 e
         if constexpr (RHT) {
 #pragma unroll
             for (int c = 0; c < B; c += 16) {
@@ -368,41 +331,7 @@ __global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
             int4 = IF4 && (s_cur & 0x80u);
         }
         const float sk = FOLD ? s * 4.0f : s;  // exact
-        // z = |y| / s (IF4's INT4 blocks: |y| 7/6 / s) as one product with
-        // the rounded reciprocal: within 1.5 units in the last place of the
-        // correctly rounded quotient, far inside the bias sums' tolerance.
-        // Scales outside [2^-75, 2^125] (where the reciprocal would leave the
-        // normal range) take the true quotient.
-        const float pre = int4 ? 7.0f / 6.0f : 1.0f;
-        const float zinv = s == 0.0f ? 0.0f : pre / sk;
-        float z[B];
-#pragma unroll
-        for (int i = 0; i < B; ++i) z[i] = fabsf(y[i]) * zinv;
-        if constexpr (S != SC_E8M0) {
-            const bool slow = s != 0.0f && !fast_div_ok(s);
-            if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-                if (slow) {
-#pragma unroll
-                    for (int i = 0; i < B; ++i) z[i] = (fabsf(y[i]) * pre) / sk;
-                }
-            }
-        }
-        const float post = int4 ? 6.0f / 7.0f : 1.0f;
-        const int bin0 = int4 ? 8 : 0;
-        // The block's terms are summed in binary32 after scaling the block by
-        // a power of two P near 1 / s (exact), so that squares of values up to
-        // the binary32 maximum neither overflow nor lose precision; the sums
-        // are scaled back exactly in binary64.  With s = 0 (an all-zero block,
-        // or an E4M3 block scale that rounded to zero) P comes from the tensor
-        // scale alpha, above every such block's values.
-        const float pref = s != 0.0f ? s : (S == SC_E4M3 ? alpha : 1.0f);
-        int pe = pref != 0.0f ? __builtin_amdgcn_frexp_expf(pref) : 0;
-        pe = pe > 126 ? 126 : (pe < -126 ? -126 : pe);
-        const float P = __builtin_amdgcn_ldexpf(1.0f, -pe);
-        const float skp = sk * P;  // exact
-        const double Pinv = __builtin_amdgcn_ldexp(1.0, pe), Pinv2 = Pinv * Pinv;
-        // grid values of the codes: E2M1 codes by the hardware FP4 decode
-        // (two per instruction, signed, exact), the uniform grids as k x step
+        // signed grid values of the codes
         float gv[B];
         if constexpr (e2m1_codes(FG)) {
 #pragma unroll
@@ -411,106 +340,295 @@ __global__ __launch_bounds__(STATS_T) void stats_kernel(const StatsArgs a)
                 gv[i] = d.x;
                 gv[i + 1] = d.y;
             }
-        }
-        // binary32 sums over the block's two halves, then binary64
-        float p1[2] = {0.f, 0.f}, p2[2] = {0.f, 0.f}, p3[2] = {0.f, 0.f}, p4[2] = {0.f, 0.f}, p5[2] = {0.f, 0.f},
-              p6[2] = {0.f, 0.f};
+            if constexpr (IF4) {
+                float gi[B];
 #pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const int h = (2 * i) / B;
-            const uint32_t sh = 4 * (i & 7);
-            const uint32_t k = (c_cur[i >> 3] >> sh) & 7u;
-            float gs;  // signed grid value
-            if constexpr (e2m1_codes(FG)) {
-                gs = gv[i];
-                if constexpr (IF4) {
-                    const float gi = u2f(f2u((float)k) | ((c_cur[i >> 3] << (28 - sh)) & 0x80000000u));
-                    gs = int4 ? gi : gs;
+                for (int w = 0; w < B / 8; ++w) decode8_uniform<FMT_INT4>(c_cur[w], gi + 8 * w);
+#pragma unroll
+                for (int i = 0; i < B; ++i) gv[i] = int4 ? gi[i] : gv[i];
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < B / 8; ++w) decode8_uniform<FG>(c_cur[w], gv + 8 * w);
+        }
+        // x_hat = g s (IF4's INT4 blocks: (g s) 6/7); z = |y| / s (INT4
+        // blocks: |y| 7/6 / s) in units of 2^-26, as one product with the
+        // refined reciprocal
+        const float post = int4 ? 6.0f / 7.0f : 1.0f;
+        const float pre = int4 ? 7.0f / 6.0f * 0x1p26f : 0x1p26f;
+        const int bin0 = int4 ? 8 : 0;
+        // With s = 0 (an all-zero block, or an E4M3 block scale that rounded
+        // to zero) the block's scale of reference is the tensor scale alpha,
+        // above every such block's values.
+        const float pref = s != 0.0f ? s : (S == SC_E4M3 ? alpha : 1.0f);
+        const bool far = !(pref >= 0x1p-30f && pref <= 0x1p30f);
+        auto terms = [&](auto scaled) {
+            constexpr bool SCALED = decltype(scaled)::value;
+            int pe = 0;
+            float P = 1.0f;
+            if constexpr (SCALED) {
+                pe = pref != 0.0f ? __builtin_amdgcn_frexp_expf(pref) : 0;
+                pe = pe > 126 ? 126 : (pe < -126 ? -126 : pe);
+                P = __builtin_amdgcn_ldexpf(1.0f, -pe);
+            }
+            const float skp = SCALED ? sk * P : sk;  // exact
+            const float zinv = s == 0.0f ? 0.0f : pre * rcp_refined(skp);
+            float p1 = 0.f, p2 = 0.f, p3 = 0.f, p4 = 0.f, p5 = 0.f, p6 = 0.f;
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                const float v = SCALED ? y[i] * P : y[i];
+                const float xk = IF4 ? (gv[i] * skp) * post : gv[i] * skp;  // P x_hat (x 4 when folded)
+                const float ek = xk - v;
+                p1 = __builtin_fmaf(v, v, p1);
+                p2 = __builtin_fmaf(ek, ek, p2);
+                p3 += ek;
+                p4 += u2f(f2u(ek) ^ (f2u(v) & 0x80000000u));  // sign(y) e (y = +-0 gives e = +-0)
+                p5 = __builtin_fmaf(xk, v, p5);
+                p6 += fabsf(ek);
+                const uint32_t k = (c_cur[i >> 3] >> (4 * (i & 7))) & 7u;
+                const uint32_t zf = (uint32_t)(fabsf(v) * zinv);
+                atomicAdd(&bins[bin0 + (int)k][tid], (1ull << 48) | zf);
+            }
+            constexpr double F2 = FOLD ? 1.0 / 16.0 : 1.0, F1 = FOLD ? 0.25 : 1.0;  // exact
+            double G2 = F2, G1 = F1;
+            if constexpr (SCALED) {
+                G2 = __builtin_amdgcn_ldexp(F2, 2 * pe);
+                G1 = __builtin_amdgcn_ldexp(F1, pe);
+            }
+            acc[0] = __builtin_fma((double)p1, G2, acc[0]);
+            acc[1] = __builtin_fma((double)p2, G2, acc[1]);
+            acc[2] = __builtin_fma((double)p3, G1, acc[2]);
+            acc[3] = __builtin_fma((double)p4, G1, acc[3]);
+            acc[4] = __builtin_fma((double)p5, G2, acc[4]);
+            acc[5] = __builtin_fma((double)p6, G1, acc[5]);
+        };
+        if (__builtin_amdgcn_ballot_w64(far) == 0)
+            terms(std::false_type{});
+        else
+            terms(std::true_type{});
+        ++nblk;
+        if constexpr (IF4) nint4 += int4 ? 1u : 0u;
+    };
+
+    // Block t is block j of view row v: t = v nb_row + j (row axis) or
+    // t = j V + v (column axis).  Loads run two blocks ahead of the block
+    // being processed (16-element blocks; one block ahead for 32), in two
+    // register sets used in turn; their position advances by a fixed step,
+    // so it is kept as a (major, minor) pair and stepped without divisions.
+    const int64_t minor_n = a.axis == 0 ? nb_row : a.V;
+    const int64_t d_major = step / minor_n, d_minor = step - d_major * minor_n;
+    const int64_t first = a.t0 + (int64_t)blockIdx.x * STATS_T + tid;
+    int64_t lt = first, major = first / minor_n, minor = first - major * minor_n;
+    auto advance = [&] {
+        lt += step;
+        minor += d_minor;
+        major += d_major;
+        if (minor >= minor_n) {
+            minor -= minor_n;
+            ++major;
+        }
+    };
+    // the block's B / 2 code bytes and its scale
+    auto load_codes = [&](int64_t coff, int64_t sidx, uint32_t (&cw)[B / 8], uint32_t &sraw) {
+        if constexpr (B == 16) {
+            const uint2 c2 = *reinterpret_cast<const uint2 *>(a.codes + coff);
+            cw[0] = c2.x;
+            cw[1] = c2.y;
+        } else {
+            const uint4 c4 = *reinterpret_cast<const uint4 *>(a.codes + coff);
+            cw[0] = c4.x;
+            cw[1] = c4.y;
+            cw[2] = c4.z;
+            cw[3] = c4.w;
+        }
+        if constexpr (S == SC_FP32)
+            sraw = __float_as_uint(static_cast<const float *>(a.scales)[sidx]);
+        else
+            sraw = static_cast<const uint8_t *>(a.scales)[sidx];
+    };
+    auto run = [&](auto &s0, auto &s1, auto load, auto unpack) {
+        auto issue = [&](auto &d) {
+            if (lt < a.t1) load(d);
+            advance();
+        };
+        auto take = [&](auto &d) {
+            float y[B];
+            unpack(d, y);
+            uint32_t c[B / 8];
+#pragma unroll
+            for (int i = 0; i < B / 8; ++i) c[i] = d.cw[i];
+            const uint32_t sc = d.s;
+            issue(d);
+            block(y, c, sc);
+        };
+        if constexpr (B == 16) {
+            issue(s0);
+            issue(s1);
+            for (int64_t t = first; t < a.t1;) {
+                take(s0);
+                t += step;
+                if (t >= a.t1) break;
+                take(s1);
+                t += step;
+            }
+        } else {
+            // 32-element blocks: one set (two would cost resident waves)
+            issue(s0);
+            for (int64_t t = first; t < a.t1; t += step) take(s0);
+        }
+    };
+    if (a.axis == 0) {
+        // row axis: block t = (v, j) holds B consecutive elements of view
+        // row v, one vector load; its codes sit at t B / 2, its scale at t
+        struct Set {
+            StatsRaw<B, IN> raw;
+            uint32_t cw[B / 8];
+            uint32_t s;
+        } s0, s1;
+        auto load = [&](Set &d) {
+            const int64_t idx = major * a.ldx + minor * B;
+            if constexpr (IN == IN_BF16) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + idx);
+#pragma unroll
+                for (int c = 0; c < B / 8; ++c) d.raw.w[c] = p[c];
+            } else {
+                const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + idx);
+#pragma unroll
+                for (int c = 0; c < B / 4; ++c) d.raw.w[c] = p[c];
+            }
+            load_codes(lt * (B / 2), lt, d.cw, d.s);
+        };
+        auto unpack = [&](const Set &d, float (&y)[B]) {
+            if constexpr (IN == IN_BF16) {
+#pragma unroll
+                for (int c = 0; c < B / 8; ++c) {
+                    const uint32_t ws[4] = {d.raw.w[c].x, d.raw.w[c].y, d.raw.w[c].z, d.raw.w[c].w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const int i = 8 * c + 2 * h;
+                        y[i] = u2f((ws[h] << 16) ^ sgn[i & 15]);
+                        y[i + 1] = u2f((ws[h] & 0xFFFF0000u) ^ sgn[(i + 1) & 15]);
+                    }
                 }
             } else {
-                gs = u2f(f2u(grid_value<FG>(k)) | ((c_cur[i >> 3] << (28 - sh)) & 0x80000000u));
+#pragma unroll
+                for (int c = 0; c < B / 4; ++c) {
+                    const float4 w = d.raw.w[c];
+                    y[4 * c] = u2f(f2u(w.x) ^ sgn[(4 * c) & 15]);
+                    y[4 * c + 1] = u2f(f2u(w.y) ^ sgn[(4 * c + 1) & 15]);
+                    y[4 * c + 2] = u2f(f2u(w.z) ^ sgn[(4 * c + 2) & 15]);
+                    y[4 * c + 3] = u2f(f2u(w.w) ^ sgn[(4 * c + 3) & 15]);
+                }
             }
-            // P x_hat = (g s P) post with the code's sign (post = 1 is exact); x 4 when folded
-            const float xk = (gs * skp) * post;
-            const float v = y[i] * P;
-            const float ek = xk - v;
-            p1[h] = __builtin_fmaf(v, v, p1[h]);
-            p2[h] = __builtin_fmaf(ek, ek, p2[h]);
-            p3[h] += ek;
-            p4[h] += u2f(f2u(ek) ^ (f2u(v) & 0x80000000u));  // sign(y) e (y = +-0 gives e = +-0)
-            p5[h] = __builtin_fmaf(xk, v, p5[h]);
-            p6[h] += fabsf(ek);
-            const int bin = bin0 + (int)k;
-            atomicAdd(&bias_bin[bin][tid], (double)(fabsf(gs) - z[i]));
-            atomicAdd(&count_bin[bin][tid], 1u);
-        }
-        constexpr double F2 = FOLD ? 1.0 / 16.0 : 1.0, F1 = FOLD ? 0.25 : 1.0;  // exact
-        const double G2 = F2 * Pinv2, G1 = F1 * Pinv;                             // exact
-        acc[0] += (double)B;
-        acc[1] = __builtin_fma((double)(p1[0] + p1[1]), G2, acc[1]);
-        acc[2] = __builtin_fma((double)(p2[0] + p2[1]), G2, acc[2]);
-        acc[3] = __builtin_fma((double)(p3[0] + p3[1]), G1, acc[3]);
-        acc[4] = __builtin_fma((double)(p4[0] + p4[1]), G1, acc[4]);
-        acc[5] = __builtin_fma((double)(p5[0] + p5[1]), G2, acc[5]);
-        acc[6] = __builtin_fma((double)(p6[0] + p6[1]), G1, acc[6]);
-        acc[7] += 1.0;
-        if constexpr (IF4) acc[8] += int4 ? 1.0 : 0.0;
-        t = tn;
+        };
+        run(s0, s1, load, unpack);
+    } else {
+        // column axis: block t = (v, j) holds source elements x[j B + i][v];
+        // consecutive lanes take consecutive v, so each of the B loads
+        // coalesces.  The loaded values are kept as they arrive and unpacked
+        // when the block is processed.
+        struct Set {
+            uint32_t h[B];
+            uint32_t cw[B / 8];
+            uint32_t s;
+        } s0, s1;
+        auto load = [&](Set &d) {
+            const int64_t v = minor, j = major;
+            if constexpr (IN == IN_BF16) {
+                const uint16_t *p = static_cast<const uint16_t *>(a.x) + (j * B) * a.ldx + v;
+#pragma unroll
+                for (int i = 0; i < B; ++i) d.h[i] = p[i * a.ldx];
+            } else {
+                const uint32_t *p = static_cast<const uint32_t *>(a.x) + (j * B) * a.ldx + v;
+#pragma unroll
+                for (int i = 0; i < B; ++i) d.h[i] = p[i * a.ldx];
+            }
+            load_codes((v * a.L + j * B) / 2, v * nb_row + j, d.cw, d.s);
+        };
+        auto unpack = [&](const Set &d, float (&y)[B]) {
+#pragma unroll
+            for (int i = 0; i < B; ++i) y[i] = u2f((IN == IN_BF16 ? d.h[i] << 16 : d.h[i]) ^ sgn[i & 15]);
+        };
+        run(s0, s1, load, unpack);
     }
-    double out[NS];
+
+    // The sums a format can make nonzero, reduced over the workgroup and
+    // stored (or, after the first launch, added) at their places in the
+    // 48-sum layout: 0..8, then the counts and bias sums of the NBIN bins
+    // (the others are zero).  Each thread reads back only its own bins.
+    constexpr int NV = 9 + 2 * NBIN;
+    double out[NV];
+    out[0] = (double)nblk * B;
 #pragma unroll
-    for (int k = 0; k < 9; ++k) out[k] = acc[k];
-#pragma unroll
-    for (int k = 9; k < NS; ++k) out[k] = 0.0;
-    // each thread reads back only its own bins (its own LDS adds are done in
-    // order before these reads)
+    for (int k = 0; k < 6; ++k) out[1 + k] = acc[k];
+    out[7] = (double)nblk;
+    out[8] = (double)nint4;
 #pragma unroll
     for (int q = 0; q < NBIN; ++q) {
-        out[16 + q] = (double)count_bin[q][tid];
-        out[32 + q] = bias_bin[q][tid];
+        const uint64_t u = bins[q][tid];
+        const double n = (double)(uint32_t)(u >> 48);
+        out[9 + q] = n;
+        out[9 + NBIN + q] = n * bin_grid<F>(q) - (double)(u & 0xFFFFFFFFFFFFull) * 0x1p-26;
     }
-    block_reduce_store<NS>(out, a.partials + (int64_t)blockIdx.x * NS);
+    double *dst = a.partials + (int64_t)blockIdx.x * NS;
+    block_reduce_store<NV>(
+        out, dst, [](int k) { return k < 9 ? k : (k < 9 + NBIN ? 16 + (k - 9) : 32 + (k - 9 - NBIN)); },
+        a.accumulate != 0);
+    // the sums no bin of this format touches: 9..15, and with 8 bins the
+    // INT4-block counts 24..31 and bias sums 40..47
+    if (tid < NS - NV) dst[tid < 7 ? 9 + tid : (tid < 15 ? 24 + (tid - 7) : 40 + (tid - 15))] = 0.0;
 }
 
 // Workgroups of the statistics grid: as many per compute unit of the current
 // device as are resident at once, at most one per STATS_T blocks, at most
 // STATS_WGS (the workspace rows).
-static int stats_grid(int64_t nblocks, int per_cu)
+template <typename K>
+static int stats_grid(K kernel, int64_t nblocks)
 {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
-        (void)hipGetLastError();
-        cus = 256;
-    }
+    static const int per_cu = [kernel] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, STATS_T, 0) != hipSuccess || n < 1) n = 1;
+        return n;
+    }();
     int64_t g = (nblocks + STATS_T - 1) / STATS_T;
-    const int64_t resident = (int64_t)cus * per_cu;
+    const int64_t resident = (int64_t)cu_count() * per_cu;
     if (g > resident) g = resident;
     if (g > STATS_WGS) g = STATS_WGS;
     return g < 1 ? 1 : (int)g;
 }
 
+// One or more launches over consecutive ranges of blocks (each thread takes
+// at most STATS_CHUNK elements per launch), the later ones adding to the
+// partial sums, then the reduction.
+template <typename K>
+static hipError_t stats_run(K kernel, int B, StatsArgs a, hipStream_t st)
+{
+    const int64_t nblocks = a.V * (a.L / B);
+    const int g = stats_grid(kernel, nblocks);
+    const int64_t per_launch = (int64_t)g * STATS_T * (STATS_CHUNK / B);
+    int64_t t0 = 0;
+    do {
+        a.t0 = t0;
+        a.t1 = nblocks - t0 > per_launch ? t0 + per_launch : nblocks;
+        a.accumulate = t0 > 0;
+        launch_kernel(kernel, dim3((unsigned)g), dim3(STATS_T), st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        t0 = a.t1;
+    } while (t0 < nblocks);
+    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(256), st, a.partials, g, a.sums);
+    return hipGetLastError();
+}
+
 template <int F, int S>
 static hipError_t stats_pick(int in_dtype, int rht, const StatsArgs &a, hipStream_t st)
 {
-    const int64_t nblocks = a.V * (a.L / block_of(S));
-    const int g = stats_grid(nblocks, stats_wg_per_cu(block_of(S)));
-    const dim3 grid((unsigned)g);
-    if (in_dtype == IN_BF16) {
-        if (rht)
-            launch_kernel((stats_kernel<F, S, IN_BF16, true>), grid, dim3(STATS_T), st, a);
-        else
-            launch_kernel((stats_kernel<F, S, IN_BF16, false>), grid, dim3(STATS_T), st, a);
-    } else {
-        if (rht)
-            launch_kernel((stats_kernel<F, S, IN_F32, true>), grid, dim3(STATS_T), st, a);
-        else
-            launch_kernel((stats_kernel<F, S, IN_F32, false>), grid, dim3(STATS_T), st, a);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(256), st, a.partials, g, a.sums);
-    return hipGetLastError();
+    constexpr int B = block_of(S);
+    if (in_dtype == IN_BF16)
+        return rht ? stats_run(stats_kernel<F, S, IN_BF16, true>, B, a, st)
+                   : stats_run(stats_kernel<F, S, IN_BF16, false>, B, a, st);
+    return rht ? stats_run(stats_kernel<F, S, IN_F32, true>, B, a, st)
+               : stats_run(stats_kernel<F, S, IN_F32, false>, B, a, st);
 }
 
 hipError_t launch_stats(int format, int scale, int in_dtype, int rht, const StatsArgs &a, hipStream_t st)
@@ -553,7 +671,7 @@ __global__ __launch_bounds__(256) void eta_kernel(const float *zq, const float *
             acc[2] += d * d;
         }
     }
-    block_reduce_store<3>(acc, partials + (int64_t)blockIdx.x * 3);
+    block_reduce_store<3>(acc, partials + (int64_t)blockIdx.x * 3, [](int k) { return k; });
 }
 
 hipError_t launch_eta(const float *zq, const float *z, int64_t M, int64_t N, int64_t ld, double *partials,

@@ -21,8 +21,6 @@
 // are free of bank conflicts.  The grid is persistent, one workgroup per
 // compute unit, each taking its tiles in turn through the same ring; tiles
 // are ordered so that the eight XCDs each work on a compact band of them.
-#include <atomic>
-
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -476,20 +474,7 @@ __global__ __launch_bounds__(GTH, 1) void gemm_kernel(const uint8_t *__restrict_
 // device (the kernel's LDS ring fills a CU), at most one per tile.
 static unsigned gemm_grid(int64_t tiles)
 {
-    static std::atomic<int> cus[64];
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-        n = cus[dev].load(std::memory_order_relaxed);
-        if (n <= 0) {
-            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-                (void)hipGetLastError();  // fall back to the MI355X count below
-                n = 0;
-            } else {
-                cus[dev].store(n, std::memory_order_relaxed);
-            }
-        }
-    }
-    if (n <= 0) n = 256;
+    const int n = cu_count();
     return (unsigned)(tiles < n ? tiles : n);
 }
 

@@ -30,6 +30,10 @@ inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipS
     }
 }
 
+// Compute units of the current device, read once per device and kept (256,
+// the MI355X's count, if the query fails).
+int cu_count();
+
 // Row kernel: one lane per 16-element chunk of a view row.
 struct RowArgs {
     const void *x;        // source (ROW axis: the view itself)
@@ -105,8 +109,10 @@ struct StatsArgs {
     const float *tensor_scale;
     double *partials;  // [grid][48]
     double *sums;      // [48]
+    int64_t t0, t1;    // blocks [t0, t1) of the view (set per launch)
+    int accumulate;    // add to the partial sums instead of storing them
 };
-constexpr int STATS_WGS = 1024;
+constexpr int STATS_WGS = 2048;
 hipError_t launch_stats(int format, int scale, int in_dtype, int rht, const StatsArgs &a, hipStream_t st);
 
 constexpr int ETA_WGS = 1024;

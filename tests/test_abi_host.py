@@ -117,7 +117,7 @@ def test_empty_inputs_are_no_ops():
 
 
 def test_workspace_sizes():
-    assert U.ufp4_workspace_size(U.OP_STATS, 100, 64) == 1024 * 48 * 8
+    assert U.ufp4_workspace_size(U.OP_STATS, 100, 64) == 2048 * 48 * 8      # one row of 48 sums per workgroup
     assert U.ufp4_workspace_size(U.OP_ETA, 100, 64) == 1024 * 3 * 8
     assert U.ufp4_workspace_size(U.OP_AMAX, 8192, 8192, U.Cfg()) == 4096 * 4      # one per 1024 chunks
     assert U.ufp4_workspace_size(U.OP_AMAX, 16384, 4096, U.Cfg(axis="col")) == 64 * 32 * 4

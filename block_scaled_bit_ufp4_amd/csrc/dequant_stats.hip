@@ -172,18 +172,37 @@ __device__ __forceinline__ void block_reduce_store(double (&acc)[NV], double *ou
     }
 }
 
-// One workgroup adds nwg rows of NV partial sums in a fixed order: wave w
-// takes sums w, w + 4, ...; for each, lane l adds rows l, l + 64, ... and the
-// wave adds its lanes by shuffles.  No barriers.
+// One workgroup of 1024 threads adds nwg rows of NV partial sums.  Thread t
+// (t < G NV, G = 1024 / NV groups) takes sum k = t mod NV over rows g,
+// g + G, g + 2G, ... (g = t / NV) into eight accumulators used in turn, so
+// eight loads are in flight and each load instruction of the workgroup reads
+// consecutive doubles; the G group sums of each k are then added in group
+// order.  The order is fixed, so the result is the same on every run.
+constexpr int RED_T = 1024;
 template <int NV>
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const double *partials, int nwg, double *sums)
+__global__ __launch_bounds__(RED_T) void reduce_partials_kernel(const double *partials, int nwg, double *sums)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int k = wave; k < NV; k += 4) {
+    constexpr int G = RED_T / NV;
+    __shared__ double part[G][NV];
+    const int t = threadIdx.x;
+    if (t < G * NV) {
+        const int k = t % NV, g = t / NV;
+        double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+        int i = g;
+        for (; i + 7 * G < nwg; i += 8 * G) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] += partials[(int64_t)(i + u * G) * NV + k];
+        }
+#pragma unroll
+        for (int u = 0; u < 7; ++u)
+            if (i + u * G < nwg) acc[u] += partials[(int64_t)(i + u * G) * NV + k];
+        part[g][k] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    }
+    __syncthreads();
+    if (t < NV) {
         double v = 0.0;
-        for (int i = lane; i < nwg; i += 64) v += partials[(int64_t)i * NV + k];
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0) sums[k] = v;
+        for (int g = 0; g < G; ++g) v += part[g][t];
+        sums[t] = v;
     }
 }
 
@@ -191,8 +210,8 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const double *part
 // Statistics: one thread per block of the view.  Row axis: consecutive lanes
 // take consecutive blocks of a view row, and a block's elements are one
 // vector load; column axis: consecutive lanes take consecutive view rows (=
-// source columns), so the loads x[l][v] coalesce.  The next block's loads are
-// issued before the current block is processed.
+// source columns), so the loads x[l][v] coalesce.  Loads run up to three
+// blocks ahead of the block being processed.
 //
 // Sums 1..6 are binary64 registers.  Each block's terms are first summed in
 // binary32 (the element's products and the error e = x_hat - y are binary32
@@ -220,6 +239,10 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const double *part
 constexpr int NS = 48;
 constexpr int STATS_T = 256;
 constexpr int64_t STATS_CHUNK = 1 << 15;  // elements per thread and launch
+// Blocks whose loads are in flight per thread: three for 16-element blocks
+// (two for IF4, whose 16 bins and two candidates take more registers), one
+// for 32-element blocks (a second set would cost a resident wave).
+constexpr int STATS_DEPTH(int B, bool IF4) { return B == 16 ? (IF4 ? 2 : 3) : 1; }
 
 template <int B, int IN>
 struct StatsRaw;
@@ -411,10 +434,10 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
     };
 
     // Block t is block j of view row v: t = v nb_row + j (row axis) or
-    // t = j V + v (column axis).  Loads run two blocks ahead of the block
-    // being processed (16-element blocks; one block ahead for 32), in two
-    // register sets used in turn; their position advances by a fixed step,
-    // so it is kept as a (major, minor) pair and stepped without divisions.
+    // t = j V + v (column axis).  Loads run STATS_DEPTH blocks ahead of the
+    // block being processed, in register sets used in turn; their position
+    // advances by a fixed step, so it is kept as a (major, minor) pair and
+    // stepped without divisions.
     const int64_t minor_n = a.axis == 0 ? nb_row : a.V;
     const int64_t d_major = step / minor_n, d_minor = step - d_major * minor_n;
     const int64_t first = a.t0 + (int64_t)blockIdx.x * STATS_T + tid;
@@ -446,47 +469,53 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
         else
             sraw = static_cast<const uint8_t *>(a.scales)[sidx];
     };
-    auto run = [&](auto &s0, auto &s1, auto load, auto unpack) {
+    // Every load is issued unconditionally (a position past the range
+    // reloads the thread's first block), so no branch surrounds a load and the
+    // waits stay as deep as the prefetch.
+    const int64_t major0 = major, minor0 = minor;
+    auto run = [&](auto (&sets)[STATS_DEPTH(B, IF4)], auto load, auto unpack) {
         auto issue = [&](auto &d) {
-            if (lt < a.t1) load(d);
+            load(d, lt < a.t1);
             advance();
         };
-        auto take = [&](auto &d) {
-            float y[B];
-            unpack(d, y);
-            uint32_t c[B / 8];
 #pragma unroll
-            for (int i = 0; i < B / 8; ++i) c[i] = d.cw[i];
-            const uint32_t sc = d.s;
-            issue(d);
-            block(y, c, sc);
-        };
-        if constexpr (B == 16) {
-            issue(s0);
-            issue(s1);
-            for (int64_t t = first; t < a.t1;) {
-                take(s0);
-                t += step;
-                if (t >= a.t1) break;
-                take(s1);
+        for (int k = 0; k < STATS_DEPTH(B, IF4); ++k) issue(sets[k]);
+        for (int64_t t = first; t < a.t1;) {
+#pragma unroll
+            for (int k = 0; k < STATS_DEPTH(B, IF4); ++k) {
+                float y[B];
+                unpack(sets[k], y);
+                // The set's registers are consumed before its next load is
+                // issued: the unpacked values are pinned in registers (so no
+                // use of them sinks into the branch below) and the code words
+                // and scale copied to fresh ones.  The load then reuses the
+                // set's registers, and the loop carries no copy of a register
+                // with a load in flight (which would wait for that load).
+#pragma unroll
+                for (int i = 0; i < B; ++i) asm volatile("" : "+v"(y[i]));
+                uint32_t c[B / 8], sc;
+#pragma unroll
+                for (int i = 0; i < B / 8; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(c[i]) : "v"(sets[k].cw[i]));
+                asm volatile("v_mov_b32 %0, %1" : "=v"(sc) : "v"(sets[k].s));
+                issue(sets[k]);
+                if (t < a.t1) block(y, c, sc);
                 t += step;
             }
-        } else {
-            // 32-element blocks: one set (two would cost resident waves)
-            issue(s0);
-            for (int64_t t = first; t < a.t1; t += step) take(s0);
         }
     };
-    if (a.axis == 0) {
+    if (first >= a.t1) {
+        // no block for this thread
+    } else if (a.axis == 0) {
         // row axis: block t = (v, j) holds B consecutive elements of view
         // row v, one vector load; its codes sit at t B / 2, its scale at t
         struct Set {
             StatsRaw<B, IN> raw;
             uint32_t cw[B / 8];
             uint32_t s;
-        } s0, s1;
-        auto load = [&](Set &d) {
-            const int64_t idx = major * a.ldx + minor * B;
+        } sets[STATS_DEPTH(B, IF4)];
+        auto load = [&](Set &d, bool ok) {
+            const int64_t tt = ok ? lt : first;
+            const int64_t idx = (ok ? major : major0) * a.ldx + (ok ? minor : minor0) * B;
             if constexpr (IN == IN_BF16) {
                 const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + idx);
 #pragma unroll
@@ -496,7 +525,7 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
 #pragma unroll
                 for (int c = 0; c < B / 4; ++c) d.raw.w[c] = p[c];
             }
-            load_codes(lt * (B / 2), lt, d.cw, d.s);
+            load_codes(tt * (B / 2), tt, d.cw, d.s);
         };
         auto unpack = [&](const Set &d, float (&y)[B]) {
             if constexpr (IN == IN_BF16) {
@@ -521,7 +550,7 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
                 }
             }
         };
-        run(s0, s1, load, unpack);
+        run(sets, load, unpack);
     } else {
         // column axis: block t = (v, j) holds source elements x[j B + i][v];
         // consecutive lanes take consecutive v, so each of the B loads
@@ -531,9 +560,9 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
             uint32_t h[B];
             uint32_t cw[B / 8];
             uint32_t s;
-        } s0, s1;
-        auto load = [&](Set &d) {
-            const int64_t v = minor, j = major;
+        } sets[STATS_DEPTH(B, IF4)];
+        auto load = [&](Set &d, bool ok) {
+            const int64_t v = ok ? minor : minor0, j = ok ? major : major0;
             if constexpr (IN == IN_BF16) {
                 const uint16_t *p = static_cast<const uint16_t *>(a.x) + (j * B) * a.ldx + v;
 #pragma unroll
@@ -549,7 +578,7 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
 #pragma unroll
             for (int i = 0; i < B; ++i) y[i] = u2f((IN == IN_BF16 ? d.h[i] << 16 : d.h[i]) ^ sgn[i & 15]);
         };
-        run(s0, s1, load, unpack);
+        run(sets, load, unpack);
     }
 
     // The sums a format can make nonzero, reduced over the workgroup and
@@ -616,7 +645,7 @@ static hipError_t stats_run(K kernel, int B, StatsArgs a, hipStream_t st)
         if (e != hipSuccess) return e;
         t0 = a.t1;
     } while (t0 < nblocks);
-    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(256), st, a.partials, g, a.sums);
+    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(RED_T), st, a.partials, g, a.sums);
     return hipGetLastError();
 }
 
@@ -680,7 +709,7 @@ hipError_t launch_eta(const float *zq, const float *z, int64_t M, int64_t N, int
     launch_kernel(eta_kernel, dim3(ETA_WGS), dim3(256), st, zq, z, M, N, ld, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    launch_kernel(reduce_partials_kernel<3>, dim3(1), dim3(256), st, partials, ETA_WGS, sums);
+    launch_kernel(reduce_partials_kernel<3>, dim3(1), dim3(RED_T), st, partials, ETA_WGS, sums);
     return hipGetLastError();
 }
 

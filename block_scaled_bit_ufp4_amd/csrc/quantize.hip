@@ -702,8 +702,18 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
 __global__ __launch_bounds__(1024) void amax_final_kernel(const float *partials, int64_t n, float *amax)
 {
     __shared__ float red[16];
-    float m = 0.0f;
-    for (int64_t i = threadIdx.x; i < n; i += 1024) m = fmaxf(m, partials[i]);
+    // four maxima in turn, so four loads are in flight (max is exact and
+    // order-free: any order gives the same result)
+    float m4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t i = threadIdx.x;
+    for (; i + 3 * 1024 < n; i += 4 * 1024) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m4[u] = fmaxf(m4[u], partials[i + u * 1024]);
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+        if (i + u * 1024 < n) m4[u] = fmaxf(m4[u], partials[i + u * 1024]);
+    float m = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();

@@ -30,8 +30,10 @@
  *     allocates nothing, keeps no pointer after a call returns and has no
  *     global state except, per host thread, the last HIP error and a pending
  *     ufp4_time_next_launch request, and, per process, each device's
- *     compute-unit count (read once by the first GEMM on that device, never
- *     changed after) and the device address of ufp4_amax_noalloc's built-in
+ *     compute-unit count (read once by the first GEMM or statistics call on
+ *     that device, never changed after), the resident workgroups per compute
+ *     unit of each statistics kernel (one occupancy query per kernel, the first
+ *     time it runs) and the device address of ufp4_amax_noalloc's built-in
  *     scratch array (looked up once per device).  Calls are reentrant and
  *     can be captured in a HIP graph (no allocation, no memset); calls of
  *     ufp4_amax_noalloc that overlap on one device share its scratch.

@@ -45,14 +45,20 @@ def test_mxfp4_gemm_matches_oracle(M, N, K, rht):
     assert rel_fro(z, want) < 1e-5  # exact products, binary32 sums
 
 
-@pytest.mark.parametrize("fmt", ["e1m2", "int4", "e2m1", "if4", "e2m1_max2"])
+@pytest.mark.parametrize("fmt", ["e1m2", "int4", "e2m1", "if4", "e2m1_max2", "mxfp4"])
 def test_dequant_bf16_gemm_matches_oracle(fmt):
+    """The dequantize-to-bf16 GEMM on every operand kind, MXFP4 (E8M0 per
+    32) included: the same operands the native mode takes."""
     U = lib()
     M, N, K = 256, 512, 256
     if fmt == "if4":  # Gaussian rows with uniform blocks, so both block types occur
         a, _ = S.mx_if4(M, K, seed=1, frac=0.3)
         b, _ = S.mx_if4(N, K, seed=2, frac=0.3)
         cfg = U.Cfg(fmt, "e4m3")
+    elif fmt == "mxfp4":
+        a = S.normal(M, K, 1.0, 1, "gemm_a")
+        b = S.normal(N, K, 1.0, 1, "gemm_b")
+        cfg = U.Cfg("e2m1", "e8m0", 32, rht="det")
     else:
         a = S.normal(M, K, 1.0, 1, "gemm_a")
         b = S.normal(N, K, 1.0, 1, "gemm_b")

@@ -47,7 +47,7 @@ __device__ __forceinline__ void nt_store16(void *p, uint32_t x, uint32_t y, uint
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 constexpr int CT = 256;  // column kernel: threads per workgroup
-constexpr int CTR = 512; // column kernel: source rows per workgroup
+constexpr int CTR = 2 * CT; // column kernel: source rows per workgroup (128 per wave)
 constexpr int CTC = 64;  // column kernel: source columns per workgroup
 constexpr int COL_GROUP = 8;  // column kernel: row tiles dispatched together
 
@@ -499,8 +499,8 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane & 7, b = lane >> 3;
     // Tile order: groups of COL_GROUP row tiles, row tile fastest, so the
-    // workgroups in flight write COL_GROUP x 256 contiguous code bytes of each
-    // view row while still sharing the source rows they read.
+    // workgroups in flight write COL_GROUP x CTR / 2 contiguous code bytes of
+    // each view row while still sharing the source rows they read.
     int ty, tx;
     {
         const int nx = (int)gridDim.x, ny = (int)gridDim.y;
@@ -650,37 +650,48 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         __syncthreads();
         const int64_t cv0 = (int64_t)tx * CTC;  // first view row of the tile
         const int64_t rs0 = (int64_t)ty * CTR;  // first source row
-        // codes: 64 view rows x 256 bytes, 16 lanes of 16 bytes per view row
+        // codes: CTC view rows x CTR / 2 bytes, CTR / 32 lanes of 16 bytes per
+        // view row
+        constexpr int CPARTS = CTR / 32;
 #pragma unroll
-        for (int q = 0; q < CTC * 16 / CT; ++q) {
-            const int idx = q * CT + tid, cl = idx >> 4, part = idx & 15;
+        for (int q = 0; q < CTC * CPARTS / CT; ++q) {
+            const int idx = q * CT + tid, cl = idx / CPARTS, part = idx % CPARTS;
             const uint2 u = st_codes[cl * CP + 2 * part], w = st_codes[cl * CP + 2 * part + 1];
             nt_store16(a.codes + (cv0 + cl) * (a.R >> 1) + (rs0 >> 1) + 16 * part, u.x, u.y, w.x, w.y);
         }
         if constexpr (S == SC_FP32) {
-            // 64 view rows x 32 scales (128 bytes), 8 lanes of 16 bytes per view row
+            // CTC view rows x NB scales (CTR / 4 bytes), CTR / 64 lanes of 16
+            // bytes per view row
+            constexpr int SPARTS = CTR / 64;
 #pragma unroll
-            for (int q = 0; q < CTC * 8 / CT; ++q) {
-                const int idx = q * CT + tid, cl = idx >> 3, part = idx & 7;
+            for (int q = 0; q < CTC * SPARTS / CT; ++q) {
+                const int idx = q * CT + tid, cl = idx / SPARTS, part = idx % SPARTS;
                 const float *p = st_scale + cl * CP + 4 * part;
                 nt_store16(static_cast<float *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) + 4 * part,
                            __float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3]));
             }
         } else if constexpr (S == SC_E4M3) {
-            // 64 view rows x 32 bytes, 2 lanes per view row
-            if (tid < CTC * 2) {
-                const int cl = tid >> 1, part = tid & 1;
+            // CTC view rows x NB bytes, NB / 16 lanes of 16 bytes per view row
+            constexpr int BPARTS = NB / 16;
+            if (tid < CTC * BPARTS) {
+                const int cl = tid / BPARTS, part = tid % BPARTS;
                 const uint4 q4 = *reinterpret_cast<const uint4 *>(st_sbyte + cl * NB + 16 * part);
                 nt_store16(static_cast<uint8_t *>(a.scales) + (cv0 + cl) * (a.R >> 4) + (rs0 >> 4) + 16 * part, q4.x,
                            q4.y, q4.z, q4.w);
             }
         } else {
-            // E8M0: 64 view rows x 16 bytes, one lane per view row
-            if (tid < CTC)
-            {
-                const uint4 q4 = *reinterpret_cast<const uint4 *>(st_sbyte + tid * NB);
-                nt_store16(static_cast<uint8_t *>(a.scales) + (cv0 + tid) * (a.R >> 5) + (rs0 >> 5), q4.x, q4.y, q4.z,
-                           q4.w);
+            // E8M0: CTC view rows x NB / 2 bytes, one lane per view row
+            if (tid < CTC) {
+                uint8_t *dst = static_cast<uint8_t *>(a.scales) + (cv0 + tid) * (a.R >> 5) + (rs0 >> 5);
+                if constexpr (NB / 2 == 16) {
+                    const uint4 q4 = *reinterpret_cast<const uint4 *>(st_sbyte + tid * NB);
+                    nt_store16(dst, q4.x, q4.y, q4.z, q4.w);
+                } else {
+                    static_assert(NB / 2 == 8, "E8M0 scale bytes per view row of a tile");
+                    const uint2 q2 = *reinterpret_cast<const uint2 *>(st_sbyte + tid * NB);
+                    const u32x2 v = {q2.x, q2.y};
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(dst));
+                }
             }
         }
     }

@@ -469,14 +469,14 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
         else
             sraw = static_cast<const uint8_t *>(a.scales)[sidx];
     };
-    // Every load is issued unconditionally (a position past the range
-    // reloads the thread's first block), so no branch surrounds a load and the
-    // waits stay as deep as the prefetch.
-    const int64_t major0 = major, minor0 = minor;
+    // Every load is issued unconditionally: the position stops at the
+    // thread's last block, which the loads past the range read again (from
+    // the cache, just after its first read), so no branch surrounds a load
+    // and the waits stay as deep as the prefetch.
     auto run = [&](auto (&sets)[STATS_DEPTH(B, IF4)], auto load, auto unpack) {
         auto issue = [&](auto &d) {
-            load(d, lt < a.t1);
-            advance();
+            load(d);
+            if (lt + step < a.t1) advance();
         };
 #pragma unroll
         for (int k = 0; k < STATS_DEPTH(B, IF4); ++k) issue(sets[k]);
@@ -513,9 +513,8 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
             uint32_t cw[B / 8];
             uint32_t s;
         } sets[STATS_DEPTH(B, IF4)];
-        auto load = [&](Set &d, bool ok) {
-            const int64_t tt = ok ? lt : first;
-            const int64_t idx = (ok ? major : major0) * a.ldx + (ok ? minor : minor0) * B;
+        auto load = [&](Set &d) {
+            const int64_t idx = major * a.ldx + minor * B;
             if constexpr (IN == IN_BF16) {
                 const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + idx);
 #pragma unroll
@@ -525,7 +524,7 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
 #pragma unroll
                 for (int c = 0; c < B / 4; ++c) d.raw.w[c] = p[c];
             }
-            load_codes(tt * (B / 2), tt, d.cw, d.s);
+            load_codes(lt * (B / 2), lt, d.cw, d.s);
         };
         auto unpack = [&](const Set &d, float (&y)[B]) {
             if constexpr (IN == IN_BF16) {
@@ -561,8 +560,8 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
             uint32_t cw[B / 8];
             uint32_t s;
         } sets[STATS_DEPTH(B, IF4)];
-        auto load = [&](Set &d, bool ok) {
-            const int64_t v = ok ? minor : minor0, j = ok ? major : major0;
+        auto load = [&](Set &d) {
+            const int64_t v = minor, j = major;
             if constexpr (IN == IN_BF16) {
                 const uint16_t *p = static_cast<const uint16_t *>(a.x) + (j * B) * a.ldx + v;
 #pragma unroll

@@ -83,6 +83,7 @@ struct BlockScale {
     float invd;     // RN(1 / sd)
     uint32_t byte;  // stored byte (E4M3 / E8M0)
     bool fast;      // Markstein division valid (or s == 0)
+    bool sub;       // E4M3 byte in the subnormal range (exponent field 0, nonzero)
 };
 
 // m: block amax of the transformed values y.  FOLD: the kernel holds 4y.
@@ -98,6 +99,7 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
         b.invd = __builtin_amdgcn_ldexpf(1.0f, -e - (FOLD ? 2 : 0));
         b.byte = (uint32_t)(e + 127);
         b.fast = true;
+        b.sub = false;
         return b;
     } else {
         if constexpr (S == SC_FP32) {
@@ -114,6 +116,7 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
             b.byte = e4m3_encode_hw(delta);
             b.s = t.alpha * e4m3_decode_hw(b.byte);
         }
+        b.sub = S == SC_E4M3 && (b.byte & 0x78u) == 0 && b.byte != 0;
         const float inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
         b.sd = FOLD ? b.s * 4.0f : b.s;
         b.invd = FOLD ? inv * 0.25f : inv;
@@ -177,9 +180,17 @@ __device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b,
         packed = pack8_e2m1(z);
     } else {
         if constexpr (S == SC_E4M3) {
-            // the E4M3 rounding of Delta can leave |z| above the grid maximum
+            // The E4M3 rounding of Delta can leave |z| above the grid maximum.
+            // Past the rounding boundary above it (gridmax + step / 2, where
+            // the FP8 convert would leave the code range) only under a block
+            // scale in E4M3's subnormal range: a normal one is within 1/16 of
+            // Delta, so |z| <= gridmax x 16/15 (3.73 < 3.75 for E1M2, 7.47 <
+            // 7.5 for INT4), where the convert's own rounding gives the same
+            // code as the clamp.  Only waves holding such a block clamp.
+            if (__builtin_amdgcn_ballot_w64(b.sub) != 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) z[i] = __builtin_amdgcn_fmed3f(z[i], -grid_max(F), grid_max(F));
+                for (int i = 0; i < 8; ++i) z[i] = __builtin_amdgcn_fmed3f(z[i], -grid_max(F), grid_max(F));
+            }
         }
         packed = pack8_uniform<F>(z);
     }
@@ -314,9 +325,14 @@ __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, 
         ef[2 * j] = d0 * d0;
         ef[2 * j + 1] = d1 * d1;
     }
+    // |zi| <= 7 x 16/15 < 7.5 under a normal E4M3 block scale (see encode8):
+    // only waves holding a subnormal one clamp
+    if (__builtin_amdgcn_ballot_w64(bs.sub) != 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zi[i] = __builtin_amdgcn_fmed3f(zi[i], -7.0f, 7.0f);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        zi[i] = __builtin_amdgcn_fmed3f(zi[i], -7.0f, 7.0f);
         const float d = (__builtin_rintf(zi[i]) * bs.s) * C67 - v[i];
         ei[i] = d * d;
     }

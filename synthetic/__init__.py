@@ -41,7 +41,7 @@ CHUNK = 1 << 20
 # tensor ids keep the streams of different tensors independent
 TID = {"quantize_x": 1, "activations_t3": 2, "llama_x": 3, "llama_w": 4, "llama_dy": 5,
        "mx_if4": 6, "gemm_a": 7, "gemm_b": 8, "uniform": 9, "edge": 10, "kv_q": 11, "kv_k": 12,
-       "kv_v": 13, "kv_lens": 14}
+       "kv_v": 13, "kv_lens": 14, "small_blocks": 15}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -205,6 +205,17 @@ def edge_cases(rows=64, cols=256, seed=0):
     x[4, 16:32] = f32_to_bf16_bits(np.float32(np.r_[1e-38, rng.standard_normal(15) * 1e-3]))
     x[5, :32] = f32_to_bf16_bits(np.float32(np.r_[1000.0, np.full(31, 1e-3)]))
     return x
+
+
+def small_blocks(rows=256, cols=512, seed=0):
+    """N(0,1) values scaled per 16-element block by 10^u, u uniform in
+    [-6.5, -3.5], with x[0][0] = 1 the tensor's largest magnitude: under a
+    two-level E4M3 scale most block scales land in E4M3's subnormal range."""
+    rng = np.random.default_rng([seed, TID["small_blocks"]])
+    x = rng.standard_normal((rows, cols))
+    x = x * np.repeat(10.0 ** rng.uniform(-6.5, -3.5, (rows, cols // 16)), 16, axis=1)
+    x[0, 0] = 1.0
+    return f32_to_bf16_bits(x.astype(np.float32))
 
 
 def digest(h: np.ndarray) -> str:

@@ -96,6 +96,22 @@ def test_corner_case_inputs(d):
     check_quant(x, d)
 
 
+@pytest.mark.parametrize("fmt", ["e1m2", "int4", "e2m1", "if4"])
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("rht", ["none", "random"])
+def test_subnormal_block_scales(fmt, axis, rht):
+    """Blocks far below the tensor's largest magnitude take E4M3 block scales
+    in the subnormal range, where |y| / s can pass the grid's upper rounding
+    boundary: the kernels clamp only in waves holding such a block."""
+    x = S.small_blocks(256, 512, seed=2)
+    if axis == "col":
+        x = np.ascontiguousarray(x.T)
+    d = dict(format=fmt, scale="e4m3", block=16, rht=rht, rounding="rtne", axis=axis)
+    _, _, _, _, _, _, want = check_quant(x, d)
+    b = want.scales & 0x7F
+    assert np.any((b > 0) & (b < 8))  # the case is reached
+
+
 @pytest.mark.parametrize("axis", ["row", "col"])
 @pytest.mark.parametrize("rht", ["none", "random", "det"])
 def test_amax_and_transform(axis, rht):

@@ -289,3 +289,30 @@ def test_attenuation_is_product_of_operand_alphas():
     al_b = O.finalize(O.stats(b, cfg))["alpha"]
     assert abs(eta - al_a * al_b) < 0.01
     assert eta < 1.0
+
+
+@pytest.mark.parametrize("fmt,gmax,step", [("e1m2", 3.5, 0.5), ("int4", 7.0, 1.0)])
+@pytest.mark.parametrize("kind", ["small_blocks", "t3"])
+def test_e4m3_block_scale_bound(fmt, gmax, step, kind):
+    """Under a normal E4M3 block scale (exponent field nonzero) |y| / s stays
+    within gridmax x 16/15, below the rounding boundary gridmax + step / 2 of
+    the uniform grids: the E4M3 rounding of Delta is within 1/16 of it.  Under
+    a subnormal one it can pass that boundary, and the code saturates at 7
+    (the inputs with small blocks reach that case)."""
+    x = S.small_blocks(256, 512, seed=2) if kind == "small_blocks" else S.activations_t3(256, 512, seed=2)
+    cfg = O.Cfg(fmt, "e4m3")
+    q = O.quantize(x, cfg)
+    y = np.abs(S.bf16_bits_to_f32(x)).reshape(256, 32, 16)
+    dec = np.array([O.lib().orc_e4m3_decode(int(b)) for b in range(128)], np.float32)
+    s = (np.float32(q.alpha) * dec[q.scales & 0x7F]).astype(np.float32)
+    normal = (q.scales & 0x78) != 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        zmax = np.where(s > 0, (y / s[..., None]).max(axis=2), 0.0)
+    assert zmax[normal].max() <= gmax * 16 / 15
+    assert zmax[normal].max() < gmax + step / 2
+    sub = ((q.scales & 0x78) == 0) & (q.scales != 0)
+    if kind == "small_blocks":
+        over = sub & (zmax > gmax + step / 2)
+        assert over.any()
+        k = np.stack([q.codes & 7, (q.codes >> 4) & 7], axis=-1).reshape(256, 32, 16)
+        assert np.all(k[over].max(axis=1) == 7)

@@ -279,14 +279,6 @@ __device__ __forceinline__ void decode8_uniform(uint32_t w, float *g)
     g[7] = o1.y;
 }
 
-// 1 / x for normal x and normal 1 / x: the hardware reciprocal and one
-// Newton step (about half a unit in the last place).
-__device__ __forceinline__ float rcp_refined(float x)
-{
-    const float r = __builtin_amdgcn_rcpf(x);
-    return __builtin_fmaf(r, __builtin_fmaf(-x, r, 1.0f), r);
-}
-
 // Grid value g[q] of bin q (IF4: bins 8..15 are the INT4 blocks' codes).
 template <int F>
 __device__ __forceinline__ double bin_grid(int q)
@@ -395,7 +387,7 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
                 P = __builtin_amdgcn_ldexpf(1.0f, -pe);
             }
             const float skp = SCALED ? sk * P : sk;  // exact
-            const float zinv = s == 0.0f ? 0.0f : pre * rcp_refined(skp);
+            const float zinv = s == 0.0f ? 0.0f : pre * rcp_rn(skp);
             float p1 = 0.f, p2 = 0.f, p3 = 0.f, p4 = 0.f, p5 = 0.f, p6 = 0.f;
 #pragma unroll
             for (int i = 0; i < B; ++i) {

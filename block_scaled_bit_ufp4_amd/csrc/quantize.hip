@@ -47,8 +47,10 @@ __device__ __forceinline__ void nt_store16(void *p, uint32_t x, uint32_t y, uint
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 constexpr int CT = 256;  // column kernel: threads per workgroup
-constexpr int CTR = 2 * CT; // column kernel: source rows per workgroup (128 per wave)
 constexpr int CTC = 64;  // column kernel: source columns per workgroup
+constexpr int CCG = CTC / 8;          // column kernel: 8-column groups, one per lane of a wave row
+constexpr int CRB = 64 / CCG;         // column kernel: 16-row blocks per wave
+constexpr int CTR = CT / 64 * CRB * 16; // column kernel: source rows per workgroup
 constexpr int COL_GROUP = 8;  // column kernel: row tiles dispatched together
 
 enum : int { MODE_QUANT = 0, MODE_AMAX = 1, MODE_RHT = 2 };
@@ -80,7 +82,7 @@ __device__ __forceinline__ TensorConst tensor_const(const float *amax)
 struct BlockScale {
     float s;        // effective scale (x_hat = value * s)
     float sd;       // divisor applied to the kernel's values (4 s when x 1/4 is folded)
-    float invd;     // RN(1 / sd)
+    float invd;     // RN(1 / sd) where fast (0 otherwise)
     uint32_t byte;  // stored byte (E4M3 / E8M0)
     bool fast;      // Markstein division valid (or s == 0)
     bool sub;       // E4M3 byte in the subnormal range (exponent field 0, nonzero)
@@ -117,10 +119,11 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
             b.s = t.alpha * e4m3_decode_hw(b.byte);
         }
         b.sub = S == SC_E4M3 && (b.byte & 0x78u) == 0 && b.byte != 0;
-        const float inv = b.s == 0.0f ? 0.0f : 1.0f / b.s;
         b.sd = FOLD ? b.s * 4.0f : b.s;
-        b.invd = FOLD ? inv * 0.25f : inv;
         b.fast = b.s == 0.0f || (b.sd >= 0x1p-75f && b.sd <= 0x1p125f);
+        // the reciprocal serves the fast quotients only (s and 1 / s normal there)
+        const float inv = b.s != 0.0f && b.fast ? rcp_rn(b.s) : 0.0f;
+        b.invd = FOLD ? inv * 0.25f : inv;
         return b;
     }
 }
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
     constexpr bool FOLD = MODE == MODE_QUANT && RHT && IN == IN_BF16 && F != FMT_IF4;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane & 7, b = lane >> 3;
+    const int g = lane % CCG, b = lane / CCG;
     // Tile order: groups of COL_GROUP row tiles, row tile fastest, so the
     // workgroups in flight write COL_GROUP x CTR / 2 contiguous code bytes of
     // each view row while still sharing the source rows they read.
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         ty = grp * COL_GROUP + in % gy;
         tx = in / gy;
     }
-    const int64_t r0 = (int64_t)ty * CTR + wave * 128 + b * 16;  // first source row of this lane
+    const int64_t r0 = (int64_t)ty * CTR + wave * (CRB * 16) + b * 16;  // first source row of this lane
     const int64_t c0 = (int64_t)tx * CTC + g * 8;                // first source column
     const bool active = r0 < a.R && c0 < a.C;
 
@@ -619,7 +622,13 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
             }
         } else {
             float m = absmax16(v);
-            if constexpr (S == SC_E8M0) m = fmaxf(m, xor8(m));  // partner lane holds the other 16 rows
+            if constexpr (S == SC_E8M0) {
+                // the partner lane (the next 16-row block) holds the other 16 rows
+                if constexpr (CCG == 8)
+                    m = fmaxf(m, xor8(m));
+                else
+                    m = fmaxf(m, __shfl_xor(m, CCG));
+            }
             if (!active) continue;
             if constexpr (FOLD) m = m * 0.25f;
             const BlockScale bs = block_scale<F == FMT_IF4 ? FMT_E2M1 : F, S, FOLD>(m, tc);
@@ -641,7 +650,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
                 hi = encode8<F, S, FOLD, SR>(v + 8, bs, w + 8);
             }
             if (staged) {
-                const int cl = g * 8 + j, rb = wave * 8 + b;  // tile-local view row, 16-row block
+                const int cl = g * 8 + j, rb = wave * CRB + b;  // tile-local view row, 16-row block
                 st_codes[cl * CP + rb] = make_uint2(lo, hi);
                 if constexpr (S == SC_E8M0) {
                     if ((b & 1) == 0) st_sbyte[cl * NB + (rb >> 1)] = (uint8_t)sbyte;

@@ -229,44 +229,20 @@ __device__ __forceinline__ uint32_t rtne_code(float a)
     }
 }
 
-// Stochastic rounding of a >= 0 on format F with one Philox word w:
-// k = k_lo + (u < frac), u = (w >> 8) 2^-24.  frac is exact (the cell widths
-// are powers of two), and u < frac is evaluated as (w >> 8) < frac 2^24 in
-// binary32, where both sides are exact.
-template <int F>
-__device__ __forceinline__ uint32_t sr_code(float a, uint32_t w)
+// Stochastic rounding of a >= 0 on E2M1 with one Philox word w: the element
+// rounds up from its cell's lower point when (w >> 12) + F reaches 2^20, F =
+// floor(frac 2^20) the position inside the cell cut to 20 bits.  With T =
+// k_lo 2^20 + F that is k = (T + (w >> 12)) >> 20, and T comes from the bits
+// of a: below 1 (cell width 1/2) T = floor(a 2^21), exact in the convert;
+// in [1, 6) the exponent and the top mantissa bit give k_lo + 252 and the 22
+// mantissa bits below it the position, so T + 252 2^20 = bits(a) >> 2.  The
+// uniform grids round through the FP8 convert instead (pack8_uniform_sr).
+__device__ __forceinline__ uint32_t sr_code_e2m1(float a, uint32_t w)
 {
-    if constexpr (F == FMT_E1M2 || F == FMT_INT4) {
-        // Uniform grids, in integers.  With t = a in grid units (a x 2 for
-        // E1M2, exact) and T = ceil(t 2^24) (exact: t 2^24 < 2^27 is a
-        // binary32 value and its ceiling an integer below 2^32),
-        // T = k_lo 2^24 + ceil(frac 2^24), so
-        //   (T + 2^24 - 1 - (w >> 8)) >> 24 = k_lo + ((w >> 8) < ceil(frac 2^24))
-        //                                  = k_lo + (u < frac),
-        // since for an integer W, W < x holds exactly when W < ceil(x).
-        // Clamping a to the grid maximum gives code 7.
-        constexpr float G = grid_max(F);
-        constexpr float SC = F == FMT_E1M2 ? 0x1p25f : 0x1p24f;
-        const uint32_t T = (uint32_t)__builtin_ceilf(fminf(a, G) * SC);
-        return (T + 0xFFFFFFu - (w >> 8)) >> 24;
-    } else {
-        const float fu = (float)(w >> 8);
-        if (a >= 6.0f) return 7u;
-        if (a < 1.0f) {
-            const float t = a * 2.0f;
-            const float kl = __builtin_floorf(t);
-            const float frac = t - kl;
-            return (uint32_t)kl + (fu < frac * 0x1p24f ? 1u : 0u);
-        }
-        // a in [1, 6): truncate to one mantissa bit for the lower grid point
-        const uint32_t b = f2u(a);
-        const uint32_t glo_bits = b & 0xFFC00000u;
-        const uint32_t klo = (b >> 22) - 252u;
-        // cell width = 2^(e-1) with e = unbiased exponent of a; frac = (a - g) / width
-        const float inv_w = u2f((255u - (b >> 23)) << 23);  // 2^(128 - biased exponent)
-        const float frac = (a - u2f(glo_bits)) * inv_w;
-        return klo + (fu < frac * 0x1p24f ? 1u : 0u);
-    }
+    const uint32_t W = w >> 12;
+    if (a >= 6.0f) return 7u;
+    if (a < 1.0f) return ((uint32_t)(a * 0x1p21f) + W) >> 20;
+    return ((f2u(a) >> 2) + W - (252u << 20)) >> 20;
 }
 
 // ---------------------------------------------------------------------------
@@ -316,6 +292,35 @@ __device__ __forceinline__ uint32_t pack8_uniform(const float *z)
     const uint32_t d0 = __builtin_bit_cast(uint32_t, w0), d1 = __builtin_bit_cast(uint32_t, w1);
     const uint32_t n0 = ((d0 >> 4) & 0x08080808u) | (d0 & 0x07070707u);
     const uint32_t n1 = ((d1 >> 4) & 0x08080808u) | (d1 & 0x07070707u);
+    const uint32_t t0 = n0 | (n0 >> 4), t1 = n1 | (n1 >> 4);
+    return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
+}
+
+// Stochastic rounding of 8 signed scaled values onto a uniform grid, one
+// Philox word each, through the FP8 convert with stochastic rounding: z is
+// clamped to the grid maximum (so 2|z|, or |z| for INT4, stays within the
+// subnormal codes 0..7) and the convert returns sign << 7 | k with k = k_lo + 1
+// exactly when (w >> 12) + floor(frac 2^20) reaches 2^20, frac = t - k_lo
+// (checked on gfx950 against that rule on 2^30 pairs per grid: z of every
+// binary32 exponent and sign, w random or at the rounding threshold and one
+// below).  The bytes fold into nibbles as in pack8_uniform.
+template <int F>
+__device__ __forceinline__ uint32_t pack8_uniform_sr(const float *z, const uint32_t *w)
+{
+    constexpr float SC = F == FMT_E1M2 ? 256.0f : 512.0f;
+    constexpr float G = grid_max(F);
+    int d0 = 0, d1 = 0;
+    d0 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d0, __builtin_amdgcn_fmed3f(z[0], -G, G), w[0], SC, 0);
+    d0 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d0, __builtin_amdgcn_fmed3f(z[1], -G, G), w[1], SC, 1);
+    d0 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d0, __builtin_amdgcn_fmed3f(z[2], -G, G), w[2], SC, 2);
+    d0 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d0, __builtin_amdgcn_fmed3f(z[3], -G, G), w[3], SC, 3);
+    d1 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d1, __builtin_amdgcn_fmed3f(z[4], -G, G), w[4], SC, 0);
+    d1 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d1, __builtin_amdgcn_fmed3f(z[5], -G, G), w[5], SC, 1);
+    d1 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d1, __builtin_amdgcn_fmed3f(z[6], -G, G), w[6], SC, 2);
+    d1 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d1, __builtin_amdgcn_fmed3f(z[7], -G, G), w[7], SC, 3);
+    const uint32_t u0 = (uint32_t)d0, u1 = (uint32_t)d1;
+    const uint32_t n0 = ((u0 >> 4) & 0x08080808u) | (u0 & 0x07070707u);
+    const uint32_t n1 = ((u1 >> 4) & 0x08080808u) | (u1 & 0x07070707u);
     const uint32_t t0 = n0 | (n0 >> 4), t1 = n1 | (n1 >> 4);
     return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
 }

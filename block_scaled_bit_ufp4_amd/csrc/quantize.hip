@@ -129,8 +129,9 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
 }
 
 // Signed scaled values z_i = RN(y_i / s) for 8 kernel values v_i (v = 4y when
-// FOLD).  SR: quotients below 2^-100 are redone by division (their only
-// influence is whether they are zero).
+// FOLD).  The fast quotient can be off only for |v| < 2^-100, where |z| <
+// 2^-25: RTNE gives code 0 there, and so does SR, which rounds up only from
+// 2^-20 of a step above the lower point.
 template <int S, bool FOLD, bool SR>
 __device__ __forceinline__ void scaled8(const float *v, const BlockScale &b, float *z)
 {
@@ -146,19 +147,6 @@ __device__ __forceinline__ void scaled8(const float *v, const BlockScale &b, flo
 #pragma unroll
             for (int i = 0; i < 8; ++i) z[i] = (FOLD ? v[i] * 0.25f : v[i]) / b.s;
         }
-        if constexpr (SR) {
-            // rare: a branch the whole wave takes or skips, so the common
-            // case pays no division
-            bool tiny = false;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) tiny |= fabsf(z[i]) < 0x1p-100f && v[i] != 0.0f && b.s != 0.0f;
-            if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (fabsf(z[i]) < 0x1p-100f && v[i] != 0.0f && b.s != 0.0f)
-                        z[i] = (FOLD ? v[i] * 0.25f : v[i]) / b.s;
-            }
-        }
     }
 }
 
@@ -169,11 +157,13 @@ __device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b,
     float z[8];
     scaled8<S, FOLD, SR>(v, b, z);
     uint32_t packed;
-    if constexpr (SR) {
+    if constexpr (SR && F == FMT_E2M1) {
         packed = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            packed |= ((f2u(z[i]) >> 28 & 8u) | sr_code<F>(fabsf(z[i]), w[i])) << (4 * i);
+            packed |= ((f2u(z[i]) >> 28 & 8u) | sr_code_e2m1(fabsf(z[i]), w[i])) << (4 * i);
+    } else if constexpr (SR) {
+        packed = pack8_uniform_sr<F>(z, w);
     } else if constexpr (F == FMT_E2M1) {
         packed = pack8_e2m1(z);
     } else if constexpr (e2m1_codes(F)) {

@@ -76,9 +76,10 @@
  *          (m = 0 gives E = -127).
  *   z    = y / s (correctly rounded); s = 0 gives code 0.
  *   RTNE: nearest grid point, ties to the even code, saturating at gridmax.
- *   SR:   k = k_lo + (u < frac) with u = (w >> 8) 2^-24, w = Philox4x32-10 word
- *          n mod 4 at key = sr_seed, counter = (lo32(n/4), hi32(n/4), sr_stream, 0),
- *          n = v L + l the element's index in the view.
+ *   SR:   k = k_lo + 1 when (w >> 12) + floor(frac 2^20) >= 2^20, else k_lo
+ *          (frac = position of |z| in its cell; 20 random bits), w = Philox4x32-10
+ *          word n mod 4 at key = sr_seed, counter = (lo32(n/4), hi32(n/4),
+ *          sr_stream, 0), n = v L + l the element's index in the view.
  *   IF4:  FP4 candidate = RTNE of y/s on E2M1; INT4 candidate k = rint((y x 7/6)/s)
  *          clamped to 7, dequantized as (k x s) x 6/7; the candidate with the
  *          smaller binary32 squared error (pairwise sum) wins, ties to FP4.

@@ -140,9 +140,15 @@ int orc_round_rtne(float z, int fmt)
 
 /* Stochastic rounding: [IF4] 6.1 gives floor(x) + (random() < frac); [UFP4-TW]
  * 五 applies it to dY only.  On a non-uniform grid "floor" is the grid point
- * just below |z| and frac the position inside that cell.  The uniform u is the
- * top 24 bits of one Philox word: u = (w >> 8) * 2^-24, so u < frac is decided
- * exactly.  |z| at or above the grid maximum gives the maximum. */
+ * just below |z| and frac the position inside that cell.  The pages fix no
+ * resolution; here both sides of the comparison have 20 bits: frac is cut to
+ * F = floor(frac 2^20) and random() is U 2^-20 with U = 2^20 - 1 - (w >> 12),
+ * the complement of the top 20 bits of one Philox word w.  The element rounds
+ * up when U < F, i.e. when (w >> 12) + F reaches 2^20; so P(up) = F 2^-20,
+ * within 2^-20 below frac, and an |z| less than 2^-20 of a cell above its
+ * lower point always rounds down.  |z| at or above the grid maximum gives the
+ * maximum.  (F is exact: frac is a short binary fraction, the cell widths
+ * being powers of two.) */
 int orc_round_sr(float z, int fmt, uint32_t w)
 {
     const double *g = grid_of(fmt);
@@ -156,8 +162,9 @@ int orc_round_sr(float z, int fmt, uint32_t w)
         for (int j = 1; j <= km; ++j)
             if (g[j] <= a) lo = j;
         double frac = (a - g[lo]) / (g[lo + 1] - g[lo]);
-        double u = (double)(w >> 8) * 0x1p-24;
-        k = lo + (u < frac ? 1 : 0);
+        uint32_t F = (uint32_t)floor(frac * 0x1p20);
+        uint32_t U = 0xFFFFFu - (w >> 12);
+        k = lo + (U < F ? 1 : 0);
     }
     return (signbit(z) ? 8 : 0) | k;
 }

@@ -211,3 +211,34 @@ def test_sr_is_unbiased(fmt):
     assert O.round_sr(g[7] * 3, fmt, 0) == 7
     assert O.round_sr(-1e-3, fmt, 0) & 8
     _ = rng
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e1m2", "int4"])
+def test_sr_resolution_and_direction(fmt):
+    """The SR decision at 20-bit resolution (the reading of IF4 page 6.1's
+    random() < frac): over the 2^20 words w = j 2^12 + r, r any low 12 bits,
+    exactly floor(frac 2^20) round up, and they are the largest j.  frac and
+    its 20-bit floor are computed here exactly with fractions."""
+    from fractions import Fraction
+    g = O.grid(fmt)
+    rng = np.random.default_rng(3)
+    j = np.arange(1 << 20, dtype=np.uint64)
+    for a in [0.1, 0.3, 0.8, 1.2, 1.7, 2.3, 2.9, 3.3, 4.4, 5.5, 6.9, 0.75]:
+        a = np.float32(min(a, float(g[7]) * 0.999))
+        k_lo = int(np.nonzero(g <= a)[0].max())
+        frac = (Fraction(float(a)) - Fraction(float(g[k_lo]))) / (Fraction(float(g[k_lo + 1])) - Fraction(float(g[k_lo])))
+        F = int(frac * 2**20)  # floor (frac >= 0)
+        r = rng.integers(0, 4096, size=j.size).astype(np.uint64)
+        w = ((j << np.uint64(12)) | r).astype(np.uint32)
+        codes = O.round_sr_array(np.full(j.size, a, np.float32), w, fmt) & 7
+        assert set(np.unique(codes)) <= {k_lo, k_lo + 1}
+        up = codes == k_lo + 1
+        assert int(up.sum()) == F, (fmt, float(a), int(up.sum()), F)
+        assert np.array_equal(up, j >= (1 << 20) - F)
+    # less than 2^-20 of a step above a grid point: never up, even for the largest word
+    step = float(g[1] - g[0])
+    for a in [step * 2.0**-21, step * 2.0**-30, float(g[2]) + float(g[3] - g[2]) * 2.0**-21]:
+        z = np.full(4, a, np.float32)
+        lo = int(np.nonzero(g <= np.float32(a))[0].max())
+        w = np.array([0xFFFFFFFF, 0xFFFFF000, 0x80000000, 0], np.uint32)
+        assert np.all(O.round_sr_array(z, w, fmt) == lo)

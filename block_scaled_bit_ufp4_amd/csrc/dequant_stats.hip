@@ -172,38 +172,31 @@ __device__ __forceinline__ void block_reduce_store(double (&acc)[NV], double *ou
     }
 }
 
-// One workgroup of 1024 threads adds nwg rows of NV partial sums.  Thread t
-// (t < G NV, G = 1024 / NV groups) takes sum k = t mod NV over rows g,
-// g + G, g + 2G, ... (g = t / NV) into eight accumulators used in turn, so
-// eight loads are in flight and each load instruction of the workgroup reads
-// consecutive doubles; the G group sums of each k are then added in group
-// order.  The order is fixed, so the result is the same on every run.
-constexpr int RED_T = 1024;
+// One workgroup per sum k (grid NV) adds column k of nwg rows of NV partial
+// sums: thread t loads rows t, t + RED_T, ... (all its loads issued at once,
+// nwg <= RED_T RED_ROWS), adds them in row order, and the workgroup adds its
+// threads in a fixed tree (lane butterfly, then the waves in order).  The
+// order is fixed, so the result is the same on every run; with one round of
+// loads per thread the reduction is one memory latency long.
+constexpr int RED_T = 256;
+constexpr int RED_ROWS = 8;
+static_assert(STATS_WGS <= RED_T * RED_ROWS && ETA_WGS <= RED_T * RED_ROWS, "one round of loads");
 template <int NV>
 __global__ __launch_bounds__(RED_T) void reduce_partials_kernel(const double *partials, int nwg, double *sums)
 {
-    constexpr int G = RED_T / NV;
-    __shared__ double part[G][NV];
-    const int t = threadIdx.x;
-    if (t < G * NV) {
-        const int k = t % NV, g = t / NV;
-        double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-        int i = g;
-        for (; i + 7 * G < nwg; i += 8 * G) {
+    const int k = blockIdx.x, t = threadIdx.x;
+    double v[RED_ROWS];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] += partials[(int64_t)(i + u * G) * NV + k];
-        }
-#pragma unroll
-        for (int u = 0; u < 7; ++u)
-            if (i + u * G < nwg) acc[u] += partials[(int64_t)(i + u * G) * NV + k];
-        part[g][k] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    for (int u = 0; u < RED_ROWS; ++u) {
+        const int row = t + u * RED_T;
+        v[u] = row < nwg ? partials[(int64_t)row * NV + k] : 0.0;
     }
+    double acc = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    __shared__ double red[RED_T / 64];
+    if ((t & 63) == 0) red[t >> 6] = acc;
     __syncthreads();
-    if (t < NV) {
-        double v = 0.0;
-        for (int g = 0; g < G; ++g) v += part[g][t];
-        sums[t] = v;
-    }
+    if (t == 0) sums[k] = ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 // ---------------------------------------------------------------------------
@@ -636,7 +629,7 @@ static hipError_t stats_run(K kernel, int B, StatsArgs a, hipStream_t st)
         if (e != hipSuccess) return e;
         t0 = a.t1;
     } while (t0 < nblocks);
-    launch_kernel(reduce_partials_kernel<NS>, dim3(1), dim3(RED_T), st, a.partials, g, a.sums);
+    launch_kernel(reduce_partials_kernel<NS>, dim3(NS), dim3(RED_T), st, a.partials, g, a.sums);
     return hipGetLastError();
 }
 
@@ -700,7 +693,7 @@ hipError_t launch_eta(const float *zq, const float *z, int64_t M, int64_t N, int
     launch_kernel(eta_kernel, dim3(ETA_WGS), dim3(256), st, zq, z, M, N, ld, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    launch_kernel(reduce_partials_kernel<3>, dim3(1), dim3(RED_T), st, partials, ETA_WGS, sums);
+    launch_kernel(reduce_partials_kernel<3>, dim3(3), dim3(RED_T), st, partials, ETA_WGS, sums);
     return hipGetLastError();
 }
 

@@ -560,10 +560,13 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
         float v[16];
         if (active) {
             if constexpr (IN == IN_BF16) {
+                // widen with the sign diagonal applied in the same instruction
+                // (the shifted-out half is zero, so adding the sign bit flips it)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const uint32_t w = (j >> 1) == 0 ? raw[i].x : (j >> 1) == 1 ? raw[i].y : (j >> 1) == 2 ? raw[i].z : raw[i].w;
-                    v[i] = (j & 1) ? bf16hi(w) : bf16lo(w);
+                    const uint32_t sg = RHT ? ((a.smask >> i) & 1u) << 31 : 0u;
+                    v[i] = (j & 1) ? u2f((w & 0xFFFF0000u) ^ sg) : u2f((w << 16) + sg);
                 }
             } else {
                 const float *xp = static_cast<const float *>(a.x) + r0 * a.ldx + c0 + j;
@@ -575,8 +578,10 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
             for (int i = 0; i < 16; ++i) v[i] = 0.0f;
         }
         if (active && RHT) {
+            if constexpr (IN != IN_BF16) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = u2f(f2u(v[i]) ^ (((a.smask >> i) & 1u) << 31));
+                for (int i = 0; i < 16; ++i) v[i] = u2f(f2u(v[i]) ^ (((a.smask >> i) & 1u) << 31));
+            }
             fwht8(v);
             fwht8(v + 8);
 #pragma unroll

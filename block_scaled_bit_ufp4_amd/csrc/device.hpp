@@ -229,22 +229,6 @@ __device__ __forceinline__ uint32_t rtne_code(float a)
     }
 }
 
-// Stochastic rounding of a >= 0 on E2M1 with one Philox word w: the element
-// rounds up from its cell's lower point when (w >> 12) + F reaches 2^20, F =
-// floor(frac 2^20) the position inside the cell cut to 20 bits.  With T =
-// k_lo 2^20 + F that is k = (T + (w >> 12)) >> 20, and T comes from the bits
-// of a: below 1 (cell width 1/2) T = floor(a 2^21), exact in the convert;
-// in [1, 6) the exponent and the top mantissa bit give k_lo + 252 and the 22
-// mantissa bits below it the position, so T + 252 2^20 = bits(a) >> 2.  The
-// uniform grids round through the FP8 convert instead (pack8_uniform_sr).
-__device__ __forceinline__ uint32_t sr_code_e2m1(float a, uint32_t w)
-{
-    const uint32_t W = w >> 12;
-    if (a >= 6.0f) return 7u;
-    if (a < 1.0f) return ((uint32_t)(a * 0x1p21f) + W) >> 20;
-    return ((f2u(a) >> 2) + W - (252u << 20)) >> 20;
-}
-
 // ---------------------------------------------------------------------------
 // Hardware converts (verified on gfx950 against the software definitions for
 // every finite binary32: the FP4 convert equals the nearest-even E2M1 code
@@ -323,6 +307,38 @@ __device__ __forceinline__ uint32_t pack8_uniform_sr(const float *z, const uint3
     const uint32_t n1 = ((u1 >> 4) & 0x08080808u) | (u1 & 0x07070707u);
     const uint32_t t0 = n0 | (n0 >> 4), t1 = n1 | (n1 >> 4);
     return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
+}
+
+// Stochastic rounding of 8 signed scaled values onto E2M1, one Philox word
+// each, through the packed FP4 convert with stochastic rounding.  That convert
+// rounds its first value up when (seed >> 10) + floor(frac 2^22) reaches 2^22
+// (and feeds the second a rotated copy of the seed).  With the seed's low 12
+// bits cleared, seed >> 10 = 4 (w >> 12), and 4 (w >> 12) + floor(frac 2^22) >=
+// 2^22 holds exactly when (w >> 12) + floor(frac 2^20) >= 2^20: the 20-bit rule
+// of the uniform grids (checked on gfx950 on 2^30 pairs, |z| up to 32 for the
+// saturation at 6).  One value per convert, the second 0 (code 0), into byte 0:
+// this builtin does not keep the other bytes of its first operand (they come
+// back as whatever the destination register held), so only byte 0 of each
+// result is used and v_perm gathers them, the even elements' codes into the
+// low nibbles of one word and the odd ones' into another, shifted up.
+__device__ __forceinline__ uint32_t sr_fp4_byte0(float z, uint32_t w)
+{
+    const v2f p = {z, 0.0f};
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, w & 0xFFFFF000u, 1.0f, 0);
+}
+__device__ __forceinline__ uint32_t gather_byte0(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3)
+{
+    // bytes [r0.b0, r1.b0, 0, 0] | [0, 0, r2.b0, r3.b0]
+    return __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u) | __builtin_amdgcn_perm(r3, r2, 0x04000c0cu);
+}
+__device__ __forceinline__ uint32_t pack8_e2m1_sr(const float *z, const uint32_t *w)
+{
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = sr_fp4_byte0(z[i], w[i]);
+    const uint32_t e = gather_byte0(r[0], r[2], r[4], r[6]);
+    const uint32_t o = gather_byte0(r[1], r[3], r[5], r[7]);
+    return e | (o << 4);
 }
 
 // Grid value of a magnitude code.

@@ -158,10 +158,7 @@ __device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b,
     scaled8<S, FOLD, SR>(v, b, z);
     uint32_t packed;
     if constexpr (SR && F == FMT_E2M1) {
-        packed = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            packed |= ((f2u(z[i]) >> 28 & 8u) | sr_code_e2m1(fabsf(z[i]), w[i])) << (4 * i);
+        packed = pack8_e2m1_sr(z, w);
     } else if constexpr (SR) {
         packed = pack8_uniform_sr<F>(z, w);
     } else if constexpr (F == FMT_E2M1) {

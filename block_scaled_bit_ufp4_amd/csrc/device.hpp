@@ -119,9 +119,8 @@ __device__ __forceinline__ void fwht16_local(float *v)
 // z = fma(r, inv, q)  with inv = RN(1/s): Markstein's correction step, exact
 // when the residual r does not underflow.  Conditions used here: s in
 // [2^-75, 2^125] and a >= 2^-100 (r is then a normal number); for a < 2^-100
-// the quotient is below 2^-25, where only z == 0 vs z > 0 can matter (RTNE
-// gives code 0 either way); callers that care (stochastic rounding) re-divide
-// when the fast quotient is 0 for a > 0.
+// the quotient is below 2^-25, where every rounding gives code 0 (RTNE, and
+// stochastic rounding, which rounds up only from 2^-20 of a step).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool fast_div_ok(float s) { return s >= 0x1p-75f && s <= 0x1p125f; }
 

@@ -281,49 +281,46 @@ __device__ __forceinline__ float absmax16(const float *v)
 
 // Quantize one transformed 16-element chunk held by this lane; returns the
 // codes (low word: elements 0..7) and sets the scale byte / value.
-// IF4 for one 16-element block: both candidates on signed values (each
-// error is odd in y, so its square equals the one of the |y| form): FP4
-// codes from the FP4 convert and their values from the FP4 decode; INT4 from
-// a clamp, RTNE to an integer and the FP8-convert packing.  Squared errors
-// summed pairwise, spans 1, 2, 4, 8; INT4 iff strictly smaller.  Sets the
-// flag in bit 7 of sbyte.
+// IF4 for one 16-element block, on signed values: z = RN(y / s) once; the
+// E2M1 candidate's codes from the FP4 convert of z and its grid values from
+// the FP4 decode; the INT4 candidate's levels from t = RN(z 7/6), rounded and
+// packed by the FP8 convert.  Both errors in units of the scale: g - z and
+// RN(k 6/7) - z (each error is odd in y, so its square equals the |y| form).
+// Squared errors summed pairwise, spans 1, 2, 4, 8; INT4 iff strictly smaller.
+// Sets the flag in bit 7 of sbyte.
 __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, uint32_t &lo, uint32_t &hi,
                                           uint32_t &sbyte)
 {
     constexpr float C76 = 7.0f / 6.0f;
     constexpr float C67 = 6.0f / 7.0f;
-    float zf[16], zi[16];
+    float z[16], t[16];
     if (bs.fast) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            zf[i] = sdiv_fast(v[i], bs.s, bs.invd);
-            zi[i] = sdiv_fast(v[i] * C76, bs.s, bs.invd);
-        }
+        for (int i = 0; i < 16; ++i) z[i] = sdiv_fast(v[i], bs.s, bs.invd);
     } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            zf[i] = v[i] / bs.s;
-            zi[i] = (v[i] * C76) / bs.s;
-        }
+        for (int i = 0; i < 16; ++i) z[i] = v[i] / bs.s;
     }
-    const uint32_t lof = pack8_e2m1(zf), hif = pack8_e2m1(zf + 8);
+    const uint32_t lof = pack8_e2m1(z), hif = pack8_e2m1(z + 8);
     float ef[16], ei[16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const v2f g = decode2_e2m1(j < 4 ? lof : hif, j & 3);
-        const float d0 = g.x * bs.s - v[2 * j], d1 = g.y * bs.s - v[2 * j + 1];
+        const float d0 = g.x - z[2 * j], d1 = g.y - z[2 * j + 1];
         ef[2 * j] = d0 * d0;
         ef[2 * j + 1] = d1 * d1;
     }
-    // |zi| <= 7 x 16/15 < 7.5 under a normal E4M3 block scale (see encode8):
-    // only waves holding a subnormal one clamp
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = z[i] * C76;
+    // |t| <= 6 x 16/15 x 7/6 < 7.5 under a normal E4M3 block scale (see
+    // encode8): only waves holding a subnormal one clamp
     if (__builtin_amdgcn_ballot_w64(bs.sub) != 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) zi[i] = __builtin_amdgcn_fmed3f(zi[i], -7.0f, 7.0f);
+        for (int i = 0; i < 16; ++i) t[i] = __builtin_amdgcn_fmed3f(t[i], -7.0f, 7.0f);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float d = (__builtin_rintf(zi[i]) * bs.s) * C67 - v[i];
+        const float d = __builtin_rintf(t[i]) * C67 - z[i];
         ei[i] = d * d;
     }
 #pragma unroll
@@ -335,8 +332,8 @@ __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, 
         }
     const bool use_int = bs.s != 0.0f && ei[0] < ef[0];
     if (use_int) {
-        lo = pack8_uniform<FMT_INT4>(zi);
-        hi = pack8_uniform<FMT_INT4>(zi + 8);
+        lo = pack8_uniform<FMT_INT4>(t);
+        hi = pack8_uniform<FMT_INT4>(t + 8);
     } else {
         lo = lof;
         hi = hif;

@@ -80,8 +80,9 @@
  *          (frac = position of |z| in its cell; 20 random bits), w = Philox4x32-10
  *          word n mod 4 at key = sr_seed, counter = (lo32(n/4), hi32(n/4),
  *          sr_stream, 0), n = v L + l the element's index in the view.
- *   IF4:  FP4 candidate = RTNE of y/s on E2M1; INT4 candidate k = rint((y x 7/6)/s)
- *          clamped to 7, dequantized as (k x s) x 6/7; the candidate with the
+ *   IF4:  z = y/s; FP4 candidate = RTNE of z on E2M1 (grid value g); INT4
+ *          candidate k = rint(z x 7/6) clamped to 7, dequantized as (k x s) x 6/7;
+ *          errors in units of s, g - z and (k x 6/7) - z; the candidate with the
  *          smaller binary32 squared error (pairwise sum) wins, ties to FP4.
  *   Dequantization: x_hat = v x s (IF4 INT4 blocks: (k x s) x 6/7).
  */

@@ -396,20 +396,21 @@ static float deq_plain(int fmt, int code, float s)
 
 /* IF4's INT4 candidate ([IF4] 3.1.1, 3.2).  The integer grid reaches 7 while
  * E2M1 reaches 6, so with the shared block scale the integer levels are
- * stretched: a value is enlarged by 7/6 before the scale divides it, and a
- * level stands for 6/7 of (level x scale).  Reading in binary32 (each step
- * rounded once): the level is |RN(RN(y * 7/6) / s)| rounded half to even and
+ * stretched: a value in units of the scale is enlarged by 7/6 before it is
+ * rounded to a level, and a level stands for 6/7 of (level x scale).  Reading
+ * in binary32 (each step rounded once): with z = RN(y / s), the quotient the
+ * E2M1 candidate rounds, the level is |RN(z * 7/6)| rounded half to even and
  * capped at 7; its value is RN(RN(level * s) * 6/7), where 7/6 and 6/7 are
  * the binary32 constants nearest them. */
 static const float IF4_STRETCH = 7.0f / 6.0f;
 static const float IF4_SHRINK = 6.0f / 7.0f;
 
-static int if4_int_code(float y, float s)
+static int if4_int_code(float z)
 {
-    float z = (y * IF4_STRETCH) / s;
-    int level = (int)nearbyintf(fabsf(z)); /* default rounding mode: half to even */
+    float t = z * IF4_STRETCH;
+    int level = (int)nearbyintf(fabsf(t)); /* default rounding mode: half to even */
     if (level > 7) level = 7;
-    return (signbit(z) ? 8 : 0) | level;
+    return (signbit(t) ? 8 : 0) | level;
 }
 
 static float if4_int_value(int code, float s)
@@ -477,9 +478,13 @@ static void quantize_block(const orc_config *cfg, const float *y, int B, float a
     /* IF4 ([IF4] 3.1, 3.2): every block gets both an E2M1 and an INT4
      * candidate under the same scale; the one whose reconstruction is closer
      * (smaller sum of squared errors) is kept, and bit 7 of the scale byte
-     * records which (1 = INT4).  Readings: the squared errors are binary32,
-     * summed as a balanced tree over neighbours (pairs, then pairs of pairs:
-     * four levels for 16 values), and an exact tie keeps E2M1. */
+     * records which (1 = INT4).  Readings: the errors are measured in units of
+     * the block scale, against z = RN(y / s): g - z for the E2M1 grid value g,
+     * RN(level * 6/7) - z for the signed INT4 level (in exact arithmetic both
+     * are the reconstruction's error divided by s, so the ranking is the
+     * same); the squared errors are binary32, summed as a balanced tree over
+     * neighbours (pairs, then pairs of pairs: four levels for 16 values), and
+     * an exact tie keeps E2M1. */
     int fp4_code[16], int_code[16];
     float fp4_z[16], int_z[16], fp4_val[16], int_val[16], fp4_sq[16], int_sq[16];
     for (int i = 0; i < B; ++i) {
@@ -489,12 +494,16 @@ static void quantize_block(const orc_config *cfg, const float *y, int B, float a
         } else {
             fp4_z[i] = scaled(y[i], s);
             fp4_code[i] = orc_round_rtne(fp4_z[i], ORC_E2M1);
-            int_code[i] = if4_int_code(y[i], s);
-            int_z[i] = (y[i] * IF4_STRETCH) / s;
+            int_code[i] = if4_int_code(fp4_z[i]);
+            int_z[i] = fp4_z[i] * IF4_STRETCH;
         }
         fp4_val[i] = deq_plain(ORC_E2M1, fp4_code[i], s);
         int_val[i] = if4_int_value(int_code[i], s);
-        float dev_fp4 = fp4_val[i] - y[i], dev_int = int_val[i] - y[i];
+        float g = (float)grid_of(ORC_E2M1)[fp4_code[i] & 7];
+        if (fp4_code[i] & 8) g = -g;
+        float level = (float)(int_code[i] & 7);
+        if (int_code[i] & 8) level = -level;
+        float dev_fp4 = g - fp4_z[i], dev_int = level * IF4_SHRINK - fp4_z[i];
         fp4_sq[i] = dev_fp4 * dev_fp4;
         int_sq[i] = dev_int * dev_int;
     }

@@ -173,7 +173,10 @@ def test_if4_int4_top_code_maps_to_six_scales():
 
 def test_if4_selection_minimises_squared_error():
     """The flag picks the candidate with the smaller squared error; checked in
-    binary64 from the two candidate reconstructions (near-ties excepted)."""
+    binary64 from the two candidate reconstructions (near-ties excepted).  The
+    codes are the E2M1 codes of z = y / s in FP4 blocks and, in INT4 blocks,
+    the levels rint(z 7/6) capped at 7 with the sign of y (IF4 page 3.1.1),
+    computed here in numpy."""
     x, _ = S.mx_if4(256, 512, seed=1)
     cfg = O.Cfg("if4", "e4m3")
     q = O.quantize(x, cfg)
@@ -187,7 +190,7 @@ def test_if4_selection_minimises_squared_error():
     kf = textbook_codes(zf, "e2m1")
     vf = O.grid("e2m1")[kf & 7] * np.where(kf & 8, -1, 1)
     xf = vf * s_eff[..., None]
-    zi = np.where(s_eff[..., None] > 0, (y.astype(np.float32) * np.float32(7 / 6)) / s_eff[..., None], 0)
+    zi = zf * np.float32(7 / 6)
     ki = np.minimum(np.rint(np.abs(zi)), 7) * np.sign(zi)
     xi = ki * s_eff[..., None] * (6 / 7)
     ef = ((xf - y) ** 2).sum(-1)
@@ -195,6 +198,11 @@ def test_if4_selection_minimises_squared_error():
     clear = np.abs(ef - ei) > 1e-5 * np.maximum(ef, ei)
     np.testing.assert_array_equal(flag[clear], (ei < ef)[clear])
     assert clear.mean() > 0.99
+    # codes: nibble 2j of byte j low, 2j + 1 high
+    nib = np.stack([q.codes & 15, q.codes >> 4], -1).reshape(256, 32, 16).astype(np.int64)
+    want_i = (np.minimum(np.rint(np.abs(zi)), 7).astype(np.int64) | np.where(np.signbit(zi), 8, 0))
+    want = np.where(flag[..., None], want_i, kf)
+    np.testing.assert_array_equal(nib, want)
 
 
 def test_if4_uniform_blocks_choose_int4_and_share_is_plausible():

@@ -73,12 +73,21 @@ __device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1)
     return c;
 }
 
-// Four SR words for view elements n0..n0+3 (n0 a multiple of 4).
-__device__ __forceinline__ uint4 sr_words4(uint64_t n0, uint64_t seed, uint32_t stream)
+// SR words of view elements n0..n0+7 (n0 a multiple of 8), one Philox block at
+// counter n0 / 8: the 32-bit output words are read 16 bits at a time, low half
+// first, and each element's 16 bits go to the top half of its word (the low
+// half zero), where both stochastic-rounding converts read their random bits.
+__device__ __forceinline__ void sr_words8(uint64_t n0, uint64_t seed, uint32_t stream, uint32_t *w)
 {
-    const uint64_t q = n0 >> 2;
-    return philox10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), stream, 0u), (uint32_t)seed,
-                    (uint32_t)(seed >> 32));
+    const uint64_t q = n0 >> 3;
+    const uint4 r = philox10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), stream, 0u), (uint32_t)seed,
+                             (uint32_t)(seed >> 32));
+    const uint32_t o[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        w[2 * j] = o[j] << 16;
+        w[2 * j + 1] = o[j] & 0xFFFF0000u;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -120,7 +129,7 @@ __device__ __forceinline__ void fwht16_local(float *v)
 // when the residual r does not underflow.  Conditions used here: s in
 // [2^-75, 2^125] and a >= 2^-100 (r is then a normal number); for a < 2^-100
 // the quotient is below 2^-25, where every rounding gives code 0 (RTNE, and
-// stochastic rounding, which rounds up only from 2^-20 of a step).
+// stochastic rounding, which rounds up only from 2^-16 of a step).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool fast_div_ok(float s) { return s >= 0x1p-75f && s <= 0x1p125f; }
 
@@ -279,14 +288,16 @@ __device__ __forceinline__ uint32_t pack8_uniform(const float *z)
     return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
 }
 
-// Stochastic rounding of 8 signed scaled values onto a uniform grid, one
-// Philox word each, through the FP8 convert with stochastic rounding: z is
-// clamped to the grid maximum (so 2|z|, or |z| for INT4, stays within the
-// subnormal codes 0..7) and the convert returns sign << 7 | k with k = k_lo + 1
-// exactly when (w >> 12) + floor(frac 2^20) reaches 2^20, frac = t - k_lo
-// (checked on gfx950 against that rule on 2^30 pairs per grid: z of every
-// binary32 exponent and sign, w random or at the rounding threshold and one
-// below).  The bytes fold into nibbles as in pack8_uniform.
+// Stochastic rounding of 8 signed scaled values onto a uniform grid through
+// the FP8 convert with stochastic rounding: z is clamped to the grid maximum
+// (so 2|z|, or |z| for INT4, stays within the subnormal codes 0..7) and the
+// convert returns sign << 7 | k with k = k_lo + 1 exactly when (w >> 12) +
+// floor(frac 2^20) reaches 2^20, frac = t - k_lo (checked on gfx950 against
+// that rule on 2^30 pairs per grid: z of every binary32 exponent and sign, w
+// random or at the rounding threshold and one below).  The words w come from
+// sr_words8, their low 16 bits zero: with h = w >> 16, (w >> 12) = 16 h, and
+// 16 h + floor(frac 2^20) >= 2^20 holds exactly when h + floor(frac 2^16) >=
+// 2^16, the 16-bit rule.  The bytes fold into nibbles as in pack8_uniform.
 template <int F>
 __device__ __forceinline__ uint32_t pack8_uniform_sr(const float *z, const uint32_t *w)
 {
@@ -308,14 +319,13 @@ __device__ __forceinline__ uint32_t pack8_uniform_sr(const float *z, const uint3
     return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
 }
 
-// Stochastic rounding of 8 signed scaled values onto E2M1, one Philox word
-// each, through the packed FP4 convert with stochastic rounding.  That convert
-// rounds its first value up when (seed >> 10) + floor(frac 2^22) reaches 2^22
-// (and feeds the second a rotated copy of the seed).  With the seed's low 12
-// bits cleared, seed >> 10 = 4 (w >> 12), and 4 (w >> 12) + floor(frac 2^22) >=
-// 2^22 holds exactly when (w >> 12) + floor(frac 2^20) >= 2^20: the 20-bit rule
-// of the uniform grids (checked on gfx950 on 2^30 pairs, |z| up to 32 for the
-// saturation at 6).  One value per convert, the second 0 (code 0), into byte 0:
+// Stochastic rounding of 8 signed scaled values onto E2M1 through the packed
+// FP4 convert with stochastic rounding.  That convert rounds its first value
+// up when (seed >> 10) + floor(frac 2^22) reaches 2^22 (and feeds the second
+// a rotated copy of the seed).  The words of sr_words8 have their low 16 bits
+// clear, so seed >> 10 = 64 h with h = w >> 16, and 64 h + floor(frac 2^22) >=
+// 2^22 holds exactly when h + floor(frac 2^16) >= 2^16: the 16-bit rule of the
+// uniform grids.  One value per convert, the second 0 (code 0), into byte 0:
 // this builtin does not keep the other bytes of its first operand (they come
 // back as whatever the destination register held), so only byte 0 of each
 // result is used and v_perm gathers them, the even elements' codes into the
@@ -323,7 +333,7 @@ __device__ __forceinline__ uint32_t pack8_uniform_sr(const float *z, const uint3
 __device__ __forceinline__ uint32_t sr_fp4_byte0(float z, uint32_t w)
 {
     const v2f p = {z, 0.0f};
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, w & 0xFFFFF000u, 1.0f, 0);
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, w, 1.0f, 0);
 }
 __device__ __forceinline__ uint32_t gather_byte0(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3)
 {

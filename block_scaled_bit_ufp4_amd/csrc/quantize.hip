@@ -131,7 +131,7 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
 // Signed scaled values z_i = RN(y_i / s) for 8 kernel values v_i (v = 4y when
 // FOLD).  The fast quotient can be off only for |v| < 2^-100, where |z| <
 // 2^-25: RTNE gives code 0 there, and so does SR, which rounds up only from
-// 2^-20 of a step above the lower point.
+// 2^-16 of a step above the lower point.
 template <int S, bool FOLD, bool SR>
 __device__ __forceinline__ void scaled8(const float *v, const BlockScale &b, float *z)
 {
@@ -361,10 +361,7 @@ __device__ __forceinline__ uint2 quant_chunk(const float *v, const TensorConst &
         uint32_t w[16];
         if constexpr (SR) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 ww = sr_words4(n0 + 4 * q, sr_seed, sr_stream);
-                w[4 * q] = ww.x; w[4 * q + 1] = ww.y; w[4 * q + 2] = ww.z; w[4 * q + 3] = ww.w;
-            }
+            for (int q = 0; q < 2; ++q) sr_words8(n0 + 8 * q, sr_seed, sr_stream, w + 8 * q);
         }
         lo = encode8<F, S, FOLD, SR>(v, bs, w);
         hi = encode8<F, S, FOLD, SR>(v + 8, bs, w + 8);
@@ -630,10 +627,7 @@ __global__ __launch_bounds__(CT) void col_kernel(const ColArgs a)
                 if constexpr (SR) {
                     const uint64_t n0 = (uint64_t)c * (uint64_t)a.R + (uint64_t)r0;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint4 ww = sr_words4(n0 + 4 * q, a.sr_seed, a.sr_stream);
-                        w[4 * q] = ww.x; w[4 * q + 1] = ww.y; w[4 * q + 2] = ww.z; w[4 * q + 3] = ww.w;
-                    }
+                    for (int q = 0; q < 2; ++q) sr_words8(n0 + 8 * q, a.sr_seed, a.sr_stream, w + 8 * q);
                 }
                 lo = encode8<F, S, FOLD, SR>(v, bs, w);
                 hi = encode8<F, S, FOLD, SR>(v + 8, bs, w + 8);

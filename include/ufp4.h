@@ -76,10 +76,11 @@
  *          (m = 0 gives E = -127).
  *   z    = y / s (correctly rounded); s = 0 gives code 0.
  *   RTNE: nearest grid point, ties to the even code, saturating at gridmax.
- *   SR:   k = k_lo + 1 when (w >> 12) + floor(frac 2^20) >= 2^20, else k_lo
- *          (frac = position of |z| in its cell; 20 random bits), w = Philox4x32-10
- *          word n mod 4 at key = sr_seed, counter = (lo32(n/4), hi32(n/4),
- *          sr_stream, 0), n = v L + l the element's index in the view.
+ *   SR:   k = k_lo + 1 when h + floor(frac 2^16) >= 2^16, else k_lo (frac =
+ *          position of |z| in its cell; 16 random bits h per element): h is
+ *          half n mod 2 (low half first) of Philox4x32-10 word (n/2) mod 4 at
+ *          key = sr_seed, counter = (lo32(n/8), hi32(n/8), sr_stream, 0),
+ *          n = v L + l the element's index in the view.
  *   IF4:  z = y/s; FP4 candidate = RTNE of z on E2M1 (grid value g); INT4
  *          candidate k = rint(z x 7/6) clamped to 7, dequantized as (k x s) x 6/7;
  *          errors in units of s, g - z and (k x 6/7) - z; the candidate with the

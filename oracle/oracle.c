@@ -141,12 +141,13 @@ int orc_round_rtne(float z, int fmt)
 /* Stochastic rounding: [IF4] 6.1 gives floor(x) + (random() < frac); [UFP4-TW]
  * 五 applies it to dY only.  On a non-uniform grid "floor" is the grid point
  * just below |z| and frac the position inside that cell.  The pages fix no
- * resolution; here both sides of the comparison have 20 bits: frac is cut to
- * F = floor(frac 2^20) and random() is U 2^-20 with U = 2^20 - 1 - (w >> 12),
- * the complement of the top 20 bits of one Philox word w.  The element rounds
- * up when U < F, i.e. when (w >> 12) + F reaches 2^20; so P(up) = F 2^-20,
- * within 2^-20 below frac, and an |z| less than 2^-20 of a cell above its
- * lower point always rounds down.  |z| at or above the grid maximum gives the
+ * resolution; here both sides of the comparison have 16 bits: frac is cut to
+ * F = floor(frac 2^16) and random() is U 2^-16 with U = 2^16 - 1 - (w >> 16),
+ * the complement of the element's 16 random bits, which orc_sr_word puts in
+ * the top half of w (the low half is ignored).  The element rounds up when
+ * U < F, i.e. when (w >> 16) + F reaches 2^16; so P(up) = F 2^-16, within
+ * 2^-16 below frac, and an |z| less than 2^-16 of a cell above its lower
+ * point always rounds down.  |z| at or above the grid maximum gives the
  * maximum.  (F is exact: frac is a short binary fraction, the cell widths
  * being powers of two.) */
 int orc_round_sr(float z, int fmt, uint32_t w)
@@ -162,8 +163,8 @@ int orc_round_sr(float z, int fmt, uint32_t w)
         for (int j = 1; j <= km; ++j)
             if (g[j] <= a) lo = j;
         double frac = (a - g[lo]) / (g[lo + 1] - g[lo]);
-        uint32_t F = (uint32_t)floor(frac * 0x1p20);
-        uint32_t U = 0xFFFFFu - (w >> 12);
+        uint32_t F = (uint32_t)floor(frac * 0x1p16);
+        uint32_t U = 0xFFFFu - (w >> 16);
         k = lo + (U < F ? 1 : 0);
     }
     return (signbit(z) ? 8 : 0) | k;
@@ -248,17 +249,21 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
     out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-/* The SR uniform word for element n of a quantization view:
- * key = (seed lo, seed hi), counter = (lo32(n/4), hi32(n/4), stream, 0),
- * word n mod 4. */
+/* The SR random bits of element n of a quantization view, in the top half of
+ * the returned word (the low half zero).  The view's elements read Philox's
+ * 32-bit output stream 16 bits at a time, low half first: element n takes
+ * half n mod 2 of word (n / 2) mod 4 of the block at key = (seed lo, seed hi),
+ * counter = (lo32(n/8), hi32(n/8), stream, 0). */
 uint32_t orc_sr_word(uint64_t seed, uint32_t stream, uint64_t n)
 {
     uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
-    uint64_t q = n >> 2;
+    uint64_t q = n >> 3;
     uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), stream, 0u};
     uint32_t out[4];
     orc_philox4x32_10(ctr, key, out);
-    return out[n & 3];
+    uint32_t word = out[(n >> 1) & 3];
+    uint32_t half = (n & 1) ? (word >> 16) : (word & 0xFFFFu);
+    return half << 16;
 }
 
 /* ------------------------------------------------------------------------ */

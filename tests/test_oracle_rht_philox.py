@@ -165,16 +165,21 @@ def rocrand_probe():
 
 def test_philox_matches_rocrand_engine(rocrand_probe):
     """rocRAND's engine(seed, subsequence, offset=4q) runs the block with
-    key = seed and counter = (q lo, q hi, subsequence lo, subsequence hi):
-    the same mapping the SR stream uses (stream = subsequence)."""
+    key = seed and counter = (q lo, q hi, subsequence lo, subsequence hi).
+    The SR stream takes that block's counter with stream = subsequence, and
+    reads its four words 16 bits at a time, low half first: element 8q + 2j + h
+    holds bits 16h..16h+15 of word j in the top half of its SR word."""
     cases = [(0, 0, 0), (0, 0, 1), (1, 0, 0), (0x1234567890, 3, 77), (2 ** 64 - 1, 1, 2 ** 40 + 5),
              (0xDEADBEEF, 0, 123456789), (7, 0x52485400, 0)]
     args = [str(v) for c in cases for v in c]
     out = subprocess.run([rocrand_probe, *args], check=True, capture_output=True, text=True).stdout.split("\n")
     for (seed, sub, q), line in zip(cases, out):
         want = [int(t) for t in line.split()]
-        got = [O.sr_word(seed, sub, 4 * q + j) for j in range(4)]
+        got = [int(v) for v in O.philox4x32_10([q & 0xFFFFFFFF, q >> 32, sub, 0],
+                                                [seed & 0xFFFFFFFF, seed >> 32])]
         assert got == want, (seed, sub, q)
+        halves = [(x >> (16 * h)) & 0xFFFF for x in want for h in range(2)]
+        assert [O.sr_word(seed, sub, 8 * q + i) for i in range(8)] == [v << 16 for v in halves], (seed, sub, q)
     # the sign diagonal is word 0 of the counter (0,0,"RHT\0",0) block
     w = O.philox4x32_10([0, 0, 0x52485400, 0], [7, 0])
     assert O.rht_sign_mask("random", 7) == (int(w[0]) & 0xFFFF)
@@ -215,30 +220,30 @@ def test_sr_is_unbiased(fmt):
 
 @pytest.mark.parametrize("fmt", ["e2m1", "e1m2", "int4"])
 def test_sr_resolution_and_direction(fmt):
-    """The SR decision at 20-bit resolution (the reading of IF4 page 6.1's
-    random() < frac): over the 2^20 words w = j 2^12 + r, r any low 12 bits,
-    exactly floor(frac 2^20) round up, and they are the largest j.  frac and
-    its 20-bit floor are computed here exactly with fractions."""
+    """The SR decision at 16-bit resolution (the reading of IF4 page 6.1's
+    random() < frac): over the 2^16 words w = j 2^16 + r, r any low 16 bits,
+    exactly floor(frac 2^16) round up, and they are the largest j.  frac and
+    its 16-bit floor are computed here exactly with fractions."""
     from fractions import Fraction
     g = O.grid(fmt)
     rng = np.random.default_rng(3)
-    j = np.arange(1 << 20, dtype=np.uint64)
-    for a in [0.1, 0.3, 0.8, 1.2, 1.7, 2.3, 2.9, 3.3, 4.4, 5.5, 6.9, 0.75]:
+    j = np.arange(1 << 16, dtype=np.uint64)
+    for a in [0.1, 0.3, 0.8, 1.2, 1.7, 2.3, 2.9, 3.3, 4.4, 5.5, 6.9, 0.75, 1.0 + 2.0**-15, 2.5 - 2.0**-14]:
         a = np.float32(min(a, float(g[7]) * 0.999))
         k_lo = int(np.nonzero(g <= a)[0].max())
         frac = (Fraction(float(a)) - Fraction(float(g[k_lo]))) / (Fraction(float(g[k_lo + 1])) - Fraction(float(g[k_lo])))
-        F = int(frac * 2**20)  # floor (frac >= 0)
-        r = rng.integers(0, 4096, size=j.size).astype(np.uint64)
-        w = ((j << np.uint64(12)) | r).astype(np.uint32)
+        F = int(frac * 2**16)  # floor (frac >= 0)
+        r = rng.integers(0, 1 << 16, size=j.size).astype(np.uint64)
+        w = ((j << np.uint64(16)) | r).astype(np.uint32)
         codes = O.round_sr_array(np.full(j.size, a, np.float32), w, fmt) & 7
         assert set(np.unique(codes)) <= {k_lo, k_lo + 1}
         up = codes == k_lo + 1
         assert int(up.sum()) == F, (fmt, float(a), int(up.sum()), F)
-        assert np.array_equal(up, j >= (1 << 20) - F)
-    # less than 2^-20 of a step above a grid point: never up, even for the largest word
+        assert np.array_equal(up, j >= (1 << 16) - F)
+    # less than 2^-16 of a step above a grid point: never up, even for the largest word
     step = float(g[1] - g[0])
-    for a in [step * 2.0**-21, step * 2.0**-30, float(g[2]) + float(g[3] - g[2]) * 2.0**-21]:
+    for a in [step * 2.0**-17, step * 2.0**-30, float(g[2]) + float(g[3] - g[2]) * 2.0**-17]:
         z = np.full(4, a, np.float32)
         lo = int(np.nonzero(g <= np.float32(a))[0].max())
-        w = np.array([0xFFFFFFFF, 0xFFFFF000, 0x80000000, 0], np.uint32)
+        w = np.array([0xFFFFFFFF, 0xFFFF0000, 0x80000000, 0], np.uint32)
         assert np.all(O.round_sr_array(z, w, fmt) == lo)

@@ -285,9 +285,9 @@ __device__ __forceinline__ float absmax16(const float *v)
 // E2M1 candidate's codes from the FP4 convert of z and its grid values from
 // the FP4 decode; the INT4 candidate's levels from t = RN(z 7/6), rounded and
 // packed by the FP8 convert.  Both errors in units of the scale: g - z and
-// RN(k 6/7) - z (each error is odd in y, so its square equals the |y| form).
-// Squared errors summed pairwise, spans 1, 2, 4, 8; INT4 iff strictly smaller.
-// Sets the flag in bit 7 of sbyte.
+// k 6/7 - z (one FMA; each error is odd in y, so its square equals the |y|
+// form).  Each candidate's squares accumulate in element order, one FMA per
+// element; INT4 iff strictly smaller.  Sets the flag in bit 7 of sbyte.
 __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, uint32_t &lo, uint32_t &hi,
                                           uint32_t &sbyte)
 {
@@ -302,13 +302,13 @@ __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, 
         for (int i = 0; i < 16; ++i) z[i] = v[i] / bs.s;
     }
     const uint32_t lof = pack8_e2m1(z), hif = pack8_e2m1(z + 8);
-    float ef[16], ei[16];
+    float ef = 0.0f, ei = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const v2f g = decode2_e2m1(j < 4 ? lof : hif, j & 3);
         const float d0 = g.x - z[2 * j], d1 = g.y - z[2 * j + 1];
-        ef[2 * j] = d0 * d0;
-        ef[2 * j + 1] = d1 * d1;
+        ef = __builtin_fmaf(d0, d0, ef);
+        ef = __builtin_fmaf(d1, d1, ef);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) t[i] = z[i] * C76;
@@ -320,17 +320,10 @@ __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, 
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float d = __builtin_rintf(t[i]) * C67 - z[i];
-        ei[i] = d * d;
+        const float d = __builtin_fmaf(__builtin_rintf(t[i]), C67, -z[i]);
+        ei = __builtin_fmaf(d, d, ei);
     }
-#pragma unroll
-    for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2 * w) {
-            ef[i] = ef[i] + ef[i + w];
-            ei[i] = ei[i] + ei[i + w];
-        }
-    const bool use_int = bs.s != 0.0f && ei[0] < ef[0];
+    const bool use_int = bs.s != 0.0f && ei < ef;
     if (use_int) {
         lo = pack8_uniform<FMT_INT4>(t);
         hi = pack8_uniform<FMT_INT4>(t + 8);

@@ -83,8 +83,9 @@
  *          n = v L + l the element's index in the view.
  *   IF4:  z = y/s; FP4 candidate = RTNE of z on E2M1 (grid value g); INT4
  *          candidate k = rint(z x 7/6) clamped to 7, dequantized as (k x s) x 6/7;
- *          errors in units of s, g - z and (k x 6/7) - z; the candidate with the
- *          smaller binary32 squared error (pairwise sum) wins, ties to FP4.
+ *          errors in units of s, g - z and k x 6/7 - z (one fused multiply-add);
+ *          the candidate with the smaller binary32 sum of squared errors (each
+ *          square fused into the running sum, in element order) wins, ties to FP4.
  *   Dequantization: x_hat = v x s (IF4 INT4 blocks: (k x s) x 6/7).
  */
 #ifndef UFP4_H

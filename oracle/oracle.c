@@ -485,13 +485,15 @@ static void quantize_block(const orc_config *cfg, const float *y, int B, float a
      * (smaller sum of squared errors) is kept, and bit 7 of the scale byte
      * records which (1 = INT4).  Readings: the errors are measured in units of
      * the block scale, against z = RN(y / s): g - z for the E2M1 grid value g,
-     * RN(level * 6/7) - z for the signed INT4 level (in exact arithmetic both
-     * are the reconstruction's error divided by s, so the ranking is the
-     * same); the squared errors are binary32, summed as a balanced tree over
-     * neighbours (pairs, then pairs of pairs: four levels for 16 values), and
-     * an exact tie keeps E2M1. */
+     * and level * 6/7 - z rounded once (a fused multiply-add) for the signed
+     * INT4 level (in exact arithmetic both are the reconstruction's error
+     * divided by s, so the ranking is the same); each candidate's squares are
+     * accumulated in element order, each square fused into the running sum
+     * (one rounding per element, as a dot product of the errors with
+     * themselves), and an exact tie keeps E2M1. */
     int fp4_code[16], int_code[16];
-    float fp4_z[16], int_z[16], fp4_val[16], int_val[16], fp4_sq[16], int_sq[16];
+    float fp4_z[16], int_z[16], fp4_val[16], int_val[16];
+    float fp4_sq = 0.0f, int_sq = 0.0f;
     for (int i = 0; i < B; ++i) {
         if (s == 0.0f) {
             fp4_code[i] = int_code[i] = 0;
@@ -508,16 +510,12 @@ static void quantize_block(const orc_config *cfg, const float *y, int B, float a
         if (fp4_code[i] & 8) g = -g;
         float level = (float)(int_code[i] & 7);
         if (int_code[i] & 8) level = -level;
-        float dev_fp4 = g - fp4_z[i], dev_int = level * IF4_SHRINK - fp4_z[i];
-        fp4_sq[i] = dev_fp4 * dev_fp4;
-        int_sq[i] = dev_int * dev_int;
+        float dev_fp4 = g - fp4_z[i];
+        float dev_int = fmaf(level, IF4_SHRINK, -fp4_z[i]);
+        fp4_sq = fmaf(dev_fp4, dev_fp4, fp4_sq);
+        int_sq = fmaf(dev_int, dev_int, int_sq);
     }
-    for (int span = 1; span < B; span <<= 1)
-        for (int i = 0; i < B; i += 2 * span) {
-            fp4_sq[i] = fp4_sq[i] + fp4_sq[i + span];
-            int_sq[i] = int_sq[i] + int_sq[i + span];
-        }
-    int use_int = (s != 0.0f) && (int_sq[0] < fp4_sq[0]);
+    int use_int = (s != 0.0f) && (int_sq < fp4_sq);
     out->int4 = use_int;
     out->scale_b = (uint8_t)(out->scale_b | (use_int ? 0x80 : 0));
     for (int i = 0; i < B; ++i) {

@@ -269,9 +269,21 @@ __device__ __forceinline__ v2f decode2_e2m1(uint32_t w, int b)
     }
 }
 
+// The FP8 convert's bytes of 8 values (d0: elements 0..3, d1: 4..7), each
+// sign << 7 | k with k <= 7 (bits 3..6 clear), as 8 codes sign << 3 | k, byte j
+// holding element 2j in its low nibble and 2j + 1 in its high one: v_perm
+// gathers the even and the odd elements' bytes, then a 4-bit shift brings each
+// byte's sign next to its k (right for the low nibbles, left for the high ones).
+__device__ __forceinline__ uint32_t fold_fp8_codes(uint32_t d0, uint32_t d1)
+{
+    const uint32_t ev = __builtin_amdgcn_perm(d1, d0, 0x06040200u);  // elements 0, 2, 4, 6
+    const uint32_t od = __builtin_amdgcn_perm(d1, d0, 0x07050301u);  // elements 1, 3, 5, 7
+    return (((od << 4) | od) & 0xF0F0F0F0u) | ((ev | (ev >> 4)) & 0x0F0F0F0Fu);
+}
+
 // 8 signed scaled values on the uniform grids -> 8 codes: the FP8 convert
-// gives bytes sign<<7 | k; the sign moves to bit 3 and byte pairs fold into
-// nibble pairs.  Requires |z| <= gridmax (+ less than half a step).
+// gives bytes sign<<7 | k, folded into nibbles.  Requires |z| <= gridmax (+
+// less than half a step).
 template <int F>
 __device__ __forceinline__ uint32_t pack8_uniform(const float *z)
 {
@@ -281,11 +293,7 @@ __device__ __forceinline__ uint32_t pack8_uniform(const float *z)
     w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, z[2], z[3], SC, true);
     w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, z[4], z[5], SC, false);
     w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, z[6], z[7], SC, true);
-    const uint32_t d0 = __builtin_bit_cast(uint32_t, w0), d1 = __builtin_bit_cast(uint32_t, w1);
-    const uint32_t n0 = ((d0 >> 4) & 0x08080808u) | (d0 & 0x07070707u);
-    const uint32_t n1 = ((d1 >> 4) & 0x08080808u) | (d1 & 0x07070707u);
-    const uint32_t t0 = n0 | (n0 >> 4), t1 = n1 | (n1 >> 4);
-    return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
+    return fold_fp8_codes(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1));
 }
 
 // Stochastic rounding of 8 signed scaled values onto a uniform grid through
@@ -312,11 +320,7 @@ __device__ __forceinline__ uint32_t pack8_uniform_sr(const float *z, const uint3
     d1 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d1, __builtin_amdgcn_fmed3f(z[5], -G, G), w[5], SC, 1);
     d1 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d1, __builtin_amdgcn_fmed3f(z[6], -G, G), w[6], SC, 2);
     d1 = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d1, __builtin_amdgcn_fmed3f(z[7], -G, G), w[7], SC, 3);
-    const uint32_t u0 = (uint32_t)d0, u1 = (uint32_t)d1;
-    const uint32_t n0 = ((u0 >> 4) & 0x08080808u) | (u0 & 0x07070707u);
-    const uint32_t n1 = ((u1 >> 4) & 0x08080808u) | (u1 & 0x07070707u);
-    const uint32_t t0 = n0 | (n0 >> 4), t1 = n1 | (n1 >> 4);
-    return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
+    return fold_fp8_codes((uint32_t)d0, (uint32_t)d1);
 }
 
 // Stochastic rounding of 8 signed scaled values onto E2M1 through the packed

@@ -74,8 +74,16 @@ def parse():
     return p.parse_args()
 
 
+# headers every kernel source includes: a change to them changes the kernels too
+KERNEL_HEADERS = [os.path.join(ROOT, "block_scaled_bit_ufp4_amd", "csrc", h) for h in ("device.hpp", "kernels.hpp")]
+
+
 def src_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """SHA-256 prefix of a kernel source together with the headers it includes."""
+    h = hashlib.sha256()
+    for p in [path] + KERNEL_HEADERS:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(pmc_file=None, kernel_src=None):

@@ -85,7 +85,8 @@ struct BlockScale {
     float invd;     // RN(1 / sd) where fast (0 otherwise)
     uint32_t byte;  // stored byte (E4M3 / E8M0)
     bool fast;      // Markstein division valid (or s == 0)
-    bool sub;       // E4M3 byte in the subnormal range (exponent field 0, nonzero)
+    bool sub;       // a scale that can leave |y| / s past the grid's top rounding boundary:
+                    // an E4M3 byte in the subnormal range, or a subnormal FP32 scale
 };
 
 // m: block amax of the transformed values y.  FOLD: the kernel holds 4y.
@@ -118,7 +119,10 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
             b.byte = e4m3_encode_hw(delta);
             b.s = t.alpha * e4m3_decode_hw(b.byte);
         }
-        b.sub = S == SC_E4M3 && (b.byte & 0x78u) == 0 && b.byte != 0;
+        if constexpr (S == SC_E4M3)
+            b.sub = (b.byte & 0x78u) == 0 && b.byte != 0;
+        else
+            b.sub = b.s != 0.0f && b.s < 0x1p-126f;
         b.sd = FOLD ? b.s * 4.0f : b.s;
         b.fast = b.s == 0.0f || (b.sd >= 0x1p-75f && b.sd <= 0x1p125f);
         // the reciprocal serves the fast quotients only (s and 1 / s normal there)
@@ -160,6 +164,15 @@ __device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b,
     if constexpr (SR && F == FMT_E2M1) {
         packed = pack8_e2m1_sr(z, w);
     } else if constexpr (SR) {
+        // The rounding must stay within the codes 0..7.  A normal FP32 scale
+        // RN(m / gridmax) keeps |z| within 2^-22 of the grid maximum, where
+        // stochastic rounding (which rounds up only from 2^-16 of a step)
+        // always rounds down: only waves holding a subnormal FP32 scale
+        // clamp.  Under E4M3 and E8M0 scales |z| can pass the maximum.
+        if (S != SC_FP32 || __builtin_amdgcn_ballot_w64(b.sub) != 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) z[i] = __builtin_amdgcn_fmed3f(z[i], -grid_max(F), grid_max(F));
+        }
         packed = pack8_uniform_sr<F>(z, w);
     } else if constexpr (F == FMT_E2M1) {
         packed = pack8_e2m1(z);
@@ -169,14 +182,16 @@ __device__ __forceinline__ uint32_t encode8(const float *v, const BlockScale &b,
         for (int i = 0; i < 8; ++i) z[i] = __builtin_amdgcn_fmed3f(z[i], -grid_max(F), grid_max(F));
         packed = pack8_e2m1(z);
     } else {
-        if constexpr (S == SC_E4M3) {
-            // The E4M3 rounding of Delta can leave |z| above the grid maximum.
-            // Past the rounding boundary above it (gridmax + step / 2, where
-            // the FP8 convert would leave the code range) only under a block
-            // scale in E4M3's subnormal range: a normal one is within 1/16 of
-            // Delta, so |z| <= gridmax x 16/15 (3.73 < 3.75 for E1M2, 7.47 <
-            // 7.5 for INT4), where the convert's own rounding gives the same
-            // code as the clamp.  Only waves holding such a block clamp.
+        if constexpr (S != SC_E8M0) {
+            // The rounding of the block scale can leave |z| above the grid
+            // maximum.  Past the rounding boundary above it (gridmax + step /
+            // 2, where the FP8 convert would leave the code range) only under
+            // an E4M3 scale in its subnormal range (a normal one is within
+            // 1/16 of Delta, so |z| <= gridmax x 16/15: 3.73 < 3.75 for E1M2,
+            // 7.47 < 7.5 for INT4, where the convert's own rounding gives the
+            // same code as the clamp) or a subnormal FP32 scale (a normal one
+            // is RN(m / gridmax), within a unit in the last place).  Only
+            // waves holding such a block clamp.
             if (__builtin_amdgcn_ballot_w64(b.sub) != 0) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) z[i] = __builtin_amdgcn_fmed3f(z[i], -grid_max(F), grid_max(F));

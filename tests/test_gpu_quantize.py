@@ -112,6 +112,50 @@ def test_subnormal_block_scales(fmt, axis, rht):
     assert np.any((b > 0) & (b < 8))  # the case is reached
 
 
+def binary32_tiny_blocks(rows=96, cols=256, seed=0):
+    """binary32 N(0,1) blocks scaled by 2^-e, e drawn per 16-element block in
+    [110, 151], so many blocks lie in (or reach into) the binary32 subnormal
+    range, where a single-level FP32 block scale m / gridmax is itself
+    subnormal and loses precision; plus blocks whose only nonzero value is a
+    few units of 2^-149."""
+    rng = np.random.default_rng([seed, 97])
+    e = rng.integers(110, 152, (rows, cols // 16)).repeat(16, axis=1)
+    x = (rng.standard_normal((rows, cols)) * np.exp2(-e.astype(np.float64))).astype(np.float32)
+    x[0, :16] = 0
+    x[0, 0] = np.float32(5 * 2.0 ** -149)
+    x[1, :16] = 0
+    x[1, 3] = np.float32(-11 * 2.0 ** -149)
+    x[2, :16] = np.float32(2.0 ** -149) * rng.integers(-40, 41, 16).astype(np.float32)
+    return x
+
+
+def tiny_configs():
+    out = []
+    for fmt, scale, rnd, rht, axis in itertools.product(["e1m2", "int4", "e2m1"], ["fp32", "e4m3"], ["rtne", "sr"],
+                                                        ["none", "random"], ["row", "col"]):
+        out.append(dict(format=fmt, scale=scale, block=16, rht=rht, rounding=rnd, axis=axis))
+    for rht, axis in itertools.product(["none", "random"], ["row", "col"]):
+        out.append(dict(format="if4", scale="e4m3", block=16, rht=rht, rounding="rtne", axis=axis))
+        out.append(dict(format="e2m1", scale="e8m0", block=32, rht=rht, rounding="rtne", axis=axis))
+    return out
+
+
+@pytest.mark.parametrize("d", tiny_configs(), ids=cfg_id)
+def test_binary32_subnormal_blocks(d):
+    """binary32 sources with blocks down in the subnormal range: where the block
+    scale is subnormal, |y| / s can pass the grid's largest code, and the codes
+    must still saturate there as the oracle's do."""
+    U = lib()
+    x = binary32_tiny_blocks()
+    if d["axis"] == "col":
+        x = np.ascontiguousarray(x.T)
+    cfg = U.Cfg(**d, rht_seed=1234, sr_seed=77, sr_stream=1 if d["axis"] == "col" else 0)
+    q = U.ufp4_quantize(to_device_f32(x), cfg)
+    want = O.quantize(x, oracle_cfg(cfg))
+    assert_bits_equal(host(q.codes), want.codes, "codes")
+    assert_bits_equal(host(q.scales), want.scales, "scales")
+
+
 @pytest.mark.parametrize("axis", ["row", "col"])
 @pytest.mark.parametrize("rht", ["none", "random", "det"])
 def test_amax_and_transform(axis, rht):

@@ -150,10 +150,19 @@ def test_binary32_subnormal_blocks(d):
     if d["axis"] == "col":
         x = np.ascontiguousarray(x.T)
     cfg = U.Cfg(**d, rht_seed=1234, sr_seed=77, sr_stream=1 if d["axis"] == "col" else 0)
-    q = U.ufp4_quantize(to_device_f32(x), cfg)
-    want = O.quantize(x, oracle_cfg(cfg))
+    xd = to_device_f32(x)
+    q = U.ufp4_quantize(xd, cfg)
+    ocfg = oracle_cfg(cfg)
+    want = O.quantize(x, ocfg)
     assert_bits_equal(host(q.codes), want.codes, "codes")
     assert_bits_equal(host(q.scales), want.scales, "scales")
+    # the dequantized values and the statistics of the same blocks
+    assert_bits_equal(host(U.ufp4_dequantize(q)), O.dequantize(want, ocfg, x.shape), "dequant")
+    got = host(U.ufp4_stats(xd, q))
+    ref = O.stats(x, ocfg)
+    assert np.all(np.isfinite(got)), got
+    compare_sums(got, ref)
+    np.testing.assert_array_equal(got[[0, 7, 8] + list(range(16, 32))], ref[[0, 7, 8] + list(range(16, 32))])
 
 
 @pytest.mark.parametrize("axis", ["row", "col"])

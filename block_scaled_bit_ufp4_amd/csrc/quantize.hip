@@ -298,11 +298,12 @@ __device__ __forceinline__ float absmax16(const float *v)
 // codes (low word: elements 0..7) and sets the scale byte / value.
 // IF4 for one 16-element block, on signed values: z = RN(y / s) once; the
 // E2M1 candidate's codes from the FP4 convert of z and its grid values from
-// the FP4 decode; the INT4 candidate's levels from t = RN(z 7/6), rounded and
-// packed by the FP8 convert.  Both errors in units of the scale: g - z and
-// k 6/7 - z (one FMA; each error is odd in y, so its square equals the |y|
-// form).  Each candidate's squares accumulate in element order, one FMA per
-// element; INT4 iff strictly smaller.  Sets the flag in bit 7 of sbyte.
+// the FP4 decode; the INT4 candidate's levels from t = RN(z 7/6), rounded by
+// the FP8 convert and read back by its decode.  Both errors in units of the
+// scale: g - z and k 6/7 - z (one FMA; each error is odd in y, so its square
+// equals the |y| form).  Each candidate's squares accumulate in element
+// order, one FMA per element; INT4 iff strictly smaller.  Sets the flag in
+// bit 7 of sbyte.
 __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, uint32_t &lo, uint32_t &hi,
                                           uint32_t &sbyte)
 {
@@ -333,15 +334,33 @@ __device__ __forceinline__ void if4_chunk(const float *v, const BlockScale &bs, 
 #pragma unroll
         for (int i = 0; i < 16; ++i) t[i] = __builtin_amdgcn_fmed3f(t[i], -7.0f, 7.0f);
     }
+    // the levels k = RN(t), ties to even, through the FP8 convert (bytes
+    // sign << 7 | |k|, the subnormal |k| 2^-9), read back exactly by the FP8
+    // decode: one convert and one decode per pair instead of a rounding per
+    // element, and the bytes are the INT4 codes once folded
+    uint32_t kb[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float d = __builtin_fmaf(__builtin_rintf(t[i]), C67, -z[i]);
-        ei = __builtin_fmaf(d, d, ei);
+    for (int q = 0; q < 4; ++q) {
+        v2i16 w = {0, 0};
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, t[4 * q], t[4 * q + 1], 512.0f, false);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, t[4 * q + 2], t[4 * q + 3], 512.0f, true);
+        kb[q] = __builtin_bit_cast(uint32_t, w);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const v2f k01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kb[q], 512.0f, false);
+        const v2f k23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kb[q], 512.0f, true);
+        const float k[4] = {k01.x, k01.y, k23.x, k23.y};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float d = __builtin_fmaf(k[j], C67, -z[4 * q + j]);
+            ei = __builtin_fmaf(d, d, ei);
+        }
     }
     const bool use_int = bs.s != 0.0f && ei < ef;
     if (use_int) {
-        lo = pack8_uniform<FMT_INT4>(t);
-        hi = pack8_uniform<FMT_INT4>(t + 8);
+        lo = fold_fp8_codes(kb[0], kb[1]);
+        hi = fold_fp8_codes(kb[2], kb[3]);
     } else {
         lo = lof;
         hi = hif;

@@ -367,8 +367,10 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
         const int bin0 = int4 ? 8 : 0;
         // With s = 0 (an all-zero block, or an E4M3 block scale that rounded
         // to zero) the block's scale of reference is the tensor scale alpha,
-        // above every such block's values.
-        const float pref = s != 0.0f ? s : (S == SC_E4M3 ? alpha : 1.0f);
+        // above every such block's values; an FP32 scale is 0 only for a
+        // block below 2^-147, whose values the largest scaling (2^126) keeps
+        // exact and normal.
+        const float pref = s != 0.0f ? s : (S == SC_E4M3 ? alpha : 0x1p-149f);
         const bool far = !(pref >= 0x1p-30f && pref <= 0x1p30f);
         auto terms = [&](auto scaled) {
             constexpr bool SCALED = decltype(scaled)::value;
@@ -385,7 +387,13 @@ __global__ __launch_bounds__(STATS_T) __attribute__((amdgpu_waves_per_eu(block_o
 #pragma unroll
             for (int i = 0; i < B; ++i) {
                 const float v = SCALED ? y[i] * P : y[i];
-                const float xk = IF4 ? (gv[i] * skp) * post : gv[i] * skp;  // P x_hat (x 4 when folded)
+                // P x_hat (x 4 when folded).  Scaled blocks take x_hat as the
+                // dequantizer rounds it, g s (then x 6/7 in IF4's INT4 blocks),
+                // before the exact scalings by P and by 4 (one at a time: P
+                // reaches 2^126): for blocks whose x_hat is subnormal that
+                // rounding is coarser than a product taken after scaling.
+                const float xk = SCALED ? ((IF4 ? (gv[i] * s) * post : gv[i] * s) * P) * (FOLD ? 4.0f : 1.0f)
+                                        : (IF4 ? (gv[i] * skp) * post : gv[i] * skp);
                 const float ek = xk - v;
                 p1 = __builtin_fmaf(v, v, p1);
                 p2 = __builtin_fmaf(ek, ek, p2);

@@ -86,7 +86,8 @@ struct BlockScale {
     uint32_t byte;  // stored byte (E4M3 / E8M0)
     bool fast;      // Markstein division valid (or s == 0)
     bool sub;       // a scale that can leave |y| / s past the grid's top rounding boundary:
-                    // an E4M3 byte in the subnormal range, or a subnormal FP32 scale
+                    // a subnormal scale, an E4M3 byte in the subnormal range, or a
+                    // subnormal E4M3 denominator alpha gridmax
 };
 
 // m: block amax of the transformed values y.  FOLD: the kernel holds 4y.
@@ -119,10 +120,11 @@ __device__ __forceinline__ BlockScale block_scale(float m, const TensorConst &t)
             b.byte = e4m3_encode_hw(delta);
             b.s = t.alpha * e4m3_decode_hw(b.byte);
         }
+        // (a subnormal scale, or under E4M3 a subnormal alpha gridmax, keeps
+        // too few bits for the bound on |z| that the clamp relies on)
+        b.sub = b.s != 0.0f && b.s < 0x1p-126f;
         if constexpr (S == SC_E4M3)
-            b.sub = (b.byte & 0x78u) == 0 && b.byte != 0;
-        else
-            b.sub = b.s != 0.0f && b.s < 0x1p-126f;
+            b.sub = b.sub || ((b.byte & 0x78u) == 0 && b.byte != 0) || (t.den != 0.0f && t.den < 0x1p-126f);
         b.sd = FOLD ? b.s * 4.0f : b.s;
         b.fast = b.s == 0.0f || (b.sd >= 0x1p-75f && b.sd <= 0x1p125f);
         // the reciprocal serves the fast quotients only (s and 1 / s normal there)

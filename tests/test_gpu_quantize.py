@@ -140,13 +140,16 @@ def tiny_configs():
     return out
 
 
+@pytest.mark.parametrize("shift", [0, 25], ids=["mixed", "all_tiny"])
 @pytest.mark.parametrize("d", tiny_configs(), ids=cfg_id)
-def test_binary32_subnormal_blocks(d):
+def test_binary32_subnormal_blocks(d, shift):
     """binary32 sources with blocks down in the subnormal range: where the block
     scale is subnormal, |y| / s can pass the grid's largest code, and the codes
-    must still saturate there as the oracle's do."""
+    must still saturate there as the oracle's do.  With shift 25 the whole
+    tensor is tiny (amax near 2^-135), so the two-level tensor scale and the
+    E4M3 scales built on it are subnormal as well."""
     U = lib()
-    x = binary32_tiny_blocks()
+    x = binary32_tiny_blocks() * np.float32(2.0 ** -shift)
     if d["axis"] == "col":
         x = np.ascontiguousarray(x.T)
     cfg = U.Cfg(**d, rht_seed=1234, sr_seed=77, sr_stream=1 if d["axis"] == "col" else 0)

@@ -129,6 +129,15 @@ def binary32_tiny_blocks(rows=96, cols=256, seed=0):
     return x
 
 
+def binary32_huge_blocks(rows=96, cols=256, seed=0):
+    """binary32 N(0,1) blocks scaled by 2^e, e drawn per block in [90, 120]: the
+    block maxima reach about 2^122, so squares and sums of squares overflow
+    binary32 while every transform stays finite (16 x 2^122 < 2^128)."""
+    rng = np.random.default_rng([seed, 98])
+    e = rng.integers(90, 121, (rows, cols // 16)).repeat(16, axis=1)
+    return (rng.standard_normal((rows, cols)) * np.exp2(e.astype(np.float64))).astype(np.float32)
+
+
 def tiny_configs():
     out = []
     for fmt, scale, rnd, rht, axis in itertools.product(["e1m2", "int4", "e2m1"], ["fp32", "e4m3"], ["rtne", "sr"],
@@ -140,16 +149,17 @@ def tiny_configs():
     return out
 
 
-@pytest.mark.parametrize("shift", [0, 25], ids=["mixed", "all_tiny"])
+@pytest.mark.parametrize("shift", [0, 25, None], ids=["mixed", "all_tiny", "huge"])
 @pytest.mark.parametrize("d", tiny_configs(), ids=cfg_id)
-def test_binary32_subnormal_blocks(d, shift):
+def test_binary32_extreme_blocks(d, shift):
     """binary32 sources with blocks down in the subnormal range: where the block
     scale is subnormal, |y| / s can pass the grid's largest code, and the codes
     must still saturate there as the oracle's do.  With shift 25 the whole
     tensor is tiny (amax near 2^-135), so the two-level tensor scale and the
-    E4M3 scales built on it are subnormal as well."""
+    E4M3 scales built on it are subnormal as well.  The "huge" case takes the
+    other end: block maxima near 2^122, squares past the binary32 range."""
     U = lib()
-    x = binary32_tiny_blocks() * np.float32(2.0 ** -shift)
+    x = binary32_huge_blocks() if shift is None else binary32_tiny_blocks() * np.float32(2.0 ** -shift)
     if d["axis"] == "col":
         x = np.ascontiguousarray(x.T)
     cfg = U.Cfg(**d, rht_seed=1234, sr_seed=77, sr_stream=1 if d["axis"] == "col" else 0)

@@ -90,11 +90,11 @@ static_assert(ROWS_PER_WAVE == 64, "one scale row per lane");
 // copies each wave issues: operand data of one stage, scales of one group
 constexpr int DATA_COPIES = 2 * (ROWS_PER_WAVE / 16);
 constexpr int scale_copies(bool fp4, bool pad) { return fp4 ? (pad ? 8 : 2) : 0; }
-// The bf16 path issues each stage's operand copy in two halves at two points
-// of the step (see gemm_step), which shortens its step by about a fifth at
-// 8192^3; the FP4 path, held back by its clock rather than by issue, keeps
-// one copy point.
-constexpr bool split_copies(bool fp4) { return !fp4; }
+// Both paths issue each stage's operand copy in two halves at two points of
+// the step (see gemm_step).  That shortens the bf16 step by about a fifth at
+// 8192^3; the FP4 step gains fewer cycles and loses part of them to the clock
+// (it runs at the board's power limit), 2-3 % net in an A/B in one process.
+constexpr bool split_copies(bool) { return true; }
 
 // Asynchronous global -> LDS copy of one stage's operand data, shared by the
 // waves: wave w copies tile rows 64 w .. 64 w + 63 of A and of B, 16 rows
@@ -300,9 +300,9 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags &f, c
 // four multiply zeroed fragments.  So the body has no branches around
 // matrix work and the scheduling barriers hold the order within it.  Restrict
 // slot pointers tell the compiler which slot each access touches, so the
-// copies into the other slots stay in flight.  Where the copies are split
-// (bf16), the barrier's copy takes the first half of each wave's rows of
-// stage k + 4, and the second half follows at the start of the next step,
+// copies into the other slots stay in flight.  The copies are split: the
+// barrier's copy takes the first half of each wave's rows of stage k + 4
+// (with the group's scales at position 0), and the second half follows at the start of the next step,
 // into the same slot (pv there): every wave has passed the barrier behind
 // its last read of that slot, and the copies in flight at each wait are
 // still the four halves of stages k + 2 and k + 3.

@@ -372,10 +372,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _time(fn, torch, stream, reps):
+def _time(fn, torch, stream, reps, warm=2):
     """Milliseconds per call over reps back-to-back calls, HIP events on the
-    stream at the ends only."""
-    for _ in range(2):
+    stream at the ends only, after warm untimed calls."""
+    for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -397,12 +397,16 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
     cfg = U.Cfg("e2m1", "e8m0", 32, rht="random", rht_seed=0)
     qa, qb = U.ufp4_quantize(a, cfg), U.ufp4_quantize(b, cfg)
     c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ms_call = _time(lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c), torch, stream, reps)
+    # The clock ramps up over the first ~0.1 s of back-to-back GEMMs (an
+    # alternating A/B read 0.36 ms per call in the first 20 and 0.30 ms by the
+    # fifth 20): 300 untimed calls first, so the timed ones run at the rate
+    # the chip sustains (at its power limit).
+    ms_call = _time(lambda: U.ufp4_qgemm(qa, qb, "mxfp4", c=c), torch, stream, 5 * reps, warm=300)
     cfg2 = U.Cfg("e1m2", "fp32", rht="random", rht_seed=0)
     ea, eb = U.ufp4_quantize(a, cfg2), U.ufp4_quantize(b, cfg2)
     ws = torch.empty(U.ufp4_workspace_size(U.OP_QGEMM, M + N, K, cfg2), dtype=torch.uint8, device=dev)
-    ms_e1m2 = _time(lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws), torch, stream, reps)
-    ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, reps)
+    ms_e1m2 = _time(lambda: U.ufp4_qgemm(ea, eb, "bf16", c=c, ws=ws), torch, stream, 2 * reps, warm=100)
+    ms_bf16 = _time(lambda: U.ufp4_gemm_bf16(a, b, c=c), torch, stream, 2 * reps, warm=100)
     tf = flop / (ms_call * 1e-3) / 1e12
     # attenuation and output SQNR of both paths against Z = A B^T of the bf16
     # inputs, and the whole path (quantize both operands, then the GEMM)
@@ -444,7 +448,7 @@ def bench_gemm(U, S, torch, dev, stream, reps=10):
         c4[name] = {"ms": round(ms_, 4), "eta": round(float(sm[0] / sm[1]), 6),
                     "sqnr_db": round(float(10 * np.log10(sm[1] / sm[2])), 3)}
     return {"workload": "8192^3 MXFP4 (E2M1 + E8M0/32, RHT-16) native scaled MFMA, fp32 out",
-            "ms": round(ms_call, 4), "timing": "back-to-back calls (one kernel each), events at the ends",
+            "ms": round(ms_call, 4), "timing": "50 back-to-back calls (one kernel each) after 300 untimed ones (the clock settles), events at the ends",
             "tflops": round(tf, 1), "peak_tflops": FP4_PEAK_TFLOPS, "frac": round(tf / FP4_PEAK_TFLOPS, 4),
             "eta": quality["mxfp4"]["eta"], "sqnr_db": quality["mxfp4"]["sqnr_db"],
             "quantize_and_gemm_ms": round(ms_e2e_mx, 4),

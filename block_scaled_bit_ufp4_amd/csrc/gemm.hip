@@ -33,7 +33,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int GBM = 256;   // workgroup tile rows (M)
 constexpr int GBN = 256;   // workgroup tile columns (N)
 constexpr int GKB = 64;    // bytes of K per row per stage
-constexpr int GROUP_M = 8; // tile-row group of the raster order
+constexpr int GROUP_M = 4; // tile-row group of the raster order
 
 // byte offset of 16-byte chunk c of row r in a stage (64 bytes per row)
 __device__ __forceinline__ int lds_off(int r, int c) { return r * GKB + ((c ^ ((r >> 2) & 3)) << 4); }

@@ -169,8 +169,16 @@ def test_binary32_extreme_blocks(d, shift):
     want = O.quantize(x, ocfg)
     assert_bits_equal(host(q.codes), want.codes, "codes")
     assert_bits_equal(host(q.scales), want.scales, "scales")
-    # the dequantized values and the statistics of the same blocks
+    # the dequantized values (also through the inverse transform) and the
+    # statistics of the same blocks
     assert_bits_equal(host(U.ufp4_dequantize(q)), O.dequantize(want, ocfg, x.shape), "dequant")
+    assert_bits_equal(host(U.ufp4_dequantize(q, inverse_rht=True)), O.dequantize(want, ocfg, x.shape, inverse=True),
+                      "dequant inverse")
+    if d["scale"] == "e4m3":
+        # the tensor amax and the standalone transform of the same source
+        assert host(U.ufp4_amax(xd, cfg))[0] == np.float32(O.amax(x, ocfg))
+        assert_bits_equal(host(U.ufp4_rht(xd, d["axis"], d["rht"], 1234)), O.rht_view(x, d["axis"], d["rht"], 1234),
+                          "rht f32")
     got = host(U.ufp4_stats(xd, q))
     ref = O.stats(x, ocfg)
     assert np.all(np.isfinite(got)), got

@@ -254,7 +254,7 @@ def cpu_gemm_baseline(S, rows, threads, M=8192, N=8192, K=8192):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the quantizer shards by rows "
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1 (the quantizer shards by rows "
                                    "with no exchange except a 4-byte amax MAX all-reduce, not run here)"}))
         sys.exit(2)
     import torch
